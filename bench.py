@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE experts forward pass on one MI355X.
+
+One step = one pass of the whole hot path over one batch: router logits (x . Wr^T) + softmax
+top-k (moe_route), expert grouping (moe_permute), gate/up grouped GEMM + SwiGLU and down grouped
+GEMM with the fused unpermute/weighting epilogue (moe_experts_forward), and the k-slot combine
+(moe_combine). Workload: the Mixtral-shaped prefill layer (T=4096 tokens, d=4096, f=14336, E=8,
+top-2, bf16 with fp32 accumulation), synthetic seeded inputs already resident in HBM.
+
+Prints one JSON line: active TFLOP/s (6*T*k*d*f per step), tokens/s, the roofline of the dominant
+kernel (gate/up GEMM, MFMA-bound) timed with HIP events on the launch stream, the Mixtral-shaped
+decode layer (T=32, weight-streaming, HBM-bound) on the same weights, and the CPU oracle timed on a
+bounded token sample as a reference baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE layer active TFLOP/s (prefill) + tokens/s (decode), % MFMA/HBM peak"
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device buffers for one MoE layer workload and a step() that enqueues the whole path."""
+
+    def __init__(self, moe, spec, x, Wr, Wg, Wu, Wd, n_ev_steps):
+        import torch
+        self.moe, self.spec = moe, spec
+        self.lib = moe.load_library()
+        dev = "cuda"
+        T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
+        P = T * k
+        self.x, self.Wr, self.Wg, self.Wu, self.Wd = x, Wr, Wg, Wu, Wd
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.sp = torch.empty(P, dtype=torch.int32, device=dev)
+        self.pp = torch.empty(P, dtype=torch.int32, device=dev)
+        pw = self.lib.moe_permute_workspace_size(T, k, E)
+        self.pws = torch.empty(max(pw, 1), dtype=torch.uint8, device=dev)
+        ew = self.lib.moe_experts_workspace_size(T, d, f, E, k, moe.MOE_BF16, moe.MOE_BF16)
+        self.ews = torch.empty(ew, dtype=torch.uint8, device=dev)
+        self.y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+        self.events = [[moe.event_create() for _ in range(4)] for _ in range(n_ev_steps)]
+        self.ev_arrays = [(ctypes.c_void_p * 4)(*e) for e in self.events]
+        self.args = moe.moe_experts_args(
+            T, d, f, E, k, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_Y_SLOTS,
+            x.data_ptr(), None, Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), None, None, None,
+            self.offsets.data_ptr(), self.sp.data_ptr(), self.w.data_ptr(), self.y.data_ptr(),
+            self.ews.data_ptr(), self.ews.numel(), None)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        self._route = (None, p(x), moe.MOE_BF16, p(Wr), T, d, E, k, p(self.logits), p(self.ids),
+                       p(self.w), self.stream)
+        self._perm = (p(self.ids), T, k, E, p(self.counts), p(self.offsets), p(self.sp),
+                      p(self.pp), None, 0, None, 0, None, None, p(self.pws), self.pws.numel(),
+                      self.stream)
+        self._comb = (p(self.y), moe.MOE_BF16, moe.MOE_Y_SLOTS, None, None, T, k, d, p(self.out),
+                      moe.MOE_BF16, self.stream)
+
+    def step(self, ev_index=None):
+        lib, chk = self.lib, self.moe._check
+        chk(lib.moe_route(*self._route))
+        chk(lib.moe_permute(*self._perm))
+        self.args.events = (ctypes.cast(self.ev_arrays[ev_index], ctypes.c_void_p)
+                            if ev_index is not None else None)
+        chk(lib.moe_experts_forward(ctypes.byref(self.args), self.stream))
+        chk(lib.moe_combine(*self._comb))
+
+    def kernel_ms(self, n):
+        g1 = [self.moe.event_elapsed_ms(e[0], e[1]) for e in self.events[:n]]
+        g2 = [self.moe.event_elapsed_ms(e[2], e[3]) for e in self.events[:n]]
+        return sum(g1) / n, sum(g2) / n
+
+
+def time_steps(layer, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer.step(ev_index=i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
+    """The oracle, as it stands, on the first n tokens of the workload (routing included)."""
+    import numpy as np
+    import oracle
+    ex = oracle.Experts(*W_np)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(n):
+        xs = np.ascontiguousarray(x_np[:n])
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(xs, Wr_np)
+        ids, w = oracle.route(lg, spec.k)
+        oracle.moe_forward(xs, ex, ids, w)
+        return time.perf_counter() - t0
+
+    n = 8
+    dt = run(n)
+    n2 = int(min(spec.T, max(n, n * seconds / max(dt, 1e-3))))
+    if n2 > n:
+        n, dt = n2, run(n2)
+    toks = n / dt
+    return {
+        "value": round(spec.active_flops() / spec.T * toks / 1e12, 6),
+        "unit": "TFLOP/s",
+        "tokens_per_s": round(toks, 2),
+        "seconds": round(dt, 2),
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "first %d of the %d tokens of %s (%d token-expert pairs): router logits, "
+                  "top-k routing, experts and combine, fp64 per-token loop" % (
+                      n, spec.T, spec.name, n * spec.k),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_softmax_amd as moe
+    import synth
+
+    torch.cuda.set_device(0)
+    spec = synth.MIXTRAL_PREFILL
+    T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
+    log("generating %s inputs" % spec.name)
+    t0 = time.perf_counter()
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    x_np = synth.gen_x(spec)
+    Wr_np = synth.gen_router_weight(spec)
+    W_np = [synth.gen_expert_weight(spec, n) for n in ("gate", "up", "down")]
+    x, Wr = up(x_np), up(Wr_np)
+    Wg, Wu, Wd = (up(a) for a in W_np)
+    log("inputs ready in %.1fs" % (time.perf_counter() - t0))
+
+    layer = Layer(moe, spec, x, Wr, Wg, Wu, Wd, max(args.steps, 1))
+    el = time_steps(layer, args.steps, args.warmup)
+    ms = el / args.steps * 1e3
+    g1_ms, g2_ms = layer.kernel_ms(args.steps)
+    flops = spec.active_flops()
+    tflops = flops / (el / args.steps) / 1e12
+    g1_flops = 4.0 * spec.P * d * f
+    g1_tflops = g1_flops / (g1_ms * 1e-3) / 1e12
+    counts = layer.counts.cpu().numpy()
+    log("prefill: %.3f ms/step, %.1f TFLOP/s; gate/up %.3f ms (%.1f TFLOP/s), down %.3f ms"
+        % (ms, tflops, g1_ms, g1_tflops, g2_ms))
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name, "T": T, "d": d, "f": f, "E": E, "k": k,
+            "tokens_per_s": round(T / (el / args.steps), 1),
+            "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+            "expert_rows_min_max": [int(counts.min()), int(counts.max())],
+            "gate_up_ms": round(g1_ms, 4), "down_ms": round(g2_ms, 4),
+            "down_tflops": round(2.0 * spec.P * d * f / (g2_ms * 1e-3) / 1e12, 2),
+        },
+        "roofline": {
+            "kernel": "gemm_bf16_kernel<gate_up> (gate/up grouped GEMM + SwiGLU)",
+            "bound": "mfma", "achieved": round(g1_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(g1_tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    del layer
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        dspec = synth.MIXTRAL_DECODE
+        xd = up(synth.gen_x(dspec))
+        dl = Layer(moe, dspec, xd, Wr, Wg, Wu, Wd, args.decode_steps)
+        eld = time_steps(dl, args.decode_steps, 5)
+        dms = eld / args.decode_steps * 1e3
+        d1, d2 = dl.kernel_ms(args.decode_steps)
+        dcounts = dl.counts.cpu().numpy()
+        touched = int((dcounts > 0).sum())
+        w_bytes_gu = touched * 2 * f * d * 2
+        w_bytes_dn = touched * d * f * 2
+        gbs1 = w_bytes_gu / (d1 * 1e-3) / 1e9
+        layer_gbs = (w_bytes_gu + w_bytes_dn) / (dms * 1e-3) / 1e9
+        log("decode: %.3f ms/step, %.0f tokens/s; gate/up %.3f ms (%.0f GB/s), down %.3f ms"
+            % (dms, dspec.T / (eld / args.decode_steps), d1, gbs1, d2))
+        result["decode"] = {
+            "workload": dspec.name,
+            "tokens_per_s": round(dspec.T / (eld / args.decode_steps), 1),
+            "ms_per_step": round(dms, 4),
+            "layer_weight_GBps": round(layer_gbs, 1),
+            "pct_hbm_peak": round(100 * layer_gbs / HBM_PEAK_GBS, 2),
+            "experts_touched": touched,
+            "roofline": {
+                "kernel": "decode_bf16_kernel<gate_up> (weight-streaming gate/up GEMM + SwiGLU)",
+                "bound": "hbm", "achieved": round(gbs1, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs1 / HBM_PEAK_GBS, 4), "traffic": None,
+                "down_ms": round(d2, 4),
+            },
+        }
+        del dl
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (~%.0fs)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(spec, x_np, Wr_np, W_np, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) sparse mixture-of-experts experts forward pass.
+ *
+ * The layer (Transformers docs page "Experts backends", introduction): for every token the router
+ * picks k experts, the token's hidden state is projected through those experts' parameters, and
+ * the expert outputs are summed with the routing weights. The router (lira-now explainer "Mixture
+ * of Experts (MoE): a practical explanation", section 5, router step by step): logits over E
+ * experts -> softmax -> top-k -> renormalise the k selected probabilities. Each expert is a gated
+ * MLP (same Transformers page, backends table rows deepgemm_megamoe and sonicmoe):
+ *     y = W_down (silu(W_gate x) * (W_up x)),   silu(z) = z / (1 + exp(-z)).
+ * Tokens are grouped by selected expert so that one grouped GEMM serves every expert (same table,
+ * row grouped_mm). The optional fine-grained FP8 path follows the Transformers page "Fine-grained
+ * FP8" (introduction): e4m3 weights with one fp32 scale per 128x128 block, e4m3 activations with a
+ * dynamic fp32 scale per token per 128 input channels.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named x, logits, w_*, s_*, ids, counts, offsets, sorted_pair, pair_pos, y, out,
+ *    workspace are DEVICE pointers owned by the caller. The library never allocates, frees or
+ *    synchronises; all work is enqueued on `stream` (NULL = the null stream) and completes
+ *    asynchronously in stream order.
+ *  - Row-major, contiguous tensors. Weights use the nn.Linear layout (out_features x in_features),
+ *    so a projection is x W^T: W_gate, W_up are [E, f, d] and W_down is [E, d, f].
+ *  - T tokens, d hidden size, f expert intermediate size, E experts, k experts per token,
+ *    P = T*k (token, slot) pairs, pair index p = t*k + j.
+ *  - Arguments are checked on the host before anything is enqueued. On any error nothing is
+ *    enqueued and no output is written; the status says why. A failed launch returns
+ *    MOE_ERR_DEVICE. Faults inside kernels surface at the caller's next synchronisation.
+ *  - The library is stateless and re-entrant; calls on different streams may overlap as long as
+ *    their buffers do not.
+ *  - Limits: 1 <= k <= E <= 1024, k <= 32, T >= 1, T*k < 2^31, d and f >= 1.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* bad sizes, k > E, null required pointer, unknown enum */
+  MOE_ERR_UNSUPPORTED = 2,        /* valid request without a kernel (e.g. fp8 dims not /128) */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_DEVICE = 4              /* a HIP launch or API call failed */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,       /* IEEE binary32 */
+  MOE_BF16 = 1,      /* bfloat16 */
+  MOE_FP8_E4M3 = 2   /* OCP E4M3FN: bias 7, max 448, no infinities */
+} moe_dtype;
+
+/* Layout of the expert outputs that moe_experts_forward writes and moe_combine reads. */
+typedef enum {
+  MOE_Y_PERMUTED = 0, /* y [P, d]: unweighted expert outputs, rows in sorted-pair order */
+  MOE_Y_SLOTS = 1,    /* y [T, k, d]: y[t][j] = w[t][j] * expert_{ids[t][j]}(x[t]) (fused
+                         unpermute + weighting in the down-projection epilogue) */
+  MOE_Y_ACC_F32 = 2   /* y [T, d] fp32: the weighted sum accumulated with atomic adds (zeroed by
+                         moe_experts_forward); summation order, and so rounding, is not fixed
+                         when k > 2 */
+} moe_y_layout;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_route - router: softmax over E expert logits, top-k, renormalise.
+ * (lira-now explainer, section 5, steps 2-5 and its pseudocode; gyaansetu explainer, top-k
+ * routing.)
+ *
+ *  logits      [T, E] fp32, or NULL to compute logits = x . w_router^T here in fp32.
+ *  x           [T, d] of x_dtype (MOE_F32 or MOE_BF16); used only when logits == NULL.
+ *  w_router    [E, d] fp32; used only when logits == NULL.
+ *  logits_out  [T, E] fp32: receives the logits that the selection used. Required when
+ *              logits == NULL (the computed logits live there); nullable otherwise.
+ *  topk_ids    [T, k] int32 out: expert ids by descending logit; equal logits go to the lower
+ *              expert index. (Selecting on logits picks the same set as selecting on softmax
+ *              probabilities, since softmax is strictly increasing.)
+ *  topk_w      [T, k] fp32 out: w[t][j] = exp(l_j - l_max) / sum_{j'<k} exp(l_j' - l_max), the
+ *              selected softmax probabilities renormalised to sum to 1.
+ * ------------------------------------------------------------------------------------------ */
+moe_status moe_route(const float* logits, const void* x, moe_dtype x_dtype,
+                     const float* w_router, int T, int d, int E, int k, float* logits_out,
+                     int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_permute - group the P = T*k (token, slot) pairs by expert.
+ * (Transformers "Experts backends" page, backends table row grouped_mm: tokens are sorted by
+ * their selected expert so one grouped GEMM projects them all.)
+ *
+ *  topk_ids     [T, k] int32 in [0, E).
+ *  counts       [E] int32 out: pairs per expert.
+ *  offsets      [E+1] int32 out: exclusive prefix sum of counts; offsets[E] = P.
+ *  sorted_pair  [P] int32 out: pair indices p = t*k + j, expert by expert, ascending p within an
+ *               expert (a stable sort, so the result is deterministic).
+ *  pair_pos     [P] int32 out: inverse of sorted_pair (pair p sits at row pair_pos[p]).
+ *  x, x_perm    optional gather (both NULL to skip): x_perm[r] = x[sorted_pair[r] / k], rows of d
+ *               elements of x_dtype (MOE_F32, MOE_BF16 or MOE_FP8_E4M3).
+ *  x_scales     FP8 only, [T, d/128] fp32; x_perm_scales [P, d/128] receives the gathered rows.
+ *  workspace    device scratch of at least moe_permute_workspace_size(T, k, E) bytes.
+ * ------------------------------------------------------------------------------------------ */
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
+                       moe_dtype x_dtype, const float* x_scales, int d, void* x_perm,
+                       float* x_perm_scales, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+size_t moe_permute_workspace_size(int T, int k, int E);
+
+/* ------------------------------------------------------------------------------------------
+ * fp8_quantize_act - dynamic per-token, per-group activation quantisation to e4m3.
+ * (Transformers "Fine-grained FP8" page, introduction: activations are quantised per group per
+ * token, the group matching the weights' 128 input channels, with scales computed at run time.)
+ *
+ *  x          [rows_in, K] of x_dtype (MOE_F32 or MOE_BF16).
+ *  row_index  nullable [M] int32: output row i quantises input row row_index[i] (gather while
+ *             quantising); NULL means output row i = input row i (rows_in = M).
+ *  q          [M, K] e4m3 codes out; scales [M, K/group] fp32 out.
+ *  Per group: s = amax/448 in fp32 (s = 1 if the group is all zero), q = e4m3(v / s) with IEEE
+ *  fp32 division, round-to-nearest-even, saturating at +-448. group must be 128; K % 128 == 0.
+ * ------------------------------------------------------------------------------------------ */
+moe_status fp8_quantize_act(const void* x, moe_dtype x_dtype, int M, int K, int group,
+                            const int32_t* row_index, uint8_t* q, float* scales,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * fp8_quantize_weight - offline 128x128 block quantisation of expert weights to e4m3.
+ * (Transformers "Fine-grained FP8" page, introduction: weights are quantised to 8 bits per
+ * two-dimensional block, weight_block_size = (128, 128).)
+ *
+ *  w       [batch, N, K] of w_dtype (MOE_F32 or MOE_BF16), e.g. batch = E experts.
+ *  q       [batch, N, K] e4m3 codes out; scales [batch, N/128, K/128] fp32 out.
+ *  Same rounding rule as fp8_quantize_act with the block's absmax. N % 128 == K % 128 == 0.
+ * ------------------------------------------------------------------------------------------ */
+moe_status fp8_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                               int block, uint8_t* q, float* scales, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_experts_forward - both grouped projections of every selected expert.
+ * (Transformers "Experts backends" page: introduction and backends table rows grouped_mm,
+ * deepgemm_megamoe, sonicmoe; the decode-time switch to a small-batch kernel; AWS fused-MoE news
+ * page, sections on swap-AB: small token counts put the large weight dimension on the matrix
+ * unit's fixed-size side.)
+ *
+ * Gate and up projections run as one grouped GEMM whose epilogue applies SwiGLU and writes the
+ * hidden activation h [P, f] to the workspace (bf16; e4m3 + per-128 scales on the fp8 path).
+ * The down projection runs as a second grouped GEMM whose epilogue writes y in a->y_layout.
+ * Small batches (P <= 256) use weight-streaming kernels with the weight rows on the MFMA M side.
+ *
+ * Supported dtype combinations (act_dtype / w_dtype / y_dtype):
+ *    F32 / F32 / F32                 fp32 everywhere
+ *    BF16 / BF16 / BF16 or F32       bf16 MFMA, fp32 accumulation
+ *    FP8_E4M3 / FP8_E4M3 / BF16 or F32
+ *        x = e4m3 codes [T, d] with x_scales [T, d/128] (from fp8_quantize_act); weights e4m3
+ *        with block scales; fp32 accumulation with per-128-K scale promotion; h is re-quantised
+ *        per pair per 128 channels. d % 128 == f % 128 == 0.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  int T, d, f, E, k;
+  moe_dtype act_dtype;           /* dtype of x */
+  moe_dtype w_dtype;             /* dtype of the expert weights */
+  moe_dtype y_dtype;             /* element type of y for MOE_Y_PERMUTED / MOE_Y_SLOTS */
+  moe_y_layout y_layout;
+  const void* x;                 /* [T, d] token activations */
+  const float* x_scales;         /* FP8: [T, d/128] */
+  const void* w_gate;            /* [E, f, d] */
+  const void* w_up;              /* [E, f, d] */
+  const void* w_down;            /* [E, d, f] */
+  const float* s_gate;           /* FP8: [E, f/128, d/128] */
+  const float* s_up;             /* FP8: [E, f/128, d/128] */
+  const float* s_down;           /* FP8: [E, d/128, f/128] */
+  const int32_t* offsets;        /* [E+1] from moe_permute */
+  const int32_t* sorted_pair;    /* [P] from moe_permute */
+  const float* topk_w;           /* [T, k] routing weights (MOE_Y_SLOTS, MOE_Y_ACC_F32) */
+  void* y;                       /* output, see moe_y_layout */
+  void* workspace;               /* >= moe_experts_workspace_size(...) bytes */
+  size_t workspace_bytes;
+  void** events;                 /* nullable: 4 hipEvent_t recorded on `stream` before/after the
+                                    gate/up GEMM and before/after the down GEMM (for timing) */
+} moe_experts_args;
+
+moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream);
+
+size_t moe_experts_workspace_size(int T, int d, int f, int E, int k, moe_dtype act_dtype,
+                                  moe_dtype w_dtype);
+
+/* ------------------------------------------------------------------------------------------
+ * moe_combine - weighted sum of each token's k expert outputs.
+ * (Transformers "Experts backends" page, introduction; lira-now explainer, section 4 (router +
+ * combine) and section 5 step 6: y = sum_i w_i * expert_i(x).)
+ *
+ *  MOE_Y_PERMUTED: out[t] = sum_{j<k} topk_w[t][j] * y[pair_pos[t*k+j]]   (y [P, d])
+ *  MOE_Y_SLOTS:    out[t] = sum_{j<k} y[t][j]                             (y [T, k, d])
+ *  MOE_Y_ACC_F32:  out[t] = y[t]                                          (y [T, d] fp32)
+ *  Sums run in fp32 in the order j = 0..k-1; one rounding to out_dtype (MOE_F32 or MOE_BF16).
+ *  pair_pos and topk_w are read only for MOE_Y_PERMUTED.
+ * ------------------------------------------------------------------------------------------ */
+moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
+                       const int32_t* pair_pos, const float* topk_w, int T, int k, int d,
+                       void* out, moe_dtype out_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Timing helpers (thin wrappers over HIP events, for callers without their own HIP bindings).
+ * ------------------------------------------------------------------------------------------ */
+moe_status moe_event_create(void** event);
+moe_status moe_event_destroy(void* event);
+moe_status moe_event_record(void* event, hipStream_t stream);
+/* Waits for `stop`, then writes the milliseconds between the two recorded events. */
+moe_status moe_event_elapsed_ms(void* start, void* stop, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,291 @@
+// C ABI of libmoe: argument validation, workspace layout and kernel dispatch.
+// Every check runs on the host before anything is enqueued; on error nothing is launched and no
+// output is touched.
+#include <limits.h>
+
+#include "common.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool is_float_type(moe_dtype t) { return t == MOE_F32 || t == MOE_BF16; }
+
+inline size_t elem_size(moe_dtype t) { return t == MOE_F32 ? 4 : t == MOE_BF16 ? 2 : 1; }
+
+inline moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+moe_status check_topology(int T, int E, int k) {
+  if (T < 1 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+  if (E > kMaxExperts || k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(T) * k > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Small-batch (weight streaming) kernels take over at or below this many pairs.
+constexpr int kDecodeMaxPairs = 256;
+
+struct ExpertsLayout {
+  size_t cum_a, cum_b, h, h_scales, total;
+};
+
+ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, moe_dtype w) {
+  (void)d;
+  ExpertsLayout L{};
+  const size_t P = static_cast<size_t>(T) * k;
+  size_t off = 0;
+  L.cum_a = off;
+  off = align_up(off + (E + 1) * sizeof(int32_t));
+  L.cum_b = off;
+  off = align_up(off + (E + 1) * sizeof(int32_t));
+  L.h = off;
+  const size_t h_elem = (w == MOE_FP8_E4M3) ? 1 : (act == MOE_F32 ? 4 : 2);
+  off = align_up(off + P * f * h_elem);
+  L.h_scales = off;
+  if (w == MOE_FP8_E4M3) off = align_up(off + P * (f / kFp8Group) * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+__global__ void zero_f32_kernel(float* p, size_t n) {
+  size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i < n; i += static_cast<size_t>(gridDim.x) * blockDim.x) p[i] = 0.0f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_route(const float* logits, const void* x, moe_dtype x_dtype,
+                     const float* w_router, int T, int d, int E, int k, float* logits_out,
+                     int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  moe_status st = check_topology(T, E, k);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!logits) {
+    if (!x || !w_router || !logits_out || d < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (!is_float_type(x_dtype)) return MOE_ERR_UNSUPPORTED;
+    if (static_cast<long long>(T) * d > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    hipError_t e = launch_router_logits(x, x_dtype, w_router, T, d, E, logits_out, stream);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    logits = logits_out;
+  } else if (logits_out && logits_out != logits) {
+    hipError_t e = hipMemcpyAsync(logits_out, logits, sizeof(float) * static_cast<size_t>(T) * E,
+                                  hipMemcpyDeviceToDevice, stream);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  return dev(launch_topk_softmax(logits, T, E, k, topk_ids, topk_w, stream));
+}
+
+size_t moe_permute_workspace_size(int T, int k, int E) {
+  if (check_topology(T, E, k) != MOE_OK) return 0;
+  return align_up(permute_workspace_bytes(T * k, E));
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
+                       moe_dtype x_dtype, const float* x_scales, int d, void* x_perm,
+                       float* x_perm_scales, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  moe_status st = check_topology(T, E, k);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !counts || !offsets || !sorted_pair || !pair_pos) return MOE_ERR_INVALID_ARGUMENT;
+  const bool gather = x != nullptr || x_perm != nullptr;
+  if (gather) {
+    if (!x || !x_perm || d < 1) return MOE_ERR_INVALID_ARGUMENT;
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16 && x_dtype != MOE_FP8_E4M3)
+      return MOE_ERR_INVALID_ARGUMENT;
+    if (x_dtype == MOE_FP8_E4M3) {
+      if (d % kFp8Group) return MOE_ERR_UNSUPPORTED;
+      if (!x_scales || !x_perm_scales) return MOE_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (!workspace || workspace_bytes < moe_permute_workspace_size(T, k, E))
+    return workspace ? MOE_ERR_WORKSPACE_TOO_SMALL : MOE_ERR_INVALID_ARGUMENT;
+  const int P = T * k;
+  hipError_t e = launch_permute(topk_ids, P, E, counts, offsets, sorted_pair, pair_pos, workspace,
+                                stream);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (gather) {
+    e = launch_gather_rows(x, static_cast<size_t>(d) * elem_size(x_dtype), sorted_pair, P, k,
+                           x_perm, stream);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    if (x_dtype == MOE_FP8_E4M3) {
+      e = launch_gather_rows(x_scales, static_cast<size_t>(d / kFp8Group) * sizeof(float),
+                             sorted_pair, P, k, x_perm_scales, stream);
+      if (e != hipSuccess) return MOE_ERR_DEVICE;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status fp8_quantize_act(const void* x, moe_dtype x_dtype, int M, int K, int group,
+                            const int32_t* row_index, uint8_t* q, float* scales,
+                            hipStream_t stream) {
+  if (!x || !q || !scales || M < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!is_float_type(x_dtype)) return MOE_ERR_INVALID_ARGUMENT;
+  if (group != kFp8Group || K % kFp8Group) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 8)) return MOE_ERR_UNSUPPORTED;
+  return dev(launch_quantize_act(x, x_dtype, M, K, row_index, q, scales, stream));
+}
+
+moe_status fp8_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                               int block, uint8_t* q, float* scales, hipStream_t stream) {
+  if (!w || !q || !scales || batch < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!is_float_type(w_dtype)) return MOE_ERR_INVALID_ARGUMENT;
+  if (block != kFp8Group || N % kFp8Group || K % kFp8Group) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(batch) * (N / kFp8Group) * (K / kFp8Group) > INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  return dev(launch_quantize_weight(w, w_dtype, batch, N, K, q, scales, stream));
+}
+
+size_t moe_experts_workspace_size(int T, int d, int f, int E, int k, moe_dtype act_dtype,
+                                  moe_dtype w_dtype) {
+  if (check_topology(T, E, k) != MOE_OK || d < 1 || f < 1) return 0;
+  return experts_layout(T, d, f, E, k, act_dtype, w_dtype).total;
+}
+
+moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
+  if (!a) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_topology(a->T, a->E, a->k);
+  if (st != MOE_OK) return st;
+  if (a->d < 1 || a->f < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!a->x || !a->w_gate || !a->w_up || !a->w_down || !a->offsets || !a->sorted_pair || !a->y)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (a->y_layout != MOE_Y_PERMUTED && a->y_layout != MOE_Y_SLOTS && a->y_layout != MOE_Y_ACC_F32)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (a->y_layout != MOE_Y_PERMUTED && !a->topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!is_float_type(a->y_dtype)) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_dtype act = a->act_dtype, w = a->w_dtype;
+  const bool f32 = act == MOE_F32 && w == MOE_F32;
+  const bool bf16 = act == MOE_BF16 && w == MOE_BF16;
+  const bool fp8 = act == MOE_FP8_E4M3 && w == MOE_FP8_E4M3;
+  if (!f32 && !bf16 && !fp8) return MOE_ERR_UNSUPPORTED;
+  if (f32 && a->y_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (bf16 && (a->d % 64 || a->f % 64)) return MOE_ERR_UNSUPPORTED;
+  if (fp8) {
+    if (a->d % kFp8Group || a->f % kFp8Group) return MOE_ERR_UNSUPPORTED;
+    if (!a->x_scales || !a->s_gate || !a->s_up || !a->s_down) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const long long P = static_cast<long long>(a->T) * a->k;
+  // 32-bit element offsets inside the kernels
+  if (static_cast<long long>(a->T) * a->d > INT_MAX / 2 || P * a->f > INT_MAX / 2 ||
+      P * a->d > INT_MAX / 2 || static_cast<long long>(a->f) * a->d > INT_MAX / 4)
+    return MOE_ERR_UNSUPPORTED;
+  const ExpertsLayout L = experts_layout(a->T, a->d, a->f, a->E, a->k, act, w);
+  if (!a->workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  char* ws = static_cast<char*>(a->workspace);
+  ExpertsLaunch X{};
+  X.T = a->T;
+  X.d = a->d;
+  X.f = a->f;
+  X.E = a->E;
+  X.k = a->k;
+  X.a = a->x;
+  X.a_gather = 1;
+  X.a_scales = a->x_scales;
+  X.sorted_pair = a->sorted_pair;
+  X.w_gate = a->w_gate;
+  X.w_up = a->w_up;
+  X.w_down = a->w_down;
+  X.s_gate = a->s_gate;
+  X.s_up = a->s_up;
+  X.s_down = a->s_down;
+  X.offsets = a->offsets;
+  X.tile_cum_a = reinterpret_cast<int32_t*>(ws + L.cum_a);
+  X.tile_cum_b = reinterpret_cast<int32_t*>(ws + L.cum_b);
+  X.topk_w = a->topk_w;
+  X.y_layout = a->y_layout;
+  X.y_bf16 = a->y_dtype == MOE_BF16;
+  X.y = a->y;
+  X.h = ws + L.h;
+  X.h_scales = reinterpret_cast<float*>(ws + L.h_scales);
+  X.ev = a->events;
+
+  const bool decode = bf16 && P <= kDecodeMaxPairs && a->d % 128 == 0 && a->f % 128 == 0;
+  int bm_a, bm_b;
+  if (f32) { bm_a = bm_b = f32_tile_rows(); }
+  else if (fp8) { bm_a = fp8_tile_rows_gateup(); bm_b = fp8_tile_rows_down(); }
+  else if (decode) { bm_a = bm_b = decode_tile_rows(); }
+  else { bm_a = bf16_tile_rows_gateup(); bm_b = bf16_tile_rows_down(); }
+
+  hipError_t e = launch_tile_table(a->offsets, a->E, bm_a, bm_b,
+                                   const_cast<int32_t*>(X.tile_cum_a),
+                                   const_cast<int32_t*>(X.tile_cum_b), stream);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  if (a->y_layout == MOE_Y_ACC_F32) {
+    const size_t n = static_cast<size_t>(a->T) * a->d;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 65536))),
+                       dim3(256), 0, stream, static_cast<float*>(a->y), n);
+    if ((e = hipGetLastError()) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  if (f32) e = launch_experts_f32(X, stream);
+  else if (fp8) e = launch_experts_fp8(X, stream);
+  else if (decode) e = launch_experts_bf16_decode(X, stream);
+  else e = launch_experts_bf16(X, stream);
+  if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
+  return dev(e);
+}
+
+moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
+                       const int32_t* pair_pos, const float* topk_w, int T, int k, int d,
+                       void* out, moe_dtype out_dtype, hipStream_t stream) {
+  if (!y || !out || T < 1 || k < 1 || d < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (layout != MOE_Y_PERMUTED && layout != MOE_Y_SLOTS && layout != MOE_Y_ACC_F32)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!is_float_type(y_dtype) || !is_float_type(out_dtype)) return MOE_ERR_INVALID_ARGUMENT;
+  if (layout == MOE_Y_ACC_F32 && y_dtype != MOE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (layout == MOE_Y_PERMUTED && (!pair_pos || !topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+  if (static_cast<long long>(T) * k * d > (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  return dev(launch_combine(y, y_dtype, layout, pair_pos, topk_w, T, k, d, out, out_dtype, stream));
+}
+
+moe_status moe_event_create(void** event) {
+  if (!event) return MOE_ERR_INVALID_ARGUMENT;
+  hipEvent_t ev;
+  if (hipEventCreate(&ev) != hipSuccess) return MOE_ERR_DEVICE;
+  *event = ev;
+  return MOE_OK;
+}
+
+moe_status moe_event_destroy(void* event) {
+  if (!event) return MOE_ERR_INVALID_ARGUMENT;
+  return dev(hipEventDestroy(static_cast<hipEvent_t>(event)));
+}
+
+moe_status moe_event_record(void* event, hipStream_t stream) {
+  if (!event) return MOE_ERR_INVALID_ARGUMENT;
+  return dev(hipEventRecord(static_cast<hipEvent_t>(event), stream));
+}
+
+moe_status moe_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return MOE_ERR_INVALID_ARGUMENT;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return MOE_ERR_DEVICE;
+  return dev(hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)));
+}
+
+}  // extern "C"

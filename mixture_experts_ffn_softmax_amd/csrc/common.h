@@ -1,0 +1,133 @@
+// Internal helpers shared by the HIP sources of libmoe (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kFp8Group = 128;   // activation group width and weight block edge
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+// Raw 16-byte vector (a native vector type, so copies stay in registers).
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// ---- scalar formats -------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// OCP E4M3FN encode: round to nearest even, saturate to +-448 (0x7E / 0xFE); zero keeps its sign.
+// Normal range: round the fp32 mantissa from 23 to 3 bits with the add-half-minus-one-plus-lsb
+// trick, then rebias the exponent (fp32 bias 127 -> e4m3 bias 7). Below 2^-6 the e4m3 grid is the
+// uniform subnormal step 2^-9, so the code is rint(|v| * 2^9).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;                 // |v| >= 448 (and inf/nan)
+  if (a < 0x3c800000u) {                                     // |v| < 2^-6
+    float m = rintf(__uint_as_float(a) * 512.0f);
+    return sign | static_cast<uint32_t>(m);
+  }
+  uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+  return sign | ((r >> 20) - (120u << 3));
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t ex = (c >> 3) & 0xfu, man = c & 0x7u;
+  float v = ex == 0 ? static_cast<float>(man) * 0x1p-9f
+                    : __uint_as_float(((ex + 120u) << 23) | (man << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
+// ---- wave helpers -------------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+// ---- grouped-GEMM tile schedule ----------------------------------------------------------------
+//
+// The rows of a grouped GEMM are the P pairs in expert-sorted order; expert e owns rows
+// [offsets[e], offsets[e+1]). A row tile never straddles two experts, so expert e contributes
+// ceil(M_e / BM) row tiles. tile_cum[e] = number of row tiles of experts < e (tile_cum[E] = total).
+// Logical tiles are numbered expert-major, then output-column tile, then row tile, so that the
+// row tiles sharing one weight panel are adjacent and run together.
+
+struct TileCoord {
+  int e;       // expert
+  int row0;    // first sorted row of the tile
+  int rows;    // valid rows in the tile (1..BM)
+  int ntile;   // output-column tile index
+};
+
+// Maps a hardware block index to a tile; returns false for blocks beyond the real tile count.
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8); each XCD is
+// handed one contiguous range of logical tiles so that blocks sharing weight panels and input rows
+// share that XCD's L2.
+__device__ __forceinline__ bool map_tile(const int32_t* __restrict__ tile_cum,
+                                         const int32_t* __restrict__ offsets, int E, int BM,
+                                         int NT, TileCoord& tc) {
+  const int total = tile_cum[E] * NT;
+  const int chunk = (total + 7) / 8;
+  const int b = blockIdx.x;
+  const int slot = b >> 3;
+  if (slot >= chunk) return false;
+  const int logical = (b & 7) * chunk + slot;
+  if (logical >= total) return false;
+  // largest e with tile_cum[e] * NT <= logical (experts with no rows have equal tile_cum entries)
+  int lo = 0, hi = E;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (tile_cum[mid] * NT <= logical) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int nrt = tile_cum[e + 1] - tile_cum[e];
+  const int rem = logical - tile_cum[e] * NT;
+  const int ntile = rem / nrt;
+  const int rt = rem - ntile * nrt;
+  const int start = offsets[e] + rt * BM;
+  tc.e = e;
+  tc.row0 = start;
+  tc.rows = min(BM, offsets[e + 1] - start);
+  tc.ntile = ntile;
+  return true;
+}
+
+// Upper bound on the number of row tiles: sum_e ceil(M_e/BM) <= floor(P/BM) + min(E, P).
+inline int max_row_tiles(int P, int E, int BM) { return P / BM + (E < P ? E : P); }
+
+}  // namespace moe

@@ -1,0 +1,77 @@
+// Kernel launchers of libmoe (internal). Arguments are validated by the C ABI layer before any of
+// these is called; every launcher only enqueues work on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+hipError_t launch_router_logits(const void* x, moe_dtype x_dtype, const float* wr, int T, int d,
+                                int E, float* logits, hipStream_t stream);
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                               hipStream_t stream);
+
+size_t permute_workspace_bytes(int P, int E);
+hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, void* workspace,
+                          hipStream_t stream);
+hipError_t launch_gather_rows(const void* x, size_t row_bytes, const int32_t* sorted_pair, int P,
+                              int k, void* x_perm, hipStream_t stream);
+
+hipError_t launch_quantize_act(const void* x, moe_dtype x_dtype, int M, int K,
+                               const int32_t* row_index, uint8_t* q, float* scales,
+                               hipStream_t stream);
+hipError_t launch_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                                  uint8_t* q, float* scales, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
+                          const int32_t* pair_pos, const float* topk_w, int T, int k, int d,
+                          void* out, moe_dtype out_dtype, hipStream_t stream);
+
+hipError_t launch_tile_table(const int32_t* offsets, int E, int bm_a, int bm_b, int32_t* cum_a,
+                             int32_t* cum_b, hipStream_t stream);
+
+// Everything one experts forward needs, resolved by the ABI layer.
+struct ExpertsLaunch {
+  int T, d, f, E, k;
+  const void* a;              // x [T, d] (a_gather = 1: row of pair = sorted_pair[pos] / k) or
+  int a_gather;               // x_perm [P, d] in sorted order (a_gather = 0)
+  const float* a_scales;      // fp8: [T, d/128] (gather) or [P, d/128]
+  const int32_t* sorted_pair;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  const int32_t* offsets;
+  const int32_t* tile_cum_a;  // row tiles of the gate/up GEMM
+  const int32_t* tile_cum_b;  // row tiles of the down GEMM
+  const float* topk_w;
+  int y_layout;
+  int y_bf16;
+  void* y;
+  void* h;                    // workspace: hidden activations [P, f]
+  float* h_scales;            // fp8: [P, f/128]
+  void** ev;                  // nullable timing events (4)
+};
+
+int f32_tile_rows();
+hipError_t launch_experts_f32(const ExpertsLaunch& L, hipStream_t stream);
+
+int bf16_tile_rows_gateup();
+int bf16_tile_rows_down();
+hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream);
+
+int decode_tile_rows();
+hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream);
+
+int fp8_tile_rows_gateup();
+int fp8_tile_rows_down();
+hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,158 @@
+// Grouping the (token, slot) pairs by expert: per-chunk histograms, one scan over
+// (chunk x expert), a stable scatter, and an optional coalesced row gather.
+//
+// Transformers "Experts backends" page, backends table row grouped_mm: tokens are sorted by their
+// selected expert so one grouped GEMM projects them all. The order inside an expert is the flat
+// pair index (stable), which makes the permutation deterministic.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;       // pairs per block in the histogram and scatter kernels
+constexpr int kScatterThreads = 256;
+
+__global__ __launch_bounds__(256) void chunk_histogram_kernel(const int32_t* __restrict__ ids,
+                                                              int P, int E,
+                                                              int32_t* __restrict__ chunk_hist) {
+  __shared__ int hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kChunk;
+  const int p1 = min(P, p0 + kChunk);
+  for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&hist[ids[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    chunk_hist[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
+}
+
+// One block of 1024 threads. counts[e] = sum over chunks; offsets = exclusive scan over experts;
+// chunk_base[c][e] = offsets[e] + pairs of expert e in chunks before c.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ chunk_hist,
+                                                    int nchunks, int E, int P,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ chunk_base) {
+  __shared__ int s[kMaxExperts];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) total += chunk_hist[static_cast<size_t>(c) * E + e];
+    counts[e] = total;
+  }
+  s[e] = (e < E) ? total : 0;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 1024 entries.
+  for (int o = 1; o < kMaxExperts; o <<= 1) {
+    int v = (e >= o) ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    int run = s[e] - total;  // exclusive
+    offsets[e] = run;
+    for (int c = 0; c < nchunks; ++c) {
+      chunk_base[static_cast<size_t>(c) * E + e] = run;
+      run += chunk_hist[static_cast<size_t>(c) * E + e];
+    }
+  }
+  if (e == 0) offsets[E] = P;
+}
+
+// Stable scatter. The chunk's pairs are taken 256 at a time in flat order; inside a wave, lanes
+// holding the same expert are found with one ballot per expert-id bit, and a lane's rank is the
+// number of such lanes below it. The four waves then claim their positions one after another from
+// the running per-expert cursor in LDS, so positions follow the flat pair order exactly.
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int id_bits,
+    const int32_t* __restrict__ chunk_base, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_pos) {
+  __shared__ int cursor[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    cursor[e] = chunk_base[static_cast<size_t>(blockIdx.x) * E + e];
+  __syncthreads();
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int p0 = blockIdx.x * kChunk;
+  const int p1 = min(P, p0 + kChunk);
+  for (int base = p0; base < p1; base += kScatterThreads) {
+    const int p = base + threadIdx.x;
+    const bool valid = p < p1;
+    const int e = valid ? ids[p] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < id_bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      match &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(match & below);
+    const int cnt = __popcll(match);
+    for (int w = 0; w < kScatterThreads / kWave; ++w) {
+      if (w == wave && valid) {
+        const int pos = cursor[e] + rank;
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+        if (rank == 0) cursor[e] = pos + cnt;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// x_perm[r] = x[sorted_pair[r] / k]; one wave per row, 16-byte vectors when the row allows it.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ x,
+                                                          size_t row_bytes,
+                                                          const int32_t* __restrict__ sorted_pair,
+                                                          int P, int k,
+                                                          uint8_t* __restrict__ x_perm) {
+  const int r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (r >= P) return;
+  const int t = sorted_pair[r] / k;
+  const uint8_t* src = x + static_cast<size_t>(t) * row_bytes;
+  uint8_t* dst = x_perm + static_cast<size_t>(r) * row_bytes;
+  const int lane = lane_id();
+  if ((row_bytes & 15) == 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(x_perm)) & 15) == 0) {
+    const size_t n = row_bytes / 16;
+    for (size_t i = lane; i < n; i += kWave)
+      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+  } else {
+    for (size_t i = lane; i < row_bytes; i += kWave) dst[i] = src[i];
+  }
+}
+
+}  // namespace
+
+size_t permute_workspace_bytes(int P, int E) {
+  const size_t nchunks = (static_cast<size_t>(P) + kChunk - 1) / kChunk;
+  return 2 * nchunks * static_cast<size_t>(E) * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, void* workspace,
+                          hipStream_t stream) {
+  const int nchunks = (P + kChunk - 1) / kChunk;
+  int32_t* chunk_hist = static_cast<int32_t*>(workspace);
+  int32_t* chunk_base = chunk_hist + static_cast<size_t>(nchunks) * E;
+  int id_bits = 0;
+  while ((1 << id_bits) < E) ++id_bits;
+  hipLaunchKernelGGL(chunk_histogram_kernel, dim3(nchunks), dim3(256), 0, stream, ids, P, E,
+                     chunk_hist);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, stream, chunk_hist, nchunks, E, P,
+                     counts, offsets, chunk_base);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(kScatterThreads), 0, stream, ids, P, E,
+                     id_bits, chunk_base, sorted_pair, pair_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, size_t row_bytes, const int32_t* sorted_pair, int P,
+                              int k, void* x_perm, hipStream_t stream) {
+  dim3 grid((P + 3) / 4), block(256);
+  hipLaunchKernelGGL(gather_rows_kernel, grid, block, 0, stream, static_cast<const uint8_t*>(x),
+                     row_bytes, sorted_pair, P, k, static_cast<uint8_t*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,145 @@
+// Fine-grained FP8 quantisation (Transformers "Fine-grained FP8" page, introduction): activations
+// per token per 128 input channels with run-time scales, weights per 128x128 block.
+// Rule for one group/block: s = amax / 448 (fp32, IEEE division; s = 1 if all zero),
+// q = e4m3(v / s), round-to-nearest-even, saturating at +-448.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+template <typename XT>
+__device__ __forceinline__ void load8(const XT* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
+  uint4 r = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// One wave covers 4 groups of one row: 16 lanes per group, 8 consecutive elements per lane.
+template <typename XT>
+__global__ __launch_bounds__(256) void quantize_act_kernel(const XT* __restrict__ x, int M, int K,
+                                                           const int32_t* __restrict__ row_index,
+                                                           uint8_t* __restrict__ q,
+                                                           float* __restrict__ scales) {
+  const int G = K / kFp8Group;
+  const int waves_per_row = (G + 3) / 4;
+  const int wid = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int row = wid / waves_per_row;
+  if (row >= M) return;
+  const int lane = lane_id();
+  const int g = (wid - row * waves_per_row) * 4 + lane / 16;
+  const bool active = g < G;
+  const int src_row = row_index ? row_index[row] : row;
+  const int col = g * kFp8Group + (lane & 15) * 8;
+  float v[8];
+  if (active) {
+    load8(x + static_cast<size_t>(src_row) * K + col, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (!active) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / s) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / s) << (8 * i);
+  *reinterpret_cast<uint2*>(q + static_cast<size_t>(row) * K + col) = make_uint2(lo, hi);
+  if ((lane & 15) == 0) scales[static_cast<size_t>(row) * G + g] = s;
+}
+
+// One block of 256 threads per 128x128 block: each thread owns 64 elements (16 rows x 4 columns
+// per pass, 4 bytes of output each), block-wide amax through LDS.
+template <typename WT>
+__global__ __launch_bounds__(256) void quantize_weight_kernel(const WT* __restrict__ w, int N,
+                                                              int K, uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales) {
+  const int KB = K / kFp8Group, NB = N / kFp8Group;
+  const int kb = blockIdx.x % KB;
+  const int nb = (blockIdx.x / KB) % NB;
+  const size_t mat = blockIdx.x / (KB * NB);
+  const WT* src = w + mat * N * static_cast<size_t>(K);
+  uint8_t* dst = q + mat * N * static_cast<size_t>(K);
+  const int c4 = (threadIdx.x & 31) * 4;   // column within block
+  const int r0 = threadIdx.x >> 5;         // 0..7
+  float v[16][4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const size_t off = static_cast<size_t>(nb * kFp8Group + r0 + 8 * i) * K + kb * kFp8Group + c4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float x;
+      if constexpr (sizeof(WT) == 2) x = bf16_bits_to_f32(src[off + c]);
+      else x = src[off + c];
+      v[i][c] = x;
+      amax = fmaxf(amax, fabsf(x));
+    }
+  }
+  amax = wave_max(amax);
+  __shared__ float red[4];
+  if (lane_id() == 0) red[threadIdx.x / kWave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const size_t off = static_cast<size_t>(nb * kFp8Group + r0 + 8 * i) * K + kb * kFp8Group + c4;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) packed |= e4m3_encode(v[i][c] / s) << (8 * c);
+    *reinterpret_cast<uint32_t*>(dst + off) = packed;
+  }
+  if (threadIdx.x == 0) scales[(mat * NB + nb) * KB + kb] = s;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const void* x, moe_dtype x_dtype, int M, int K,
+                               const int32_t* row_index, uint8_t* q, float* scales,
+                               hipStream_t stream) {
+  const int G = K / kFp8Group;
+  const long waves = static_cast<long>(M) * ((G + 3) / 4);
+  dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
+  if (x_dtype == MOE_BF16)
+    hipLaunchKernelGGL(quantize_act_kernel<uint16_t>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), M, K, row_index, q, scales);
+  else
+    hipLaunchKernelGGL(quantize_act_kernel<float>, grid, block, 0, stream,
+                       static_cast<const float*>(x), M, K, row_index, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                                  uint8_t* q, float* scales, hipStream_t stream) {
+  const long blocks = static_cast<long>(batch) * (N / kFp8Group) * (K / kFp8Group);
+  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (w_dtype == MOE_BF16)
+    hipLaunchKernelGGL(quantize_weight_kernel<uint16_t>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(w), N, K, q, scales);
+  else
+    hipLaunchKernelGGL(quantize_weight_kernel<float>, grid, block, 0, stream,
+                       static_cast<const float*>(w), N, K, q, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,162 @@
+"""The C ABI library: it loads without a GPU, exports every symbol include/moe.h declares, and
+rejects bad arguments on the host before anything is enqueued (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_ffn_softmax_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+# A non-null address that is never dereferenced: every call below fails validation first.
+FAKE = ctypes.c_void_p(0x1000)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from mixture_experts_ffn_softmax_amd import build
+        build.build()
+    return moe.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_experts_forward", "moe_combine",
+              "fp8_quantize_act"):
+        assert n in names
+    assert sorted(moe.EXPORTED_SYMBOLS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in _declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def test_route_validation(lib):
+    INV, UNS = moe.MOE_ERR_INVALID_ARGUMENT, moe.MOE_ERR_UNSUPPORTED
+    # k > E, k < 1, T < 1
+    assert lib.moe_route(FAKE, None, 0, None, 4, 0, 2, 3, None, FAKE, FAKE, None) == INV
+    assert lib.moe_route(FAKE, None, 0, None, 4, 0, 8, 0, None, FAKE, FAKE, None) == INV
+    assert lib.moe_route(FAKE, None, 0, None, 0, 0, 8, 2, None, FAKE, FAKE, None) == INV
+    # too many experts / too large k
+    assert lib.moe_route(FAKE, None, 0, None, 4, 0, 2048, 2, None, FAKE, FAKE, None) == UNS
+    assert lib.moe_route(FAKE, None, 0, None, 4, 0, 64, 33, None, FAKE, FAKE, None) == UNS
+    # missing outputs
+    assert lib.moe_route(FAKE, None, 0, None, 4, 0, 8, 2, None, None, FAKE, None) == INV
+    # computing logits needs x, w_router and logits_out
+    assert lib.moe_route(None, FAKE, moe.MOE_BF16, None, 4, 64, 8, 2, FAKE, FAKE, FAKE,
+                         None) == INV
+    assert lib.moe_route(None, FAKE, moe.MOE_BF16, FAKE, 4, 64, 8, 2, None, FAKE, FAKE,
+                         None) == INV
+    assert lib.moe_route(None, FAKE, moe.MOE_FP8_E4M3, FAKE, 4, 64, 8, 2, FAKE, FAKE, FAKE,
+                         None) == UNS
+
+
+def test_permute_validation(lib):
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    ws = lib.moe_permute_workspace_size(16, 2, 8)
+    assert ws > 0
+    assert lib.moe_permute_workspace_size(16, 9, 8) == 0
+    args = [FAKE, 16, 2, 8, FAKE, FAKE, FAKE, FAKE, None, 0, None, 0, None, None]
+    assert lib.moe_permute(*args, FAKE, ws - 1, None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_permute(*args, None, ws, None) == INV
+    bad = list(args)
+    bad[4] = None  # counts
+    assert lib.moe_permute(*bad, FAKE, ws, None) == INV
+    # gather needs both x and x_perm; fp8 gather needs scales and d % 128 == 0
+    g = list(args)
+    g[8] = FAKE
+    assert lib.moe_permute(*g, FAKE, ws, None) == INV
+    g[9], g[11], g[12] = moe.MOE_FP8_E4M3, 100, FAKE
+    assert lib.moe_permute(*g, FAKE, ws, None) == moe.MOE_ERR_UNSUPPORTED
+    g[11] = 128
+    assert lib.moe_permute(*g, FAKE, ws, None) == INV
+
+
+def test_quantize_validation(lib):
+    UNS, INV = moe.MOE_ERR_UNSUPPORTED, moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.fp8_quantize_act(FAKE, moe.MOE_BF16, 4, 100, 128, None, FAKE, FAKE, None) == UNS
+    assert lib.fp8_quantize_act(FAKE, moe.MOE_BF16, 4, 256, 64, None, FAKE, FAKE, None) == UNS
+    assert lib.fp8_quantize_act(FAKE, moe.MOE_FP8_E4M3, 4, 256, 128, None, FAKE, FAKE,
+                                None) == INV
+    assert lib.fp8_quantize_act(None, moe.MOE_BF16, 4, 256, 128, None, FAKE, FAKE, None) == INV
+    assert lib.fp8_quantize_act(ctypes.c_void_p(0x1002), moe.MOE_BF16, 4, 256, 128, None, FAKE,
+                                FAKE, None) == UNS  # misaligned
+    assert lib.fp8_quantize_weight(FAKE, moe.MOE_F32, 2, 128, 200, 128, FAKE, FAKE, None) == UNS
+    assert lib.fp8_quantize_weight(FAKE, moe.MOE_F32, 0, 128, 256, 128, FAKE, FAKE, None) == INV
+
+
+def _args(**kw):
+    base = dict(T=32, d=256, f=512, E=8, k=2, act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_BF16,
+                y_dtype=moe.MOE_BF16, y_layout=moe.MOE_Y_SLOTS, x=0x1000, x_scales=None,
+                w_gate=0x1000, w_up=0x1000, w_down=0x1000, s_gate=None, s_up=None, s_down=None,
+                offsets=0x1000, sorted_pair=0x1000, topk_w=0x1000, y=0x1000, workspace=0x1000,
+                workspace_bytes=1 << 40, events=None)
+    base.update(kw)
+    return moe.moe_experts_args(**base)
+
+
+def _fwd(lib, **kw):
+    a = _args(**kw)
+    return lib.moe_experts_forward(ctypes.byref(a), None)
+
+
+def test_experts_validation(lib):
+    INV, UNS = moe.MOE_ERR_INVALID_ARGUMENT, moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_experts_forward(None, None) == INV
+    assert _fwd(lib, k=9) == INV
+    assert _fwd(lib, d=0) == INV
+    assert _fwd(lib, x=None) == INV
+    assert _fwd(lib, topk_w=None) == INV                      # slots need routing weights
+    assert _fwd(lib, y_layout=7) == INV
+    assert _fwd(lib, w_dtype=moe.MOE_FP8_E4M3) == UNS          # mixed bf16 act / fp8 weights
+    assert _fwd(lib, act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32) == UNS  # f32 needs f32 y
+    assert _fwd(lib, d=200) == UNS                             # bf16 path needs d % 64 == 0
+    fp8 = dict(act_dtype=moe.MOE_FP8_E4M3, w_dtype=moe.MOE_FP8_E4M3)
+    assert _fwd(lib, d=192, **fp8) == UNS                      # fp8 needs d % 128 == 0
+    assert _fwd(lib, **fp8) == INV                             # fp8 needs the scales
+    need = lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_BF16, moe.MOE_BF16)
+    assert need >= 32 * 2 * 512 * 2
+    assert _fwd(lib, workspace_bytes=need - 1) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert _fwd(lib, workspace=None) == INV
+    assert lib.moe_experts_workspace_size(32, 256, 512, 8, 9, moe.MOE_BF16, moe.MOE_BF16) == 0
+
+
+def test_combine_validation(lib):
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, moe.MOE_Y_PERMUTED, None, FAKE, 4, 2, 64, FAKE,
+                           moe.MOE_BF16, None) == INV
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, moe.MOE_Y_ACC_F32, None, None, 4, 2, 64, FAKE,
+                           moe.MOE_BF16, None) == INV
+    assert lib.moe_combine(FAKE, moe.MOE_FP8_E4M3, moe.MOE_Y_SLOTS, None, None, 4, 2, 64, FAKE,
+                           moe.MOE_BF16, None) == INV
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, 5, None, None, 4, 2, 64, FAKE, moe.MOE_BF16,
+                           None) == INV
+
+
+def test_event_helpers_validate(lib):
+    assert lib.moe_event_create(None) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_event_destroy(None) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_event_elapsed_ms(None, None, None) == moe.MOE_ERR_INVALID_ARGUMENT
