@@ -144,6 +144,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain fp32 copy kernel (out = in * 1) over this many MiB, "
+                         "3 times, to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -157,6 +161,16 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("copy probe: %d MiB read + %d MiB written per launch" % (args.copy_probe_mib,
+                                                                    args.copy_probe_mib))
+        del src, dst
     spec = synth.MIXTRAL_PREFILL
     T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
     log("generating %s inputs" % spec.name)
@@ -175,6 +189,8 @@ def main():
     Wg, Wu, Wd = (up(a) for a in W_np)
     log("inputs ready in %.1fs" % (time.perf_counter() - t0))
 
+    if args.no_prefill:
+        args.steps = 1
     layer = Layer(moe, spec, x, Wr, Wg, Wu, Wd, max(args.steps, 1))
     el = time_steps(layer, args.steps, args.warmup)
     ms = el / args.steps * 1e3

@@ -6,13 +6,13 @@
 // SwiGLU). The rows of both GEMMs are the expert-sorted pairs; the gate/up GEMM reads each pair's
 // token row straight from x (gather on load), so no permuted copy of x is needed.
 //
-// Tiling: 256 x 256 output tile per workgroup, K staged 64 at a time through LDS (double
-// buffered, 2 x 64 KB). Four waves each own a 128 x 128 quadrant = 4 x 4 MFMA 32x32 blocks, so
-// every A fragment read from LDS feeds 4 MFMAs and every B fragment 4 MFMAs. LDS rows are 128 B;
-// the 16-byte chunk c of row r is stored at chunk position c ^ (r & 7), which makes both the
-// row-wise stores and the MFMA fragment reads (32 rows x one chunk) bank-conflict free.
-// For the gate/up GEMM the 256 B-rows of a tile are 128 gate rows and the same 128 up rows, so
-// each wave holds matching gate and up accumulators and applies SwiGLU in registers.
+// Tiling: 256 x 256 output tile per workgroup of 8 waves (2 per SIMD); WM x WN waves each own a
+// (256/WM) x (256/WN) block of 32x32 MFMA tiles. K is staged 32 at a time through a ring of four
+// LDS buffers that buffer_load ... lds (global -> LDS DMA, no staging registers) fills three
+// stages ahead; one vmcnt wait and one barrier per stage. For the gate/up GEMM the 256 B-rows of
+// a tile are 128 gate rows and the same 128 up rows; each wave holds matching gate and up
+// accumulators and applies SwiGLU in registers. Results leave through LDS as whole 16-byte row
+// segments.
 #include "common.h"
 #include "launch.h"
 
@@ -21,8 +21,6 @@ namespace {
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 64;
-constexpr int kTileElems = kBM * kBK;   // bf16 elements per operand tile
 constexpr int kGateUp = 0;
 constexpr int kDown = 1;
 
@@ -34,6 +32,7 @@ struct Bf16GemmArgs {
   const uint16_t* b0;         // gate/up: W_gate [E, N, K]; down: W_down [E, N, K]
   const uint16_t* b1;         // gate/up: W_up [E, N, K]
   int K, N;
+  int a_rows;                 // rows of a (bounds of the buffer descriptor)
   const int32_t* offsets;
   const int32_t* tile_cum;
   int E;
@@ -43,21 +42,6 @@ struct Bf16GemmArgs {
   const float* topk_w;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
-
-// Loads the thread's 8 A chunks and 8 B chunks (16 bytes each) of one K slice; B rows 0..127 of
-// the tile (i < 4) come from b0, rows 128..255 from b1.
-__device__ __forceinline__ void gload8(u32x4_t (&ra)[8], u32x4_t (&rb)[8], const char* abase,
-                                       const char* b0base, const char* b1base,
-                                       const uint32_t (&aoff)[8], const uint32_t (&boff)[8],
-                                       uint32_t kbytes) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ra[i] = *reinterpret_cast<const u32x4_t*>(abase + aoff[i] + kbytes);
-    rb[i] = *reinterpret_cast<const u32x4_t*>((i < 4 ? b0base : b1base) + boff[i] + kbytes);
-  }
-}
-
 __device__ __forceinline__ u32x2_t pack_bf16x4(float4 v) {
   u32x2_t o;
   o[0] = f32_to_bf16_bits(v.x) | (static_cast<uint32_t>(f32_to_bf16_bits(v.y)) << 16);
@@ -65,156 +49,241 @@ __device__ __forceinline__ u32x2_t pack_bf16x4(float4 v) {
   return o;
 }
 
-__device__ __forceinline__ void lstore8(uint16_t* buf, const u32x4_t (&ra)[8], const u32x4_t (&rb)[8],
-                                        const uint32_t (&soff)[8]) {
+// ---------------------------------------------------------------------------------------------
+// Staging: each wave-level DMA instruction writes 1 KB = 16 rows x 64 B; lane l of it fetches the global
+// chunk that belongs at row l / 4, chunk position l % 4. Rows are 64 B (4 chunks of 16 B); the
+// logical chunk c of row r sits at position c ^ ((r >> 2) & 3), so 16 consecutive rows read at
+// one logical chunk hit 16 distinct 16-byte slots of a 256-byte bank line (conflict free).
+// ---------------------------------------------------------------------------------------------
+constexpr int kBK3 = 32;
+constexpr int kTile3 = kBM * kBK3 * 2;   // bytes per operand per stage (16 KB)
+
+__device__ __forceinline__ int swz3(int row, int chunk) {  // byte offset in a 256x64B tile
+  return row * (kBK3 * 2) + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = N and expcnt / lgkmcnt left at their maximum (no wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
+
+// Buffer resource for raw byte addressing of [base, base + bytes) (out-of-range reads return 0).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = static_cast<int>(a & 0xffffffffu);
+  r[1] = static_cast<int>(a >> 32);   // stride 0
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;                  // raw buffer, 32-bit data format
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<size_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// One wave-wide 16-byte-per-lane DMA from global memory straight into LDS: lane l's 16 bytes land
+// at lds + 16 l. Issued as inline asm so the compiler does not add LDS-DMA waits of its own; the
+// GEMM loop places explicit vmcnt waits before its barriers instead (there are no other vector
+// memory instructions in that loop).
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4_t rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+struct Dma3 {
+  i32x4_t ra, rb0, rb1;
+  uint32_t aoff[2], boff[2];   // per-lane byte offsets of the thread's two A and two B rows
+};
+
+template <int MI, int NJ>
+struct Frag3 {
+  bf16x8_t a[MI], b[NJ];
+};
+
+template <int MODE, int MI, int NJ>
+__device__ __forceinline__ void read_frags3(Frag3<MI, NJ>& f, const char* As, const char* Bs,
+                                            int arow0, int bcol0, int ks, int lane) {
+  const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    *reinterpret_cast<u32x4_t*>(buf + soff[i]) = ra[i];
-    *reinterpret_cast<u32x4_t*>(buf + kTileElems + soff[i]) = rb[i];
+  for (int i = 0; i < MI; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + swz3(arow0 + i * 32 + (lane & 31), ch));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int brow = MODE == kGateUp
+                         ? (j < NJ / 2 ? bcol0 + j * 32 : 128 + bcol0 + (j - NJ / 2) * 32)
+                         : bcol0 + j * 32;
+    f.b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz3(brow + (lane & 31), ch));
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(Bf16GemmArgs p) {
+template <int MI, int NJ>
+__device__ __forceinline__ void mfma3(f32x16_t (&acc)[MI][NJ], const Frag3<MI, NJ>& f) {
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Issues the DMA of stage `st` into one ring buffer (A tile then B tile): wave w fills rows
+// (2w + i) * 16 .. +15 of each operand (i = 0, 1); B rows 0..127 come from rb0, 128..255 from rb1.
+// Stages past the end of K re-read the last stage (never used), so every access stays in bounds.
+__device__ __forceinline__ void dma3(const char* buf, const Dma3& d, int st, int nst, int wave) {
+  const uint32_t kb = static_cast<uint32_t>(min(st, nst - 1)) * kBK3 * 2u;
+  const uint32_t base = lds_offset(buf);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dma16(base + (wave * 2 + i) * 1024, d.aoff[i], d.ra, kb);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    dma16(base + kTile3 + (wave * 2 + i) * 1024, d.boff[i], wave < 4 ? d.rb0 : d.rb1, kb);
+}
+
+template <int MODE, int WM, int WN>
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
+  static_assert(WM * WN == 8, "8 waves");
+  constexpr int MI = kBM / WM / 32;
+  constexpr int NJ = kBN / WN / 32;
   const int NT = MODE == kGateUp ? (p.N + 127) / 128 : (p.N + kBN - 1) / kBN;
   TileCoord tc;
   if (!map_tile(p.tile_cum, p.offsets, p.E, kBM, NT, tc)) return;
+  // the tile coordinates are block-uniform; say so, so descriptors and LDS bases live in SGPRs
+  tc.e = __builtin_amdgcn_readfirstlane(tc.e);
+  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+  tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
+  tc.ntile = __builtin_amdgcn_readfirstlane(tc.ntile);
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * kTileElems];
+  // Ring of four stage buffers, contiguous so the epilogue can reuse the whole 128 KB.
+  __shared__ __attribute__((aligned(1024))) char ring[4 * 2 * kTile3];
+  char* const ring0 = ring;
+  char* const ring1 = ring + 2 * kTile3;
+  char* const ring2 = ring + 4 * kTile3;
+  char* const ring3 = ring + 6 * kTile3;
   __shared__ int row_pair[kBM];
   __shared__ float row_w[kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int arow0 = wm * (kBM / WM);
+  const int bcol0 = MODE == kGateUp ? wn * (128 / WN) : wn * (kBN / WN);
 
   if (MODE == kDown) {
-    const int rr = min(tid, tc.rows - 1);
-    const int pair = p.sorted_pair[tc.row0 + rr];
-    row_pair[tid] = pair;
-    row_w[tid] = p.topk_w ? p.topk_w[pair] : 1.0f;
+    for (int r = tid; r < kBM; r += 512) {
+      const int rr = min(r, tc.rows - 1);
+      const int pair = p.sorted_pair[tc.row0 + rr];
+      row_pair[r] = pair;
+      row_w[r] = p.topk_w ? p.topk_w[pair] : 1.0f;
+    }
   }
 
-  // Global -> register -> LDS staging: thread covers rows i*32 + tid/8 (i = 0..7), 16-byte chunk
-  // tid%8 of the 128-byte K slice. Addresses are 32-bit byte offsets from uniform bases.
-  const int lrow = tid >> 3, lch = tid & 7;
-  const char* abase = reinterpret_cast<const char*>(p.a);
+  // DMA addressing: wave w fills rows (2w + i) * 16 .. +15 of each operand tile (i = 0, 1);
+  // lane l supplies row (2w + i) * 16 + l / 4 at chunk position l % 4.
+  Dma3 d;
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
-  const char* b0base = reinterpret_cast<const char*>(p.b0 + tc.e * wstride);
-  const char* b1base = MODE == kGateUp ? reinterpret_cast<const char*>(p.b1 + tc.e * wstride)
-                                       : b0base;
-  uint32_t aoff[8], boff[8];
+  d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K * 2u);
+  d.rb0 = make_rsrc(p.b0 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u);
+  d.rb1 = MODE == kGateUp ? make_rsrc(p.b1 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u)
+                          : d.rb0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = i * 32 + lrow;
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave * 2 + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     const int pos = tc.row0 + min(r, tc.rows - 1);
     const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
-    aoff[i] = (static_cast<uint32_t>(arow) * p.K + lch * 8) * 2u;
+    d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
     const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
                                   : min(tc.ntile * kBN + r, p.N - 1);
-    boff[i] = (static_cast<uint32_t>(n) * p.K + lch * 8) * 2u;
+    d.boff[i] = static_cast<uint32_t>(n) * p.K * 2u + c * 16;
   }
-  uint32_t soff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) soff[i] = swz(i * 32 + lrow, lch);
 
-  u32x4_t ra[8], rb[8];
-
-  f32x16_t acc[4][4];
+  f32x16_t acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nst = p.K / kBK;
-  gload8(ra, rb, abase, b0base, b1base, aoff, boff, 0u);
-  lstore8(smem, ra, rb, soff);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nst) {
-      const uint32_t kb = static_cast<uint32_t>(s + 1) * kBK * 2u;
-      gload8(ra, rb, abase, b0base, b1base, aoff, boff, kb);
-    }
-    const uint16_t* As = smem + buf * 2 * kTileElems;
-    const uint16_t* Bs = As + kTileElems;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      bf16x8_t af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + swz(wm * 128 + i * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int brow = MODE == kGateUp
-                             ? ((j < 2) ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32)
-                             : wn * 128 + j * 32;
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(brow + (lane & 31), ch));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (s + 1 < nst) lstore8(smem + (buf ^ 1) * 2 * kTileElems, ra, rb, soff);
-    __syncthreads();
-  }
+  const int nst = p.K / kBK3;
+  dma3(ring0, d, 0, nst, wave);
+  dma3(ring1, d, 1, nst, wave);
+  dma3(ring2, d, 2, nst, wave);
+  Frag3<MI, NJ> f0, f1;
 
-  // Accumulator layout of a 32x32 block: lane l holds column l % 32 and rows
-  // 8 * (r / 4) + 4 * (l / 32) + r % 4 for r = 0..15. Results go through LDS so that global
-  // stores are whole 16-byte row segments.
+#define MOE_STAGE3(CUR, NXT3, S)                                                     \
+  {                                                                                  \
+    wait_vmcnt<8>(); /* this wave's DMA of stage S is done (S+1, S+2 may be pending) */ \
+    __builtin_amdgcn_s_barrier();                                                    \
+    dma3(NXT3, d, (S) + 3, nst, wave);                                                    \
+    read_frags3<MODE, MI, NJ>(f0, CUR, CUR + kTile3, arow0, bcol0, 0, lane);         \
+    read_frags3<MODE, MI, NJ>(f1, CUR, CUR + kTile3, arow0, bcol0, 1, lane);         \
+    mfma3<MI, NJ>(acc, f0);                                                          \
+    mfma3<MI, NJ>(acc, f1);                                                          \
+  }
+  for (int s = 0; s < nst; s += 4) {
+    MOE_STAGE3(ring0, ring3, s)
+    if (s + 1 < nst) MOE_STAGE3(ring1, ring0, s + 1)
+    if (s + 2 < nst) MOE_STAGE3(ring2, ring1, s + 2)
+    if (s + 3 < nst) MOE_STAGE3(ring3, ring2, s + 3)
+  }
+#undef MOE_STAGE3
+  // Drain the DMA issued past the last stage before the ring is reused by the epilogue.
+  wait_vmcnt<0>();
+  __syncthreads();
+
   if (MODE == kGateUp) {
-    // h tile [256 rows][128 cols] bf16, row stride 136 elements.
+    // h tile [256 rows][128 cols] bf16, row stride 136 elements (69632 B of the ring).
     constexpr int kHS = 136;
-    uint16_t* hs = smem;
+    uint16_t* hs = reinterpret_cast<uint16_t*>(ring);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = wn * 64 + j * 32 + (lane & 31);
-          hs[row * kHS + col] = f32_to_bf16_bits(silu_mul(acc[i][j][r], acc[i][j + 2][r]));
+          const int row = arow0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = bcol0 + j * 32 + (lane & 31);
+          hs[row * kHS + col] = f32_to_bf16_bits(silu_mul(acc[i][j][r], acc[i][j + NJ / 2][r]));
         }
     __syncthreads();
     const int n0 = tc.ntile * 128;
-    for (int it = 0; it < 16; ++it) {
-      const int q = it * 256 + tid;
+    for (int q = tid; q < kBM * 16; q += 512) {
       const int row = q >> 4, ch = q & 15;
       if (row < tc.rows && n0 + ch * 8 < p.N)
         *reinterpret_cast<u32x4_t*>(p.h + static_cast<size_t>(tc.row0 + row) * p.N + n0 + ch * 8) =
             *reinterpret_cast<const u32x4_t*>(hs + row * kHS + ch * 8);
     }
   } else {
-    // Four passes of 64 rows staged as fp32 [64][260].
+    // Passes of 64 rows staged as fp32 [64][260] (66560 B of the ring).
     constexpr int kYS = 260;
-    float* ys = reinterpret_cast<float*>(smem);
+    float* ys = reinterpret_cast<float*>(ring);
     const int n0 = tc.ntile * kBN;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      if (wm == (q >> 1)) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * (q & 1) + ii;
+      for (int i = 0; i < MI; ++i) {
+        const int rbase = arow0 + i * 32;
+        if (rbase >= q * 64 && rbase < q * 64 + 64) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = ii * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-              const int col = wn * 128 + j * 32 + (lane & 31);
+              const int row = rbase - q * 64 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              const int col = bcol0 + j * 32 + (lane & 31);
               ys[row * kYS + col] = acc[i][j][r];
             }
         }
       }
       __syncthreads();
-      for (int it = 0; it < 16; ++it) {
-        const int e = it * 256 + tid;
+      for (int e = tid; e < 64 * 64; e += 512) {
         const int rl = e >> 6, c4 = (e & 63) * 4;
         const int row = q * 64 + rl;
         const int col = n0 + c4;
@@ -222,24 +291,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(Bf16GemmArgs p) {
           float4 v = *reinterpret_cast<const float4*>(ys + rl * kYS + c4);
           if (p.y_layout == MOE_Y_PERMUTED) {
             const size_t idx = static_cast<size_t>(tc.row0 + row) * p.N + col;
-            if (p.y_bf16) {
-              u32x2_t o = pack_bf16x4(v);
-              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = o;
-            } else {
-              *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
-            }
+            if (p.y_bf16) *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = pack_bf16x4(v);
+            else *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
           } else {
             const float wgt = row_w[row];
             v.x *= wgt; v.y *= wgt; v.z *= wgt; v.w *= wgt;
             const int pair = row_pair[row];
             if (p.y_layout == MOE_Y_SLOTS) {
               const size_t idx = static_cast<size_t>(pair) * p.N + col;
-              if (p.y_bf16) {
-                u32x2_t o = pack_bf16x4(v);
-                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = o;
-              } else {
-                *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
-              }
+              if (p.y_bf16) *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = pack_bf16x4(v);
+              else *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
             } else {
               float* dst = static_cast<float*>(p.y) + static_cast<size_t>(pair / p.k) * p.N + col;
               atomicAdd(dst + 0, v.x);
@@ -265,6 +326,17 @@ inline unsigned grid_for(int P, int E, int NT) {
 int bf16_tile_rows_gateup() { return kBM; }
 int bf16_tile_rows_down() { return kBM; }
 
+// Wave layout of both GEMMs: WM x WN waves (8 in total), each owning (256/WM) x (256/WN).
+#ifndef MOE_BF16_WAVES
+#define MOE_BF16_WAVES 4, 2
+#endif
+
+template <int MODE, int WM, int WN>
+hipError_t launch_gemm(const Bf16GemmArgs& g, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, WM, WN>), dim3(grid), dim3(512), 0, stream, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   const int P = L.T * L.k;
   Bf16GemmArgs g{};
@@ -276,13 +348,15 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   g.b1 = static_cast<const uint16_t*>(L.w_up);
   g.K = L.d;
   g.N = L.f;
+  g.a_rows = L.a_gather ? L.T : P;
   g.offsets = L.offsets;
   g.tile_cum = L.tile_cum_a;
   g.E = L.E;
   g.h = static_cast<uint16_t*>(L.h);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipLaunchKernelGGL(gemm_bf16_kernel<kGateUp>, dim3(grid_for(P, L.E, (L.f + 127) / 128)),
-                     dim3(256), 0, stream, g);
+  hipError_t e =
+      launch_gemm<kGateUp, MOE_BF16_WAVES>(g, grid_for(P, L.E, (L.f + 127) / 128), stream);
+  if (e != hipSuccess) return e;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
 
   Bf16GemmArgs dn{};
@@ -293,6 +367,7 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   dn.b0 = static_cast<const uint16_t*>(L.w_down);
   dn.K = L.f;
   dn.N = L.d;
+  dn.a_rows = P;
   dn.offsets = L.offsets;
   dn.tile_cum = L.tile_cum_b;
   dn.E = L.E;
@@ -301,10 +376,9 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  hipLaunchKernelGGL(gemm_bf16_kernel<kDown>, dim3(grid_for(P, L.E, (L.d + kBN - 1) / kBN)),
-                     dim3(256), 0, stream, dn);
+  e = launch_gemm<kDown, MOE_BF16_WAVES>(dn, grid_for(P, L.E, (L.d + kBN - 1) / kBN), stream);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
-  return hipGetLastError();
+  return e;
 }
 
 }  // namespace moe
