@@ -186,6 +186,7 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   if (bf16 && (a->d % 64 || a->f % 64)) return MOE_ERR_UNSUPPORTED;
   if (fp8) {
     if (a->d % kFp8Group || a->f % kFp8Group) return MOE_ERR_UNSUPPORTED;
+    if (a->d > 32768 || a->f > 32768) return MOE_ERR_UNSUPPORTED;
     if (!a->x_scales || !a->s_gate || !a->s_up || !a->s_down) return MOE_ERR_INVALID_ARGUMENT;
   }
   const long long P = static_cast<long long>(a->T) * a->k;

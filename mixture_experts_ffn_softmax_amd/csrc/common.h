@@ -17,6 +17,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
 // Raw 16-byte vector (a native vector type, so copies stay in registers).
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
@@ -77,6 +78,49 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
+}
+
+// ---- global -> LDS DMA ---------------------------------------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = N and expcnt / lgkmcnt left at their maximum (no wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Buffer resource for raw byte addressing of [base, base + bytes) (out-of-range reads return 0).
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = static_cast<int>(a & 0xffffffffu);
+  r[1] = static_cast<int>(a >> 32);   // stride 0
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;                  // raw buffer, 32-bit data format
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<size_t>((const __attribute__((address_space(3))) char*)(p)));
+}
+
+// One wave-wide 16-byte-per-lane DMA from global memory straight into LDS: lane l's 16 bytes land
+// at lds + 16 l. Issued as inline asm so the compiler does not add LDS-DMA waits of its own; the
+// GEMM loop places explicit vmcnt waits before its barriers instead (there are no other vector
+// memory instructions in that loop).
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4_t rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+// Same as dma16 with 4 bytes per lane (lane l's dword lands at lds + 4 l); inactive lanes skip.
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, i32x4_t rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
 }
 
 // ---- grouped-GEMM tile schedule ----------------------------------------------------------------

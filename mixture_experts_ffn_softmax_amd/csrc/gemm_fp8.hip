@@ -1,12 +1,388 @@
-// Fine-grained FP8 grouped GEMMs (placeholder until the e4m3 MFMA kernels land).
+// Fine-grained FP8 grouped GEMMs: e4m3 x e4m3 on the gfx950 matrix cores with fp32 accumulation.
+//
+// Transformers "Fine-grained FP8" page, introduction: weights carry one scale per 128x128 block,
+// activations one dynamic scale per token per 128 input channels. A K range of 128 therefore has
+// one activation scale per row and one weight scale per 128 output columns, so
+//     y[r][n] = sum_kb  sa[r][kb] * sw[n/128][kb] * sum_{k in kb} qa[r][k] * qw[n][k].
+// One v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales) computes exactly the inner sum of one
+// 16x16 block for one kb; its fp32 result is scaled by sa * sw and added to the accumulator.
+// The gate/up GEMM applies SwiGLU and re-quantises h per (pair, 128 channels) in its epilogue,
+// since h is the input of the down projection, a quantised linear too; the down GEMM writes y in
+// the requested layout (Transformers "Experts backends" page: gated MLP, weighted combine).
+//
+// Tiling: 128 pair rows x 256 weight rows per workgroup (gate/up: 128 gate + the same 128 up
+// rows, i.e. one full 128-channel group of h), 8 waves in a 2 x 4 grid, each 64 rows x 64
+// weight rows = 4 x 4 MFMA blocks of 16 x 16. K is staged 128 at a time (one scale block)
+// through a ring of three LDS stages filled two stages ahead by global -> LDS DMA.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
+namespace {
 
-int fp8_tile_rows_gateup() { return 128; }
-int fp8_tile_rows_down() { return 128; }
+constexpr int kBMf = 128;                          // pair rows per tile
+constexpr int kBNf = 256;                          // weight rows per tile
+constexpr int kBKf = 128;                          // K per stage (one scale block)
+constexpr int kAf = kBMf * kBKf;                   // A bytes per stage (16 KB)
+constexpr int kBf = kBNf * kBKf;                   // B bytes per stage (32 KB)
+constexpr int kStageF = kAf + kBf + kBMf * 4;      // + activation scales of the tile rows
+constexpr int kRingF = 3;
+constexpr int kMaxKBlocks = 256;                 // K <= 32768
+constexpr int kGateUp = 0;
+constexpr int kDown = 1;
 
-hipError_t launch_experts_fp8(const ExpertsLaunch&, hipStream_t) { return hipErrorNotSupported; }
+struct Fp8GemmArgs {
+  const uint8_t* a;          // gate/up: x codes [T, K] (rows gathered); down: h codes [P, K]
+  const float* a_s;          // activation scales [rows, K/128]
+  int a_gather, a_rows;
+  const int32_t* sorted_pair;
+  int k;
+  const uint8_t* b0;         // gate/up: W_gate [E, N, K]; down: W_down [E, N, K]
+  const uint8_t* b1;         // gate/up: W_up
+  const float* s0;           // block scales of b0 [E, N/128, K/128]
+  const float* s1;           // block scales of b1
+  int K, N;
+  const int32_t* offsets;
+  const int32_t* tile_cum;
+  int E;
+  uint8_t* hq;               // gate/up output codes [P, N]
+  float* hs;                 // gate/up output scales [P, N/128]
+  void* y;                   // down output
+  int y_layout, y_bf16;
+  const float* topk_w;
+};
+
+// 128-byte LDS rows: chunk c of row r sits at position c ^ ((r >> 1) & 7), so 16 consecutive rows
+// read at one logical chunk cover 16 distinct 16-byte slots of a 256-byte bank line.
+__device__ __forceinline__ int swzf(int row, int chunk) {
+  return row * kBKf + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+struct DmaF {
+  i32x4_t ra, rs, rb0, rb1;
+  uint32_t aoff[2], boff[4], soff;
+};
+
+// Stage `st` (clamped to the last real stage so every access stays in bounds) into `buf`:
+// wave w fills A rows (2w + i) * 8 .. +7, B rows (4w + i) * 8 .. +7 (one KB per instruction,
+// lane l -> row l / 8, chunk position l % 8) and the scales of A rows 16 w .. 16 w + 15.
+__device__ __forceinline__ void dmaf(const char* buf, const DmaF& d, int st, int nst, int wave,
+                                     int lane) {
+  const int sc = min(st, nst - 1);
+  const uint32_t kb = static_cast<uint32_t>(sc) * kBKf;
+  const uint32_t base = lds_offset(buf);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) dma16(base + (wave * 2 + i) * 1024, d.aoff[i], d.ra, kb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dma16(base + kAf + (wave * 4 + i) * 1024, d.boff[i], wave < 4 ? d.rb0 : d.rb1, kb);
+  if (lane < 16) dma4(base + kAf + kBf + wave * 64, d.soff, d.rs, static_cast<uint32_t>(sc) * 4u);
+}
+
+__device__ __forceinline__ i32x8_t ld32(const char* p0, const char* p1) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p0);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p1);
+  i32x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
+  constexpr int MI = 4, NJ = 4;   // 16x16 blocks per wave
+  const int NT = MODE == kGateUp ? p.N / 128 : (p.N + kBNf - 1) / kBNf;
+  TileCoord tc;
+  if (!map_tile(p.tile_cum, p.offsets, p.E, kBMf, NT, tc)) return;
+  tc.e = __builtin_amdgcn_readfirstlane(tc.e);
+  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+  tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
+  tc.ntile = __builtin_amdgcn_readfirstlane(tc.ntile);
+
+  __shared__ __attribute__((aligned(1024))) char ring[kRingF * kStageF];
+  __shared__ int row_pair[kBMf];
+  __shared__ float row_w[kBMf];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int arow0 = wm * 64;
+  // weight rows of this wave inside the tile: gate/up -> 32 gate rows + the same 32 up rows
+  const int brow0 = MODE == kGateUp ? wn * 32 : wn * 64;
+
+  if (MODE == kDown) {
+    for (int r = tid; r < kBMf; r += 512) {
+      const int pair = p.sorted_pair[tc.row0 + min(r, tc.rows - 1)];
+      row_pair[r] = pair;
+      row_w[r] = p.topk_w ? p.topk_w[pair] : 1.0f;
+    }
+  }
+
+  const int KB = p.K / kBKf;
+  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  DmaF d;
+  d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K);
+  d.rs = make_rsrc(p.a_s, static_cast<uint32_t>(p.a_rows) * KB * 4u);
+  d.rb0 = make_rsrc(p.b0 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K);
+  d.rb1 = MODE == kGateUp ? make_rsrc(p.b1 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K)
+                          : d.rb0;
+  auto src_row = [&](int r) {
+    const int pos = tc.row0 + min(r, tc.rows - 1);
+    return p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+  };
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave * 2 + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    d.aoff[i] = static_cast<uint32_t>(src_row(r)) * p.K + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
+                                  : min(tc.ntile * kBNf + r, p.N - 1);
+    d.boff[i] = static_cast<uint32_t>(n) * p.K + c * 16;
+  }
+  d.soff = static_cast<uint32_t>(src_row(wave * 16 + (lane & 15))) * KB * 4u;
+
+  // Weight scales of the tile for every K block, staged in LDS before the pipeline starts (the
+  // main loop issues no vector memory instructions besides its DMA): gate/up -> block ntile of
+  // s_gate and of s_up; down -> the two 128-column blocks of the 256-column tile.
+  __shared__ float wsc[2][kMaxKBlocks];
+  for (int i = tid; i < 2 * KB; i += 512) {
+    const int which = i >= KB, kb = i - which * KB;
+    const size_t blk = MODE == kGateUp ? static_cast<size_t>(tc.ntile)
+                                       : static_cast<size_t>(min(tc.ntile * 2 + which, p.N / 128 - 1));
+    const float* src = (MODE == kGateUp && which) ? p.s1 : p.s0;
+    wsc[which][kb] = src[(static_cast<size_t>(tc.e) * (p.N / 128) + blk) * KB + kb];
+  }
+  __syncthreads();
+  const float* sw0 = wsc[MODE == kGateUp ? 0 : (brow0 >> 7)];
+  const float* sw1 = wsc[MODE == kGateUp ? 1 : (brow0 >> 7)];
+
+  f32x4_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nst = KB;
+  char* const st0 = ring;
+  char* const st1 = ring + kStageF;
+  char* const st2 = ring + 2 * kStageF;
+  dmaf(st0, d, 0, nst, wave, lane);
+  dmaf(st1, d, 1, nst, wave, lane);
+
+  // lane -> (row / column l % 16, 32-byte k slice l / 16) of a 16x16x128 MFMA operand
+  const int lr = lane & 15, lk = lane >> 4;
+#define MOE_FP8_STAGE(CUR, NXT2, S)                                                           \
+  {                                                                                           \
+    wait_vmcnt<7>(); /* this wave's DMA of stage S is done (S+1 may be pending) */            \
+    __builtin_amdgcn_s_barrier();                                                             \
+    dmaf(NXT2, d, (S) + 2, nst, wave, lane);                                                  \
+    const float w0 = sw0[S], w1 = sw1[S];                                                     \
+    i32x8_t fa[MI], fb[NJ];                                                                   \
+    f32x4_t sa[MI];                                                                           \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                          \
+      const int row = arow0 + i * 16 + lr;                                                    \
+      fa[i] = ld32(CUR + swzf(row, 2 * lk), CUR + swzf(row, 2 * lk + 1));                     \
+      sa[i] = *reinterpret_cast<const f32x4_t*>(CUR + kAf + kBf +                             \
+                                                (arow0 + i * 16 + 4 * lk) * 4);               \
+    }                                                                                         \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                          \
+      const int row = MODE == kGateUp ? (j < 2 ? brow0 + j * 16 : 128 + brow0 + (j - 2) * 16) \
+                                      : brow0 + j * 16;                                       \
+      fb[j] = ld32(CUR + kAf + swzf(row + lr, 2 * lk), CUR + kAf + swzf(row + lr, 2 * lk + 1)); \
+    }                                                                                         \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                          \
+      const f32x4_t s0v = sa[i] * w0, s1v = sa[i] * w1;                                       \
+      _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                        \
+        const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                \
+            fa[i], fb[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);             \
+        const f32x4_t sc = (MODE == kGateUp && j >= 2) ? s1v : s0v;                           \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(part[q], sc[q], acc[i][j][q]); \
+      }                                                                                       \
+    }                                                                                         \
+  }
+  for (int s = 0; s < nst; s += 3) {
+    MOE_FP8_STAGE(st0, st2, s)
+    if (s + 1 < nst) MOE_FP8_STAGE(st1, st0, s + 1)
+    if (s + 2 < nst) MOE_FP8_STAGE(st2, st1, s + 2)
+  }
+#undef MOE_FP8_STAGE
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Accumulator layout of a 16x16 block: lane l holds column l % 16, rows 4 (l / 16) + q.
+  if (MODE == kGateUp) {
+    // h tile [128 rows][128 channels] fp32 (row stride 132), then per-row quantisation.
+    constexpr int kHS = 132;
+    float* hsb = reinterpret_cast<float*>(ring);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = arow0 + i * 16 + 4 * lk + q;
+          const int col = brow0 + j * 16 + lr;
+          hsb[row * kHS + col] = silu_mul(acc[i][j][q], acc[i][j + 2][q]);
+        }
+    __syncthreads();
+    const int row = tid >> 2, part = tid & 3;
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; c += 4) {
+      const f32x4_t t = *reinterpret_cast<const f32x4_t*>(hsb + row * kHS + part * 32 + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[c + q] = t[q];
+        amax = fmaxf(amax, fabsf(t[q]));
+      }
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (row < tc.rows) {
+      const size_t prow = static_cast<size_t>(tc.row0 + row);
+      u32x4_t o[2];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) word |= e4m3_encode(v[w * 4 + b] / s) << (8 * b);
+        o[w >> 2][w & 3] = word;
+      }
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(p.hq + prow * p.N + tc.ntile * 128 + part * 32);
+      dst[0] = o[0];
+      dst[1] = o[1];
+      if (part == 0) p.hs[prow * (p.N / 128) + tc.ntile] = s;
+    }
+  } else {
+    // Two passes of 64 rows staged as fp32 [64][260].
+    constexpr int kYS = 260;
+    float* ys = reinterpret_cast<float*>(ring);
+    const int n0 = tc.ntile * kBNf;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if (wm == pass) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              ys[(i * 16 + 4 * lk + q) * kYS + brow0 + j * 16 + lr] = acc[i][j][q];
+      }
+      __syncthreads();
+      for (int e = tid; e < 64 * 64; e += 512) {
+        const int rl = e >> 6, c4 = (e & 63) * 4;
+        const int row = pass * 64 + rl;
+        const int col = n0 + c4;
+        if (row < tc.rows && col < p.N) {
+          float4 v = *reinterpret_cast<const float4*>(ys + rl * kYS + c4);
+          if (p.y_layout == MOE_Y_PERMUTED) {
+            const size_t idx = static_cast<size_t>(tc.row0 + row) * p.N + col;
+            if (p.y_bf16) {
+              u32x2_t o;
+              o[0] = f32_to_bf16_bits(v.x) | (static_cast<uint32_t>(f32_to_bf16_bits(v.y)) << 16);
+              o[1] = f32_to_bf16_bits(v.z) | (static_cast<uint32_t>(f32_to_bf16_bits(v.w)) << 16);
+              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = o;
+            } else {
+              *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
+            }
+          } else {
+            const float wgt = row_w[row];
+            v.x *= wgt; v.y *= wgt; v.z *= wgt; v.w *= wgt;
+            const int pair = row_pair[row];
+            if (p.y_layout == MOE_Y_SLOTS) {
+              const size_t idx = static_cast<size_t>(pair) * p.N + col;
+              if (p.y_bf16) {
+                u32x2_t o;
+                o[0] = f32_to_bf16_bits(v.x) | (static_cast<uint32_t>(f32_to_bf16_bits(v.y)) << 16);
+                o[1] = f32_to_bf16_bits(v.z) | (static_cast<uint32_t>(f32_to_bf16_bits(v.w)) << 16);
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = o;
+              } else {
+                *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
+              }
+            } else {
+              float* dst = static_cast<float*>(p.y) + static_cast<size_t>(pair / p.k) * p.N + col;
+              atomicAdd(dst + 0, v.x);
+              atomicAdd(dst + 1, v.y);
+              atomicAdd(dst + 2, v.z);
+              atomicAdd(dst + 3, v.w);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+inline unsigned grid_for(int P, int E, int NT) {
+  long n = static_cast<long>(max_row_tiles(P, E, kBMf)) * NT;
+  return static_cast<unsigned>((n + 7) / 8 * 8);
+}
+
+}  // namespace
+
+int fp8_tile_rows_gateup() { return kBMf; }
+int fp8_tile_rows_down() { return kBMf; }
+
+hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream) {
+  const int P = L.T * L.k;
+  Fp8GemmArgs g{};
+  g.a = static_cast<const uint8_t*>(L.a);
+  g.a_s = L.a_scales;
+  g.a_gather = L.a_gather;
+  g.a_rows = L.a_gather ? L.T : P;
+  g.sorted_pair = L.sorted_pair;
+  g.k = L.k;
+  g.b0 = static_cast<const uint8_t*>(L.w_gate);
+  g.b1 = static_cast<const uint8_t*>(L.w_up);
+  g.s0 = L.s_gate;
+  g.s1 = L.s_up;
+  g.K = L.d;
+  g.N = L.f;
+  g.offsets = L.offsets;
+  g.tile_cum = L.tile_cum_a;
+  g.E = L.E;
+  g.hq = static_cast<uint8_t*>(L.h);
+  g.hs = L.h_scales;
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
+  hipLaunchKernelGGL(gemm_fp8_kernel<kGateUp>, dim3(grid_for(P, L.E, L.f / 128)), dim3(512), 0,
+                     stream, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+
+  Fp8GemmArgs dn{};
+  dn.a = static_cast<const uint8_t*>(L.h);
+  dn.a_s = L.h_scales;
+  dn.a_gather = 0;
+  dn.a_rows = P;
+  dn.sorted_pair = L.sorted_pair;
+  dn.k = L.k;
+  dn.b0 = static_cast<const uint8_t*>(L.w_down);
+  dn.s0 = L.s_down;
+  dn.K = L.f;
+  dn.N = L.d;
+  dn.offsets = L.offsets;
+  dn.tile_cum = L.tile_cum_b;
+  dn.E = L.E;
+  dn.y = L.y;
+  dn.y_layout = L.y_layout;
+  dn.y_bf16 = L.y_bf16;
+  dn.topk_w = L.topk_w;
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
+  hipLaunchKernelGGL(gemm_fp8_kernel<kDown>, dim3(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf)),
+                     dim3(512), 0, stream, dn);
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
+  return hipGetLastError();
+}
 
 }  // namespace moe

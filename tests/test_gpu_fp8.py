@@ -1,0 +1,145 @@
+"""GPU parity of the fine-grained FP8 layer against the oracle.
+
+Weights: fp32 masters from the generator, quantised to e4m3 with 128x128 block scales on the GPU
+(fp8_quantize_weight) and, independently, by the oracle; the codes and scales must agree
+bit-exactly, and the oracle then uses its own quantised weights. Activations: x is quantised per
+token per 128 channels by fp8_quantize_act inside the layer; the oracle applies the same rule to x
+and to h. Output bound: max|err| <= 6e-2 * max|ref| (the oracle of the quantised rule).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_softmax_amd as moe
+import oracle
+import synth
+from gpu_util import assert_close_rel_max, log, out_to_f64, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantise_on_gpu(masters):
+    q, s = moe.fp8_quantize_weight(to_dev(masters))
+    return q, s
+
+
+def _run_layer(x, logits, wq, k, y_layout="slots"):
+    (qg, sg), (qu, su), (qd, sd) = wq
+    res = moe.moe_layer(to_dev(x), qg, qu, qd, k, logits=to_dev(logits), s_gate=sg, s_up=su,
+                        s_down=sd, y_layout=y_layout)
+    torch.cuda.synchronize()
+    return res
+
+
+SMALL = [
+    synth.DSV3_FP8.with_(name="fp8_T300_d512_f256_E16_k4", T=300, d=512, f=256, E=16, k=4),
+    synth.DSV3_FP8.with_(name="fp8_T1000_d384_f640_E8_k2", T=1000, d=384, f=640, E=8, k=2),
+    synth.DSV3_FP8.with_(name="fp8_T7_d256_f128_E4_k1", T=7, d=256, f=128, E=4, k=1),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
+def test_small_fp8_layers(spec):
+    log(spec.name)
+    x = synth.gen_x(spec)
+    logits = synth.gen_logits(spec)
+    masters = [synth.gen_expert_weight(spec, n) for n in ("gate", "up", "down")]
+    wq = [_quantise_on_gpu(m) for m in masters]
+    wq_ref = [oracle.quantize_weight(m) for m in masters]
+    for (q, s), (qr, sr) in zip(wq, wq_ref):
+        np.testing.assert_array_equal(to_host(s), sr)
+        np.testing.assert_array_equal(to_host(q), qr)
+    ids_ref, w_ref = oracle.route(logits, spec.k)
+    ex = oracle.Experts(*(q for q, _ in wq_ref), *(s for _, s in wq_ref), quant_act=True)
+    ref = oracle.moe_forward(x, ex, ids_ref, w_ref)
+    for layout in ("slots", "permuted", "acc_f32"):
+        res = _run_layer(x, logits, wq, spec.k, layout)
+        np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
+        got = out_to_f64(res.out)
+        assert np.all(np.isfinite(got))
+        assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, layout))
+
+
+def test_fp8_hidden_codes_match_oracle_rule():
+    # The gate/up GEMM's h codes/scales, dequantised, stay within one e4m3 rounding step of the
+    # oracle's h (computed in fp64 before quantisation) for every pair.
+    spec = SMALL[0]
+    x = synth.gen_x(spec)
+    logits = synth.gen_logits(spec)
+    masters = [synth.gen_expert_weight(spec, n) for n in ("gate", "up", "down")]
+    wq = [_quantise_on_gpu(m) for m in masters]
+    (qg, sg), (qu, su), (qd, sd) = wq
+    ids, w, _ = moe.moe_route(spec.k, logits=to_dev(logits))
+    perm = moe.moe_permute(ids, spec.E)
+    xq, xs = moe.fp8_quantize_act(to_dev(x))
+    ws = torch.empty(moe.experts_workspace_bytes(spec.T, spec.d, spec.f, spec.E, spec.k,
+                                                 moe.MOE_FP8_E4M3, moe.MOE_FP8_E4M3),
+                     dtype=torch.uint8, device="cuda")
+    moe.moe_experts_forward(xq, qg, qu, qd, perm.offsets, perm.sorted_pair, w, spec.k,
+                            x_scales=xs, s_gate=sg, s_up=su, s_down=sd, workspace=ws)
+    torch.cuda.synchronize()
+    P, f = spec.P, spec.f
+    # workspace layout: two 256-byte-aligned tile tables, then h codes [P, f], then h scales
+    off_h = 2 * ((spec.E + 1) * 4 + 255) // 256 * 256
+    hq = to_host(ws[off_h:off_h + P * f]).reshape(P, f)
+    off_s = off_h + (P * f + 255) // 256 * 256
+    hs = to_host(ws[off_s:off_s + P * (f // 128) * 4].view(torch.float32)).reshape(P, f // 128)
+    h_gpu = oracle.e4m3_decode_array(hq) * np.repeat(hs.astype(np.float64), 128, axis=1)
+    sp = to_host(perm.sorted_pair)
+    ex = oracle.Experts(*(oracle.quantize_weight(m)[0] for m in masters),
+                        *(oracle.quantize_weight(m)[1] for m in masters), quant_act=True)
+    ids_h = to_host(ids).reshape(-1)
+    h_ref, _ = oracle.expert_pairs(x, ex, sp // spec.k, ids_h[sp], want_y=False)
+    # one e4m3 step is 2^-3 relative (normal range) plus the group scale's subnormal step
+    bound = np.abs(h_ref) * 2.0 ** -3 + np.repeat(hs.astype(np.float64), 128, axis=1) * 2.0 ** -8
+    assert np.all(np.abs(h_gpu - h_ref) <= bound + 1e-3 * np.abs(h_ref).max())
+
+
+def test_dsv3_fp8_full_sampled():
+    spec = synth.DSV3_FP8
+    T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
+    log("generating", spec.name)
+    x = synth.gen_x(spec)
+    logits = synth.gen_logits(spec)
+    ids_ref, w_ref = oracle.route(logits, k)
+    rng = np.random.default_rng(2)
+    tokens = np.sort(rng.choice(T, 12, replace=False))
+    need = sorted(set(ids_ref[tokens].reshape(-1).tolist()))
+    remap = {e: i for i, e in enumerate(need)}
+    # quantise expert by expert on the GPU; keep the oracle's own quantisation of the experts the
+    # sampled tokens use, and check those bit-exactly against the GPU's
+    dev_q, dev_s, ref_q, ref_s = {}, {}, {}, {}
+    for which in ("gate", "up", "down"):
+        rows, cols = (f, d) if which != "down" else (d, f)
+        qt = torch.empty((E, rows, cols), dtype=torch.uint8, device="cuda")
+        st = torch.empty((E, rows // 128, cols // 128), dtype=torch.float32, device="cuda")
+        rq = np.empty((len(need), rows, cols), np.uint8)
+        rs = np.empty((len(need), rows // 128, cols // 128), np.float32)
+        for e0 in range(0, E, 16):
+            chunk = list(range(e0, e0 + 16))
+            m = synth.gen_expert_weight(spec, which, experts=chunk)
+            q, s = moe.fp8_quantize_weight(to_dev(m))
+            qt[e0:e0 + 16] = q
+            st[e0:e0 + 16] = s
+            sel = [e for e in chunk if e in remap]
+            if sel:
+                oq, os_ = oracle.quantize_weight(m[[e - e0 for e in sel]])
+                for i, e in enumerate(sel):
+                    rq[remap[e]] = oq[i]
+                    rs[remap[e]] = os_[i]
+                np.testing.assert_array_equal(to_host(q[[e - e0 for e in sel]]), oq)
+                np.testing.assert_array_equal(to_host(s[[e - e0 for e in sel]]), os_)
+        dev_q[which], dev_s[which] = qt, st
+        ref_q[which], ref_s[which] = rq, rs
+    log("weights quantised; running the layer")
+    res = moe.moe_layer(to_dev(x), dev_q["gate"], dev_q["up"], dev_q["down"], k,
+                        logits=to_dev(logits), s_gate=dev_s["gate"], s_up=dev_s["up"],
+                        s_down=dev_s["down"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
+    got = out_to_f64(res.out)[tokens]
+    ex = oracle.Experts(ref_q["gate"], ref_q["up"], ref_q["down"], ref_s["gate"], ref_s["up"],
+                        ref_s["down"], quant_act=True)
+    ids_sub = np.vectorize(remap.get)(ids_ref[tokens]).astype(np.int32)
+    ref = oracle.moe_forward(x[tokens], ex, ids_sub, w_ref[tokens])
+    assert_close_rel_max(got, ref, 6e-2, spec.name)
