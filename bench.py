@@ -34,17 +34,25 @@ def log(msg):
 
 
 class Layer:
-    """Device buffers for one MoE layer workload and a step() that enqueues the whole path."""
+    """Device buffers for one MoE layer workload and a step() that enqueues the whole path:
+    moe_route (given logits, or the fp32 router GEMM), moe_permute, fp8_quantize_act (fp8
+    layers), moe_experts_forward, moe_combine."""
 
-    def __init__(self, moe, spec, x, Wr, Wg, Wu, Wd, n_ev_steps):
+    def __init__(self, moe, spec, x, W, n_ev_steps, logits=None, Wr=None, scales=None):
         import torch
         self.moe, self.spec = moe, spec
         self.lib = moe.load_library()
         dev = "cuda"
         T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
         P = T * k
-        self.x, self.Wr, self.Wg, self.Wu, self.Wd = x, Wr, Wg, Wu, Wd
-        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        Wg, Wu, Wd = W
+        self.keep = [x, Wg, Wu, Wd, logits, Wr, scales]
+        act = moe.MOE_F32 if spec.dtype == "f32" else moe.MOE_BF16
+        wdt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3}[spec.dtype]
+        ydt = moe.MOE_F32 if spec.dtype == "f32" else moe.MOE_BF16
+        tdt = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
+        self.logits = logits if logits is not None else torch.empty((T, E), dtype=torch.float32,
+                                                                   device=dev)
         self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
         self.counts = torch.empty(E, dtype=torch.int32, device=dev)
@@ -53,31 +61,51 @@ class Layer:
         self.pp = torch.empty(P, dtype=torch.int32, device=dev)
         pw = self.lib.moe_permute_workspace_size(T, k, E)
         self.pws = torch.empty(max(pw, 1), dtype=torch.uint8, device=dev)
-        ew = self.lib.moe_experts_workspace_size(T, d, f, E, k, moe.MOE_BF16, moe.MOE_BF16)
+        xact = moe.MOE_FP8_E4M3 if spec.dtype == "fp8" else act
+        ew = self.lib.moe_experts_workspace_size(T, d, f, E, k, xact, wdt)
         self.ews = torch.empty(ew, dtype=torch.uint8, device=dev)
-        self.y = torch.empty((T, k, d), dtype=torch.bfloat16, device=dev)
-        self.out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((T, k, d), dtype=tdt, device=dev)
+        self.out = torch.empty((T, d), dtype=tdt, device=dev)
         self.events = [[moe.event_create() for _ in range(4)] for _ in range(n_ev_steps)]
         self.ev_arrays = [(ctypes.c_void_p * 4)(*e) for e in self.events]
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+        self._quant = None
+        x_in, xs = x, None
+        if spec.dtype == "fp8":
+            self.xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
+            self._quant = (p(x), moe.MOE_BF16, T, d, 128, None, p(self.xq), p(self.xs),
+                           self.stream)
+            x_in, xs = self.xq, self.xs
+        sg = su = sd = None
+        if scales is not None:
+            sg, su, sd = scales
         self.args = moe.moe_experts_args(
-            T, d, f, E, k, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_Y_SLOTS,
-            x.data_ptr(), None, Wg.data_ptr(), Wu.data_ptr(), Wd.data_ptr(), None, None, None,
+            T, d, f, E, k, xact, wdt, ydt, moe.MOE_Y_SLOTS, x_in.data_ptr(),
+            xs.data_ptr() if xs is not None else None, Wg.data_ptr(), Wu.data_ptr(),
+            Wd.data_ptr(), sg.data_ptr() if sg is not None else None,
+            su.data_ptr() if su is not None else None, sd.data_ptr() if sd is not None else None,
             self.offsets.data_ptr(), self.sp.data_ptr(), self.w.data_ptr(), self.y.data_ptr(),
             self.ews.data_ptr(), self.ews.numel(), None)
-        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        p = lambda t: ctypes.c_void_p(t.data_ptr())
-        self._route = (None, p(x), moe.MOE_BF16, p(Wr), T, d, E, k, p(self.logits), p(self.ids),
-                       p(self.w), self.stream)
+        if logits is None:
+            self._route = (None, p(x), act, p(Wr), T, d, E, k, p(self.logits), p(self.ids),
+                           p(self.w), self.stream)
+        else:
+            self._route = (p(logits), None, act, None, T, d, E, k, None, p(self.ids), p(self.w),
+                           self.stream)
         self._perm = (p(self.ids), T, k, E, p(self.counts), p(self.offsets), p(self.sp),
                       p(self.pp), None, 0, None, 0, None, None, p(self.pws), self.pws.numel(),
                       self.stream)
-        self._comb = (p(self.y), moe.MOE_BF16, moe.MOE_Y_SLOTS, None, None, T, k, d, p(self.out),
-                      moe.MOE_BF16, self.stream)
+        self._comb = (p(self.y), ydt, moe.MOE_Y_SLOTS, None, None, T, k, d, p(self.out), ydt,
+                      self.stream)
 
     def step(self, ev_index=None):
         lib, chk = self.lib, self.moe._check
         chk(lib.moe_route(*self._route))
         chk(lib.moe_permute(*self._perm))
+        if self._quant is not None:
+            chk(lib.fp8_quantize_act(*self._quant))
         self.args.events = (ctypes.cast(self.ev_arrays[ev_index], ctypes.c_void_p)
                             if ev_index is not None else None)
         chk(lib.moe_experts_forward(ctypes.byref(self.args), self.stream))
@@ -135,6 +163,65 @@ def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
     }
 
 
+def measure_other(moe, synth, spec, steps, warmup):
+    """Times one extra workload (given router logits) and returns its figures."""
+    import numpy as np
+    import torch
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    t0 = time.perf_counter()
+    x = up(synth.gen_x(spec))
+    logits = up(synth.gen_logits(spec))
+    scales = None
+    if spec.dtype == "fp8":
+        W, S = [], []
+        for which in ("gate", "up", "down"):
+            rows, cols = (spec.f, spec.d) if which != "down" else (spec.d, spec.f)
+            q = torch.empty((spec.E, rows, cols), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((spec.E, rows // 128, cols // 128), dtype=torch.float32, device="cuda")
+            for e0 in range(0, spec.E, 16):
+                m = up(synth.gen_expert_weight(spec, which, experts=range(e0, min(e0 + 16, spec.E))))
+                qq, ss = moe.fp8_quantize_weight(m)
+                q[e0:e0 + 16] = qq
+                sc[e0:e0 + 16] = ss
+                del m
+            W.append(q)
+            S.append(sc)
+        scales = tuple(S)
+    else:
+        W = [up(synth.gen_expert_weight(spec, n)) for n in ("gate", "up", "down")]
+    log("%s inputs ready in %.1fs" % (spec.name, time.perf_counter() - t0))
+    layer = Layer(moe, spec, x, tuple(W), steps, logits=logits, scales=scales)
+    el = time_steps(layer, steps, warmup)
+    g1, g2 = layer.kernel_ms(steps)
+    counts = layer.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+    wbytes = {"f32": 4, "bf16": 2, "fp8": 1}[spec.dtype]
+    w_bytes = touched * 3 * spec.d * spec.f * wbytes
+    ms = el / steps * 1e3
+    r = {
+        "workload": spec.name, "ms_per_step": round(ms, 4),
+        "active_tflops": round(spec.active_flops() / (ms * 1e-3) / 1e12, 2),
+        "tokens_per_s": round(spec.T / (ms * 1e-3), 1),
+        "gate_up_ms": round(g1, 4), "down_ms": round(g2, 4),
+        "gate_up_tflops": round(4.0 * spec.P * spec.d * spec.f / (g1 * 1e-3) / 1e12, 2),
+        "down_tflops": round(2.0 * spec.P * spec.d * spec.f / (g2 * 1e-3) / 1e12, 2),
+        "weight_GBps_layer": round(w_bytes / (ms * 1e-3) / 1e9, 1),
+        "experts_touched": touched, "expert_rows_max": int(counts.max()),
+        "experts_empty": int((counts == 0).sum()),
+    }
+    log("%s: %.3f ms/step, %.1f TFLOP/s (gate/up %.3f ms, down %.3f ms)" % (
+        spec.name, ms, r["active_tflops"], g1, g2))
+    del layer
+    torch.cuda.empty_cache()
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +232,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--report", default="",
+                    help="also time the skewed 128-expert bf16 layer, the DeepSeek-V3-shaped fp8 "
+                         "layer and the tiny fp32 layer; write their figures to this JSON file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain fp32 copy kernel (out = in * 1) over this many MiB, "
                          "3 times, to calibrate HBM byte counters")
@@ -191,7 +281,7 @@ def main():
 
     if args.no_prefill:
         args.steps = 1
-    layer = Layer(moe, spec, x, Wr, Wg, Wu, Wd, max(args.steps, 1))
+    layer = Layer(moe, spec, x, (Wg, Wu, Wd), max(args.steps, 1), Wr=Wr)
     el = time_steps(layer, args.steps, args.warmup)
     ms = el / args.steps * 1e3
     g1_ms, g2_ms = layer.kernel_ms(args.steps)
@@ -237,7 +327,7 @@ def main():
     if not args.no_decode:
         dspec = synth.MIXTRAL_DECODE
         xd = up(synth.gen_x(dspec))
-        dl = Layer(moe, dspec, xd, Wr, Wg, Wu, Wd, args.decode_steps)
+        dl = Layer(moe, dspec, xd, (Wg, Wu, Wd), args.decode_steps, Wr=Wr)
         eld = time_steps(dl, args.decode_steps, 5)
         dms = eld / args.decode_steps * 1e3
         d1, d2 = dl.kernel_ms(args.decode_steps)
@@ -264,6 +354,17 @@ def main():
             },
         }
         del dl
+
+    if args.report:
+        del Wg, Wu, Wd
+        torch.cuda.empty_cache()
+        rep = [result.get("decode")]
+        for spec_o in (synth.SKEWED_128E, synth.DSV3_FP8, synth.TINY_F32):
+            rep.append(measure_other(moe, synth, spec_o, max(args.steps, 5), args.warmup))
+        with open(args.report, "w") as fh:
+            json.dump({"prefill": {k: result[k] for k in ("value", "ms_per_step", "config",
+                                                          "roofline")},
+                       "others": rep}, fh, indent=1)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (~%.0fs)" % args.cpu_seconds)
