@@ -7,9 +7,9 @@
 // token row straight from x (gather on load), so no permuted copy of x is needed.
 //
 // Tiling: 256 x 256 output tile per workgroup of 8 waves (2 per SIMD); WM x WN waves each own a
-// (256/WM) x (256/WN) block of 32x32 MFMA tiles. K is staged 32 at a time through a ring of four
-// LDS buffers that buffer_load ... lds (global -> LDS DMA, no staging registers) fills three
-// stages ahead; one vmcnt wait and one barrier per stage. For the gate/up GEMM the 256 B-rows of
+// (256/WM) x (256/WN) block of 32x32 MFMA tiles. K is staged 64 at a time through two LDS
+// buffers that buffer_load ... lds (global -> LDS DMA, no staging registers) fills one stage
+// ahead; one vmcnt wait and one barrier per stage. For the gate/up GEMM the 256 B-rows of
 // a tile are 128 gate rows and the same 128 up rows; each wave holds matching gate and up
 // accumulators and applies SwiGLU in registers. Results leave through LDS as whole 16-byte row
 // segments.
@@ -50,46 +50,50 @@ __device__ __forceinline__ u32x2_t pack_bf16x4(float4 v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Staging: each wave-level DMA instruction writes 1 KB = 16 rows x 64 B; lane l of it fetches the global
-// chunk that belongs at row l / 4, chunk position l % 4. Rows are 64 B (4 chunks of 16 B); the
-// logical chunk c of row r sits at position c ^ ((r >> 2) & 3), so 16 consecutive rows read at
+// Staging: K is staged 64 at a time (128-byte rows, one whole cache line per row per stage)
+// through two LDS buffers of 64 KB. Each wave-level DMA instruction writes 1 KB = 8 rows x 128 B;
+// lane l of it fetches the global chunk that belongs at row l / 8, chunk position l % 8. The
+// logical chunk c of row r sits at position c ^ ((r >> 1) & 7), so 16 consecutive rows read at
 // one logical chunk hit 16 distinct 16-byte slots of a 256-byte bank line (conflict free).
 // ---------------------------------------------------------------------------------------------
-constexpr int kBK3 = 32;
-constexpr int kTile3 = kBM * kBK3 * 2;   // bytes per operand per stage (16 KB)
+constexpr int kBK = 64;
+constexpr int kTile = kBM * kBK * 2;     // bytes per operand per stage (32 KB)
+constexpr int kStage = 2 * kTile;        // A + B (64 KB)
 
-__device__ __forceinline__ int swz3(int row, int chunk) {  // byte offset in a 256x64B tile
-  return row * (kBK3 * 2) + ((chunk ^ ((row >> 2) & 3)) << 4);
+__device__ __forceinline__ int swz(int row, int chunk) {  // byte offset in a 256x128B tile
+  return row * (kBK * 2) + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-struct Dma3 {
+template <int IPW>
+struct Dma {
   i32x4_t ra, rb0, rb1;
-  uint32_t aoff[2], boff[2];   // per-lane byte offsets of the thread's two A and two B rows
+  uint32_t aoff[IPW], boff[IPW];   // per-lane byte offsets of the thread's A and B rows
 };
 
 template <int MI, int NJ>
-struct Frag3 {
+struct Frag {
   bf16x8_t a[MI], b[NJ];
 };
 
 template <int MODE, int MI, int NJ>
-__device__ __forceinline__ void read_frags3(Frag3<MI, NJ>& f, const char* As, const char* Bs,
-                                            int arow0, int bcol0, int ks, int lane) {
+__device__ __forceinline__ void read_frags(Frag<MI, NJ>& f, const char* As, const char* Bs,
+                                           int arow0, int bcol0, int ks, int lane) {
   const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
-    f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + swz3(arow0 + i * 32 + (lane & 31), ch));
+    f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + swz(arow0 + i * 32 + (lane & 31), ch));
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
+    // gate/up: the first NJ/2 column blocks are gate rows, the rest the matching up rows
     const int brow = MODE == kGateUp
                          ? (j < NJ / 2 ? bcol0 + j * 32 : 128 + bcol0 + (j - NJ / 2) * 32)
                          : bcol0 + j * 32;
-    f.b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz3(brow + (lane & 31), ch));
+    f.b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(brow + (lane & 31), ch));
   }
 }
 
 template <int MI, int NJ>
-__device__ __forceinline__ void mfma3(f32x16_t (&acc)[MI][NJ], const Frag3<MI, NJ>& f) {
+__device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[MI][NJ], const Frag<MI, NJ>& f) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -97,22 +101,31 @@ __device__ __forceinline__ void mfma3(f32x16_t (&acc)[MI][NJ], const Frag3<MI, N
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Issues the DMA of stage `st` into one ring buffer (A tile then B tile): wave w fills rows
-// (2w + i) * 16 .. +15 of each operand (i = 0, 1); B rows 0..127 come from rb0, 128..255 from rb1.
-// Stages past the end of K re-read the last stage (never used), so every access stays in bounds.
-__device__ __forceinline__ void dma3(const char* buf, const Dma3& d, int st, int nst, int wave) {
-  const uint32_t kb = static_cast<uint32_t>(min(st, nst - 1)) * kBK3 * 2u;
+// Issues the DMA of stage `st` into one buffer (A tile then B tile). With NW waves, wave w fills
+// rows (IPW w + i) * 8 .. +7 of each operand (i < IPW = 32 / NW); B rows 0..127 come from rb0,
+// rows 128..255 from rb1. A rows at or past the tile's valid rows are skipped (their waves skip
+// the MFMAs). Stages past the end of K re-read the last stage (never used), so every access
+// stays in bounds.
+template <int NW>
+__device__ __forceinline__ void dma_stage(const char* buf, const Dma<32 / NW>& d, int st, int nst,
+                                          int wave, int rows) {
+  constexpr int IPW = 32 / NW;
+  const uint32_t kb = static_cast<uint32_t>(min(st, nst - 1)) * kBK * 2u;
   const uint32_t base = lds_offset(buf);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) dma16(base + (wave * 2 + i) * 1024, d.aoff[i], d.ra, kb);
+  for (int i = 0; i < IPW; ++i)
+    if ((wave * IPW + i) * 8 < rows) dma16(base + (wave * IPW + i) * 1024, d.aoff[i], d.ra, kb);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    dma16(base + kTile3 + (wave * 2 + i) * 1024, d.boff[i], wave < 4 ? d.rb0 : d.rb1, kb);
+  for (int i = 0; i < IPW; ++i)
+    dma16(base + kTile + (wave * IPW + i) * 1024, d.boff[i], wave * IPW < 16 ? d.rb0 : d.rb1, kb);
 }
 
 template <int MODE, int WM, int WN>
-__global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
-  static_assert(WM * WN == 8, "8 waves");
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p) {
+  constexpr int NW = WM * WN;
+  constexpr int kThreads = 64 * NW;
+  constexpr int IPW = 32 / NW;     // DMA instructions per wave per operand per stage
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int MI = kBM / WM / 32;
   constexpr int NJ = kBN / WN / 32;
   const int NT = MODE == kGateUp ? (p.N + 127) / 128 : (p.N + kBN - 1) / kBN;
@@ -124,12 +137,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
   tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
   tc.ntile = __builtin_amdgcn_readfirstlane(tc.ntile);
 
-  // Ring of four stage buffers, contiguous so the epilogue can reuse the whole 128 KB.
-  __shared__ __attribute__((aligned(1024))) char ring[4 * 2 * kTile3];
-  char* const ring0 = ring;
-  char* const ring1 = ring + 2 * kTile3;
-  char* const ring2 = ring + 4 * kTile3;
-  char* const ring3 = ring + 6 * kTile3;
+  // Two stage buffers, contiguous so the epilogue can reuse the whole 128 KB.
+  __shared__ __attribute__((aligned(1024))) char ring[2 * kStage];
+  char* const buf0 = ring;
+  char* const buf1 = ring + kStage;
   __shared__ int row_pair[kBM];
   __shared__ float row_w[kBM];
 
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
   const int bcol0 = MODE == kGateUp ? wn * (128 / WN) : wn * (kBN / WN);
 
   if (MODE == kDown) {
-    for (int r = tid; r < kBM; r += 512) {
+    for (int r = tid; r < kBM; r += kThreads) {
       const int rr = min(r, tc.rows - 1);
       const int pair = p.sorted_pair[tc.row0 + rr];
       row_pair[r] = pair;
@@ -149,18 +160,18 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
     }
   }
 
-  // DMA addressing: wave w fills rows (2w + i) * 16 .. +15 of each operand tile (i = 0, 1);
-  // lane l supplies row (2w + i) * 16 + l / 4 at chunk position l % 4.
-  Dma3 d;
+  // DMA addressing: lane l of instruction i of wave w supplies row (IPW w + i) * 8 + l / 8 at
+  // chunk position l % 8.
+  Dma<IPW> d;
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
   d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K * 2u);
   d.rb0 = make_rsrc(p.b0 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u);
   d.rb1 = MODE == kGateUp ? make_rsrc(p.b1 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u)
                           : d.rb0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (wave * 2 + i) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int pos = tc.row0 + min(r, tc.rows - 1);
     const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
     d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
@@ -177,31 +188,43 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nst = p.K / kBK3;
-  dma3(ring0, d, 0, nst, wave);
-  dma3(ring1, d, 1, nst, wave);
-  dma3(ring2, d, 2, nst, wave);
-  Frag3<MI, NJ> f0, f1;
-
-#define MOE_STAGE3(CUR, NXT3, S)                                                     \
-  {                                                                                  \
-    wait_vmcnt<8>(); /* this wave's DMA of stage S is done (S+1, S+2 may be pending) */ \
-    __builtin_amdgcn_s_barrier();                                                    \
-    dma3(NXT3, d, (S) + 3, nst, wave);                                                    \
-    read_frags3<MODE, MI, NJ>(f0, CUR, CUR + kTile3, arow0, bcol0, 0, lane);         \
-    read_frags3<MODE, MI, NJ>(f1, CUR, CUR + kTile3, arow0, bcol0, 1, lane);         \
-    mfma3<MI, NJ>(acc, f0);                                                          \
-    mfma3<MI, NJ>(acc, f1);                                                          \
-  }
-  for (int s = 0; s < nst; s += 4) {
-    MOE_STAGE3(ring0, ring3, s)
-    if (s + 1 < nst) MOE_STAGE3(ring1, ring0, s + 1)
-    if (s + 2 < nst) MOE_STAGE3(ring2, ring1, s + 2)
-    if (s + 3 < nst) MOE_STAGE3(ring3, ring2, s + 3)
-  }
-#undef MOE_STAGE3
-  // Drain the DMA issued past the last stage before the ring is reused by the epilogue.
+  const int nst = p.K / kBK;
+  dma_stage<NW>(buf0, d, 0, nst, wave, tc.rows);
   wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  // Waves whose rows all lie past the tile's valid rows (the short last tile of an expert) skip
+  // their fragment reads and MFMAs; the condition is wave-uniform.
+  const bool active = arow0 < tc.rows;
+  Frag<MI, NJ> fa, fb;
+  if (active) read_frags<MODE, MI, NJ>(fa, buf0, buf0 + kTile, arow0, bcol0, 0, lane);
+
+  // Stage S (from CUR, k-step-0 fragments already in fa): first the DMA of stage S+1 into NXT
+  // (read during stage S-1, which every wave finished before the last barrier), then k-steps
+  // 0..2; then the wait for this wave's DMA of stage S+1 and the barrier after which all of
+  // stage S+1 is in LDS; the next k-step-0 fragments are read while k-step 3 of stage S runs.
+#define MOE_STAGE(CUR, NXT, S)                                                       \
+  {                                                                                  \
+    dma_stage<NW>(NXT, d, (S) + 1, nst, wave, tc.rows);                              \
+    if (active) {                                                                    \
+      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 1, lane);         \
+      mfma_frags<MI, NJ>(acc, fa);                                                   \
+      read_frags<MODE, MI, NJ>(fa, CUR, CUR + kTile, arow0, bcol0, 2, lane);         \
+      mfma_frags<MI, NJ>(acc, fb);                                                   \
+      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 3, lane);         \
+      mfma_frags<MI, NJ>(acc, fa);                                                   \
+    }                                                                                \
+    wait_vmcnt<0>();                                                                 \
+    __builtin_amdgcn_s_barrier();                                                    \
+    if (active) {                                                                    \
+      read_frags<MODE, MI, NJ>(fa, NXT, NXT + kTile, arow0, bcol0, 0, lane);         \
+      mfma_frags<MI, NJ>(acc, fb);                                                   \
+    }                                                                                \
+  }
+  for (int s = 0; s < nst; s += 2) {
+    MOE_STAGE(buf0, buf1, s)
+    if (s + 1 < nst) MOE_STAGE(buf1, buf0, s + 1)
+  }
+#undef MOE_STAGE
   __syncthreads();
 
   if (MODE == kGateUp) {
@@ -220,7 +243,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
         }
     __syncthreads();
     const int n0 = tc.ntile * 128;
-    for (int q = tid; q < kBM * 16; q += 512) {
+    for (int q = tid; q < kBM * 16; q += kThreads) {
       const int row = q >> 4, ch = q & 15;
       if (row < tc.rows && n0 + ch * 8 < p.N)
         *reinterpret_cast<u32x4_t*>(p.h + static_cast<size_t>(tc.row0 + row) * p.N + n0 + ch * 8) =
@@ -248,7 +271,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(Bf16GemmArgs p) {
         }
       }
       __syncthreads();
-      for (int e = tid; e < 64 * 64; e += 512) {
+      for (int e = tid; e < 64 * 64; e += kThreads) {
         const int rl = e >> 6, c4 = (e & 63) * 4;
         const int row = q * 64 + rl;
         const int col = n0 + c4;
@@ -298,7 +321,8 @@ int bf16_tile_rows_down() { return kBM; }
 
 template <int MODE, int WM, int WN>
 hipError_t launch_gemm(const Bf16GemmArgs& g, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, WM, WN>), dim3(grid), dim3(512), 0, stream, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, stream,
+                     g);
   return hipGetLastError();
 }
 
