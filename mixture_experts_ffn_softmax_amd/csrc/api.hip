@@ -3,6 +3,8 @@
 // output is touched.
 #include <limits.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -34,12 +36,21 @@ moe_status check_topology(int T, int E, int k) {
 // Small-batch (weight streaming) kernels take over at or below this many pairs.
 constexpr int kDecodeMaxPairs = 256;
 
+inline bool uses_decode(moe_dtype act, moe_dtype w, long long P, int d, int f) {
+  return act == MOE_BF16 && w == MOE_BF16 && P <= kDecodeMaxPairs && d % 128 == 0 &&
+         f % 128 == 0;
+}
+
+// bf16 tiled GEMMs cut their tail tiles; they need partial-tile slots and counters.
+inline bool uses_split(moe_dtype act, moe_dtype w, long long P, int d, int f) {
+  return act == MOE_BF16 && w == MOE_BF16 && !uses_decode(act, w, P, d, f);
+}
+
 struct ExpertsLayout {
-  size_t cum_a, cum_b, h, h_scales, total;
+  size_t cum_a, cum_b, h, h_scales, split_partial, total;
 };
 
 ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, moe_dtype w) {
-  (void)d;
   ExpertsLayout L{};
   const size_t P = static_cast<size_t>(T) * k;
   size_t off = 0;
@@ -52,6 +63,11 @@ ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, m
   off = align_up(off + P * f * h_elem);
   L.h_scales = off;
   if (w == MOE_FP8_E4M3) off = align_up(off + P * (f / kFp8Group) * sizeof(float));
+  L.split_partial = 0;
+  if (uses_split(act, w, static_cast<long long>(P), d, f)) {
+    L.split_partial = off;
+    off = align_up(off + static_cast<size_t>(kSplitSlots) * 256 * 256 * sizeof(float));
+  }
   L.total = off;
   return L;
 }
@@ -62,6 +78,28 @@ __global__ void zero_f32_kernel(float* p, size_t n) {
 }
 
 }  // namespace
+
+namespace moe {
+
+// CUs per XCD of the current device (its 8 XCDs share the CUs evenly), cached per device and
+// capped so the split-tile slots stay within kSplitSlots.
+int cus_per_xcd() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int c = std::max(1, std::min(kSplitSlots / 8, cus / 8));
+  if (dev < 64) cache[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -224,9 +262,12 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   X.y = a->y;
   X.h = ws + L.h;
   X.h_scales = reinterpret_cast<float*>(ws + L.h_scales);
+  X.cpx = cus_per_xcd();
+  const bool split = uses_split(act, w, P, a->d, a->f);
+  X.split_partial = split ? reinterpret_cast<float*>(ws + L.split_partial) : nullptr;
   X.ev = a->events;
 
-  const bool decode = bf16 && P <= kDecodeMaxPairs && a->d % 128 == 0 && a->f % 128 == 0;
+  const bool decode = uses_decode(act, w, P, a->d, a->f);
   int bm_a, bm_b;
   if (f32) { bm_a = bm_b = f32_tile_rows(); }
   else if (fp8) { bm_a = fp8_tile_rows_gateup(); bm_b = fp8_tile_rows_down(); }

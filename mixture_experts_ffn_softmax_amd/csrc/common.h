@@ -138,20 +138,10 @@ struct TileCoord {
   int ntile;   // output-column tile index
 };
 
-// Maps a hardware block index to a tile; returns false for blocks beyond the real tile count.
-// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8); each XCD is
-// handed one contiguous range of logical tiles so that blocks sharing weight panels and input rows
-// share that XCD's L2.
-__device__ __forceinline__ bool map_tile(const int32_t* __restrict__ tile_cum,
-                                         const int32_t* __restrict__ offsets, int E, int BM,
-                                         int NT, TileCoord& tc) {
-  const int total = tile_cum[E] * NT;
-  const int chunk = (total + 7) / 8;
-  const int b = blockIdx.x;
-  const int slot = b >> 3;
-  if (slot >= chunk) return false;
-  const int logical = (b & 7) * chunk + slot;
-  if (logical >= total) return false;
+// Resolves logical tile `logical` (< tile_cum[E] * NT) to its expert, rows and column tile.
+__device__ __forceinline__ void decode_tile(const int32_t* __restrict__ tile_cum,
+                                            const int32_t* __restrict__ offsets, int E, int BM,
+                                            int NT, int logical, TileCoord& tc) {
   // largest e with tile_cum[e] * NT <= logical (experts with no rows have equal tile_cum entries)
   int lo = 0, hi = E;  // answer in [lo, hi)
   while (hi - lo > 1) {
@@ -168,7 +158,98 @@ __device__ __forceinline__ bool map_tile(const int32_t* __restrict__ tile_cum,
   tc.row0 = start;
   tc.rows = min(BM, offsets[e + 1] - start);
   tc.ntile = ntile;
+}
+
+// Maps a hardware block index to a tile; returns false for blocks beyond the real tile count.
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8); each XCD is
+// handed one contiguous range of logical tiles so that blocks sharing weight panels and input rows
+// share that XCD's L2.
+__device__ __forceinline__ bool map_tile(const int32_t* __restrict__ tile_cum,
+                                         const int32_t* __restrict__ offsets, int E, int BM,
+                                         int NT, TileCoord& tc) {
+  const int total = tile_cum[E] * NT;
+  const int chunk = (total + 7) / 8;
+  const int b = blockIdx.x;
+  const int slot = b >> 3;
+  if (slot >= chunk) return false;
+  const int logical = (b & 7) * chunk + slot;
+  if (logical >= total) return false;
+  decode_tile(tile_cum, offsets, E, BM, NT, logical, tc);
   return true;
+}
+
+// Split of the last, partial round. With one workgroup per CU and `cpx` CUs per XCD, an XCD
+// holding n tiles runs floor(n / cpx) whole rounds; the tail = n mod cpx tiles of its last round
+// would leave cpx - tail CUs idle, so each tail tile is cut into S = min(max_split, cpx / tail)
+// contiguous K ranges run by S workgroups. Every piece stores its fp32 partial tile; a second
+// kernel adds the S partials of each cut tile in piece order and runs the tile's epilogue.
+struct XcdShare {
+  int base;   // first logical tile of the XCD
+  int full;   // tiles run whole (a multiple of cpx)
+  int tail;   // tiles of the last round
+  int S;      // pieces per tail tile (1 = not cut)
+};
+
+__device__ __forceinline__ XcdShare xcd_share(int total, int x, int cpx, int max_split) {
+  XcdShare r;
+  const int chunk = (total + 7) / 8;
+  r.base = x * chunk;
+  const int n = max(0, min(chunk, total - r.base));
+  r.full = n / cpx * cpx;
+  r.tail = n - r.full;
+  r.S = r.tail > 0 ? max(1, min(max_split, cpx / r.tail)) : 1;
+  return r;
+}
+
+struct WorkUnit {
+  TileCoord tc;
+  int split;       // piece index (0 for an uncut tile)
+  int nsplit;      // pieces of this tile (1 = uncut)
+  int part_slot;   // partial-tile slot of this piece, < 8 * cpx (pieces of a tile are adjacent)
+};
+
+__device__ __forceinline__ bool map_work(const int32_t* __restrict__ tile_cum,
+                                         const int32_t* __restrict__ offsets, int E, int BM,
+                                         int NT, int cpx, int max_split, WorkUnit& w) {
+  const int b = blockIdx.x;
+  const int x = b & 7, s = b >> 3;
+  const XcdShare sh = xcd_share(tile_cum[E] * NT, x, cpx, max_split);
+  int logical;
+  if (s < sh.full) {
+    logical = sh.base + s;
+    w.split = 0;
+    w.nsplit = 1;
+    w.part_slot = 0;
+  } else {
+    const int u = s - sh.full;
+    if (u >= sh.tail * sh.S) return false;
+    logical = sh.base + sh.full + u / sh.S;
+    w.split = sh.S > 1 ? u % sh.S : 0;
+    w.nsplit = sh.S;
+    w.part_slot = x * cpx + u;
+  }
+  decode_tile(tile_cum, offsets, E, BM, NT, logical, w.tc);
+  return true;
+}
+
+// The cut tile handled by fix-up block c (< 8 * cpx): tail tile c % cpx of XCD c / cpx. Returns
+// false when that tile does not exist or was not cut; slot0 is its first partial slot.
+__device__ __forceinline__ bool map_cut_tile(const int32_t* __restrict__ tile_cum,
+                                             const int32_t* __restrict__ offsets, int E, int BM,
+                                             int NT, int cpx, int max_split, int c, TileCoord& tc,
+                                             int& nsplit, int& slot0) {
+  const int x = c / cpx, t = c % cpx;
+  const XcdShare sh = xcd_share(tile_cum[E] * NT, x, cpx, max_split);
+  if (t >= sh.tail || sh.S < 2) return false;
+  nsplit = sh.S;
+  slot0 = x * cpx + t * sh.S;
+  decode_tile(tile_cum, offsets, E, BM, NT, sh.base + sh.full + t, tc);
+  return true;
+}
+
+// Blocks to launch for map_work: per XCD at most chunk whole tiles plus cpx tail pieces.
+inline unsigned work_grid(long max_tiles, int cpx) {
+  return static_cast<unsigned>(((max_tiles + 7) / 8 + cpx) * 8);
 }
 
 // Upper bound on the number of row tiles: sum_e ceil(M_e/BM) <= floor(P/BM) + min(E, P).

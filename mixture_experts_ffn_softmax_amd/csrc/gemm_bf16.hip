@@ -13,6 +13,8 @@
 // a tile are 128 gate rows and the same 128 up rows; each wave holds matching gate and up
 // accumulators and applies SwiGLU in registers. Results leave through LDS as whole 16-byte row
 // segments.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -40,6 +42,9 @@ struct Bf16GemmArgs {
   void* y;                    // down output
   int y_layout, y_bf16;
   const float* topk_w;
+  int cpx;                    // CUs per XCD (one workgroup per CU)
+  int max_split;              // most K pieces a tail tile is cut into
+  float* partial;             // [8 * cpx][kBM * kBN] fp32 partial tiles of cut tiles
 };
 
 __device__ __forceinline__ u32x2_t pack_bf16x4(float4 v) {
@@ -104,13 +109,13 @@ __device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[MI][NJ], const Frag<M
 // Issues the DMA of stage `st` into one buffer (A tile then B tile). With NW waves, wave w fills
 // rows (IPW w + i) * 8 .. +7 of each operand (i < IPW = 32 / NW); B rows 0..127 come from rb0,
 // rows 128..255 from rb1. A rows at or past the tile's valid rows are skipped (their waves skip
-// the MFMAs). Stages past the end of K re-read the last stage (never used), so every access
-// stays in bounds.
+// the MFMAs). Stages past `last` re-read stage `last` (never used), so every access stays in
+// bounds.
 template <int NW>
-__device__ __forceinline__ void dma_stage(const char* buf, const Dma<32 / NW>& d, int st, int nst,
+__device__ __forceinline__ void dma_stage(const char* buf, const Dma<32 / NW>& d, int st, int last,
                                           int wave, int rows) {
   constexpr int IPW = 32 / NW;
-  const uint32_t kb = static_cast<uint32_t>(min(st, nst - 1)) * kBK * 2u;
+  const uint32_t kb = static_cast<uint32_t>(min(st, last)) * kBK * 2u;
   const uint32_t base = lds_offset(buf);
 #pragma unroll
   for (int i = 0; i < IPW; ++i)
@@ -120,117 +125,61 @@ __device__ __forceinline__ void dma_stage(const char* buf, const Dma<32 / NW>& d
     dma16(base + kTile + (wave * IPW + i) * 1024, d.boff[i], wave * IPW < 16 ? d.rb0 : d.rb1, kb);
 }
 
+// Partial tiles of cut tiles: fp32, in the accumulators' register order, so that thread t's
+// 16-byte group g sits at (g * kThreads + t) * 16 bytes of its slot (each wave's accesses are one
+// contiguous 1 KB).
+constexpr int kSlot4 = kBM * kBN / 4;   // f32x4 groups per slot
+
+template <int MI, int NJ, int kThreads>
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[MI][NJ], float* partial,
+                                              int slot, int tid) {
+  f32x4_t* const dst = reinterpret_cast<f32x4_t*>(partial) + static_cast<size_t>(slot) * kSlot4;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                           acc[i][j][4 * q + 3]};
+        dst[((i * NJ + j) * 4 + q) * kThreads + tid] = v;
+      }
+}
+
+// Row -> pair and routing weight of the down GEMM's output rows (rows past the tile's valid rows
+// repeat its last row; they are never stored).
+template <int kThreads>
+__device__ __forceinline__ void load_row_pairs(const Bf16GemmArgs& p, const TileCoord& tc,
+                                               int* row_pair, float* row_w, int tid) {
+  for (int r = tid; r < kBM; r += kThreads) {
+    const int rr = min(r, tc.rows - 1);
+    const int pair = p.sorted_pair[tc.row0 + rr];
+    row_pair[r] = pair;
+    row_w[r] = p.topk_w ? p.topk_w[pair] : 1.0f;
+  }
+}
+
+// Epilogue of one finished 256 x 256 tile held in the accumulators: gate/up applies SwiGLU and
+// stores the 256 x 128 h tile in bf16; down applies the routing weight and writes the requested
+// output layout. `lds` is at least 69632 bytes; row_pair / row_w are filled for the down GEMM.
 template <int MODE, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p) {
-  constexpr int NW = WM * WN;
-  constexpr int kThreads = 64 * NW;
-  constexpr int IPW = 32 / NW;     // DMA instructions per wave per operand per stage
-  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+__device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[kBM / WM / 32][kBN / WN / 32],
+                                              const Bf16GemmArgs& p, const TileCoord& tc,
+                                              char* lds, const int* row_pair,
+                                              const float* row_w) {
+  constexpr int kThreads = 64 * WM * WN;
   constexpr int MI = kBM / WM / 32;
   constexpr int NJ = kBN / WN / 32;
-  const int NT = MODE == kGateUp ? (p.N + 127) / 128 : (p.N + kBN - 1) / kBN;
-  TileCoord tc;
-  if (!map_tile(p.tile_cum, p.offsets, p.E, kBM, NT, tc)) return;
-  // the tile coordinates are block-uniform; say so, so descriptors and LDS bases live in SGPRs
-  tc.e = __builtin_amdgcn_readfirstlane(tc.e);
-  tc.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
-  tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
-  tc.ntile = __builtin_amdgcn_readfirstlane(tc.ntile);
-
-  // Two stage buffers, contiguous so the epilogue can reuse the whole 128 KB.
-  __shared__ __attribute__((aligned(1024))) char ring[2 * kStage];
-  char* const buf0 = ring;
-  char* const buf1 = ring + kStage;
-  __shared__ int row_pair[kBM];
-  __shared__ float row_w[kBM];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * (kBM / WM);
   const int bcol0 = MODE == kGateUp ? wn * (128 / WN) : wn * (kBN / WN);
-
-  if (MODE == kDown) {
-    for (int r = tid; r < kBM; r += kThreads) {
-      const int rr = min(r, tc.rows - 1);
-      const int pair = p.sorted_pair[tc.row0 + rr];
-      row_pair[r] = pair;
-      row_w[r] = p.topk_w ? p.topk_w[pair] : 1.0f;
-    }
-  }
-
-  // DMA addressing: lane l of instruction i of wave w supplies row (IPW w + i) * 8 + l / 8 at
-  // chunk position l % 8.
-  Dma<IPW> d;
-  const size_t wstride = static_cast<size_t>(p.N) * p.K;
-  d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K * 2u);
-  d.rb0 = make_rsrc(p.b0 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u);
-  d.rb1 = MODE == kGateUp ? make_rsrc(p.b1 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u)
-                          : d.rb0;
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int r = (wave * IPW + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int pos = tc.row0 + min(r, tc.rows - 1);
-    const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
-    d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
-    const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
-                                  : min(tc.ntile * kBN + r, p.N - 1);
-    d.boff[i] = static_cast<uint32_t>(n) * p.K * 2u + c * 16;
-  }
-
-  f32x16_t acc[MI][NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int nst = p.K / kBK;
-  dma_stage<NW>(buf0, d, 0, nst, wave, tc.rows);
-  wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
-  // Waves whose rows all lie past the tile's valid rows (the short last tile of an expert) skip
-  // their fragment reads and MFMAs; the condition is wave-uniform.
-  const bool active = arow0 < tc.rows;
-  Frag<MI, NJ> fa, fb;
-  if (active) read_frags<MODE, MI, NJ>(fa, buf0, buf0 + kTile, arow0, bcol0, 0, lane);
-
-  // Stage S (from CUR, k-step-0 fragments already in fa): first the DMA of stage S+1 into NXT
-  // (read during stage S-1, which every wave finished before the last barrier), then k-steps
-  // 0..2; then the wait for this wave's DMA of stage S+1 and the barrier after which all of
-  // stage S+1 is in LDS; the next k-step-0 fragments are read while k-step 3 of stage S runs.
-#define MOE_STAGE(CUR, NXT, S)                                                       \
-  {                                                                                  \
-    dma_stage<NW>(NXT, d, (S) + 1, nst, wave, tc.rows);                              \
-    if (active) {                                                                    \
-      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 1, lane);         \
-      mfma_frags<MI, NJ>(acc, fa);                                                   \
-      read_frags<MODE, MI, NJ>(fa, CUR, CUR + kTile, arow0, bcol0, 2, lane);         \
-      mfma_frags<MI, NJ>(acc, fb);                                                   \
-      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 3, lane);         \
-      mfma_frags<MI, NJ>(acc, fa);                                                   \
-    }                                                                                \
-    wait_vmcnt<0>();                                                                 \
-    __builtin_amdgcn_s_barrier();                                                    \
-    if (active) {                                                                    \
-      read_frags<MODE, MI, NJ>(fa, NXT, NXT + kTile, arow0, bcol0, 0, lane);         \
-      mfma_frags<MI, NJ>(acc, fb);                                                   \
-    }                                                                                \
-  }
-  for (int s = 0; s < nst; s += 2) {
-    MOE_STAGE(buf0, buf1, s)
-    if (s + 1 < nst) MOE_STAGE(buf1, buf0, s + 1)
-  }
-#undef MOE_STAGE
-  __syncthreads();
-
   if (MODE == kGateUp) {
     // h tile [256 rows][128 cols] bf16, row stride 136 elements (69632 B of the ring).
     constexpr int kHS = 136;
-    uint16_t* hs = reinterpret_cast<uint16_t*>(ring);
+    uint16_t* hs = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -252,7 +201,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   } else {
     // Passes of 64 rows staged as fp32 [64][260] (66560 B of the ring).
     constexpr int kYS = 260;
-    float* ys = reinterpret_cast<float*>(ring);
+    float* ys = reinterpret_cast<float*>(lds);
     const int n0 = tc.ntile * kBN;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -304,10 +253,167 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   }
 }
 
-inline unsigned grid_for(int P, int E, int NT) {
-  long n = static_cast<long>(max_row_tiles(P, E, kBM)) * NT;
-  return static_cast<unsigned>((n + 7) / 8 * 8);
+template <int MODE, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p) {
+  constexpr int NW = WM * WN;
+  constexpr int kThreads = 64 * NW;
+  constexpr int IPW = 32 / NW;     // DMA instructions per wave per operand per stage
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int MI = kBM / WM / 32;
+  constexpr int NJ = kBN / WN / 32;
+  const int NT = MODE == kGateUp ? (p.N + 127) / 128 : (p.N + kBN - 1) / kBN;
+  WorkUnit wu;
+  if (!map_work(p.tile_cum, p.offsets, p.E, kBM, NT, p.cpx, p.max_split, wu)) return;
+  // the tile coordinates are block-uniform; say so, so descriptors and LDS bases live in SGPRs
+  TileCoord tc;
+  tc.e = __builtin_amdgcn_readfirstlane(wu.tc.e);
+  tc.row0 = __builtin_amdgcn_readfirstlane(wu.tc.row0);
+  tc.rows = __builtin_amdgcn_readfirstlane(wu.tc.rows);
+  tc.ntile = __builtin_amdgcn_readfirstlane(wu.tc.ntile);
+  const int split = __builtin_amdgcn_readfirstlane(wu.split);
+  const int nsplit = __builtin_amdgcn_readfirstlane(wu.nsplit);
+
+  // Two stage buffers, contiguous so the epilogue can reuse the whole 128 KB.
+  __shared__ __attribute__((aligned(1024))) char ring[2 * kStage];
+  char* const buf0 = ring;
+  char* const buf1 = ring + kStage;
+  __shared__ int row_pair[kBM];
+  __shared__ float row_w[kBM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int arow0 = wm * (kBM / WM);
+  const int bcol0 = MODE == kGateUp ? wn * (128 / WN) : wn * (kBN / WN);
+
+  if (MODE == kDown) load_row_pairs<kThreads>(p, tc, row_pair, row_w, tid);
+
+  // DMA addressing: lane l of instruction i of wave w supplies row (IPW w + i) * 8 + l / 8 at
+  // chunk position l % 8.
+  Dma<IPW> d;
+  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K * 2u);
+  d.rb0 = make_rsrc(p.b0 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u);
+  d.rb1 = MODE == kGateUp ? make_rsrc(p.b1 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K * 2u)
+                          : d.rb0;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int pos = tc.row0 + min(r, tc.rows - 1);
+    const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+    d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
+    const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
+                                  : min(tc.ntile * kBN + r, p.N - 1);
+    d.boff[i] = static_cast<uint32_t>(n) * p.K * 2u + c * 16;
+  }
+
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // this piece's stages: [st0, st0 + nst) of the K / kBK stages
+  const int st_all = p.K / kBK;
+  const int st0 = split * st_all / nsplit;
+  const int nst = (split + 1) * st_all / nsplit - st0;
+  const int last = st0 + nst - 1;
+  dma_stage<NW>(buf0, d, st0, last, wave, tc.rows);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  // Waves whose rows all lie past the tile's valid rows (the short last tile of an expert) skip
+  // their fragment reads and MFMAs; the condition is wave-uniform.
+  const bool active = arow0 < tc.rows;
+  Frag<MI, NJ> fa, fb;
+  if (active) read_frags<MODE, MI, NJ>(fa, buf0, buf0 + kTile, arow0, bcol0, 0, lane);
+
+  // Stage S (from CUR, k-step-0 fragments already in fa): first the DMA of stage S+1 into NXT
+  // (read during stage S-1, which every wave finished before the last barrier), then k-steps
+  // 0..2; then the wait for this wave's DMA of stage S+1 and the barrier after which all of
+  // stage S+1 is in LDS; the next k-step-0 fragments are read while k-step 3 of stage S runs.
+#define MOE_STAGE(CUR, NXT, S)                                                       \
+  {                                                                                  \
+    dma_stage<NW>(NXT, d, st0 + (S) + 1, last, wave, tc.rows);                       \
+    if (active) {                                                                    \
+      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 1, lane);         \
+      mfma_frags<MI, NJ>(acc, fa);                                                   \
+      read_frags<MODE, MI, NJ>(fa, CUR, CUR + kTile, arow0, bcol0, 2, lane);         \
+      mfma_frags<MI, NJ>(acc, fb);                                                   \
+      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 3, lane);         \
+      mfma_frags<MI, NJ>(acc, fa);                                                   \
+    }                                                                                \
+    wait_vmcnt<0>();                                                                 \
+    __builtin_amdgcn_s_barrier();                                                    \
+    if (active) {                                                                    \
+      read_frags<MODE, MI, NJ>(fa, NXT, NXT + kTile, arow0, bcol0, 0, lane);         \
+      mfma_frags<MI, NJ>(acc, fb);                                                   \
+    }                                                                                \
+  }
+  for (int s = 0; s < nst; s += 2) {
+    MOE_STAGE(buf0, buf1, s)
+    if (s + 1 < nst) MOE_STAGE(buf1, buf0, s + 1)
+  }
+#undef MOE_STAGE
+  __syncthreads();
+
+  if (nsplit > 1) {
+    // a piece of a cut tile: store the partial in register order and leave the rest to the fix-up
+    store_partial<MI, NJ, kThreads>(acc, p.partial, wu.part_slot, tid);
+    return;
+  }
+  tile_epilogue<MODE, WM, WN>(acc, p, tc, ring, row_pair, row_w);
 }
+
+
+// Fix-up of the cut tiles: block c sums the partials of one cut tile in piece order and runs the
+// tile's epilogue, with the same thread layout as the GEMM kernel.
+template <int MODE, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void fixup_bf16_kernel(Bf16GemmArgs p) {
+  constexpr int kThreads = 64 * WM * WN;
+  constexpr int MI = kBM / WM / 32;
+  constexpr int NJ = kBN / WN / 32;
+  const int NT = MODE == kGateUp ? (p.N + 127) / 128 : (p.N + kBN - 1) / kBN;
+  TileCoord tc;
+  int nsplit, slot0;
+  if (!map_cut_tile(p.tile_cum, p.offsets, p.E, kBM, NT, p.cpx, p.max_split, blockIdx.x, tc,
+                    nsplit, slot0))
+    return;
+  __shared__ __attribute__((aligned(1024))) char lds[69632];
+  __shared__ int row_pair[kBM];
+  __shared__ float row_w[kBM];
+  const int tid = threadIdx.x;
+  if (MODE == kDown) load_row_pairs<kThreads>(p, tc, row_pair, row_w, tid);
+  const f32x4_t* const src =
+      reinterpret_cast<const f32x4_t*>(p.partial) + static_cast<size_t>(slot0) * kSlot4;
+  f32x16_t acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const size_t g = static_cast<size_t>(((i * NJ + j) * 4 + q) * kThreads + tid);
+        f32x4_t sum = src[g];
+        for (int t = 1; t < nsplit; ++t) sum += src[g + static_cast<size_t>(t) * kSlot4];
+        acc[i][j][4 * q] = sum[0];
+        acc[i][j][4 * q + 1] = sum[1];
+        acc[i][j][4 * q + 2] = sum[2];
+        acc[i][j][4 * q + 3] = sum[3];
+      }
+  __syncthreads();
+  tile_epilogue<MODE, WM, WN>(acc, p, tc, lds, row_pair, row_w);
+}
+
+inline long max_tiles(int P, int E, int NT) {
+  return static_cast<long>(max_row_tiles(P, E, kBM)) * NT;
+}
+
+// K pieces a tail tile may be cut into: at least 8 stages (512 of K) per piece, at most 8 pieces.
+inline int max_split_for(int K) { return std::max(1, std::min(8, K / kBK / 8)); }
 
 }  // namespace
 
@@ -319,10 +425,15 @@ int bf16_tile_rows_down() { return kBM; }
 #define MOE_BF16_WAVES 4, 2
 #endif
 
+// The GEMM, then (when tail tiles may be cut) the fix-up of the cut tiles.
 template <int MODE, int WM, int WN>
 hipError_t launch_gemm(const Bf16GemmArgs& g, unsigned grid, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_bf16_kernel<MODE, WM, WN>), dim3(grid), dim3(64 * WM * WN), 0, stream,
                      g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.max_split < 2) return e;
+  hipLaunchKernelGGL((fixup_bf16_kernel<MODE, WM, WN>), dim3(8 * g.cpx), dim3(64 * WM * WN), 0,
+                     stream, g);
   return hipGetLastError();
 }
 
@@ -342,9 +453,13 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   g.tile_cum = L.tile_cum_a;
   g.E = L.E;
   g.h = static_cast<uint16_t*>(L.h);
+  g.cpx = L.cpx;
+  g.max_split = L.split_partial ? max_split_for(L.d) : 1;
+  g.partial = L.split_partial;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
   hipError_t e =
-      launch_gemm<kGateUp, MOE_BF16_WAVES>(g, grid_for(P, L.E, (L.f + 127) / 128), stream);
+      launch_gemm<kGateUp, MOE_BF16_WAVES>(g, work_grid(max_tiles(P, L.E, (L.f + 127) / 128), L.cpx),
+                                           stream);
   if (e != hipSuccess) return e;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
 
@@ -364,8 +479,12 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   dn.y_layout = L.y_layout;
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
+  dn.cpx = L.cpx;
+  dn.max_split = L.split_partial ? max_split_for(L.f) : 1;
+  dn.partial = L.split_partial;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  e = launch_gemm<kDown, MOE_BF16_WAVES>(dn, grid_for(P, L.E, (L.d + kBN - 1) / kBN), stream);
+  e = launch_gemm<kDown, MOE_BF16_WAVES>(dn, work_grid(max_tiles(P, L.E, (L.d + kBN - 1) / kBN), L.cpx),
+                                         stream);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return e;
 }

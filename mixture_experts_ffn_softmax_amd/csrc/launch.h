@@ -35,6 +35,11 @@ hipError_t launch_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
 hipError_t launch_tile_table(const int32_t* offsets, int E, int bm_a, int bm_b, int32_t* cum_a,
                              int32_t* cum_b, hipStream_t stream);
 
+// Cut tail tiles of the bf16 GEMMs: partial-tile slots per GEMM (8 XCDs x at most 32 CUs each),
+// and the CUs per XCD the tile schedule assumes.
+constexpr int kSplitSlots = 256;
+int cus_per_xcd();
+
 // Everything one experts forward needs, resolved by the ABI layer.
 struct ExpertsLaunch {
   int T, d, f, E, k;
@@ -57,6 +62,9 @@ struct ExpertsLaunch {
   void* y;
   void* h;                    // workspace: hidden activations [P, f]
   float* h_scales;            // fp8: [P, f/128]
+  int cpx;                    // CUs per XCD (<= kSplitSlots / 8)
+  float* split_partial;       // bf16 GEMMs: [kSplitSlots][256 * 256] fp32, or null (no cutting;
+                              // the two GEMMs use it one after the other)
   void** ev;                  // nullable timing events (4)
 };
 

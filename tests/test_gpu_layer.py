@@ -78,6 +78,35 @@ def test_small_bf16_layers(spec):
         _check_layer(spec, inp, res, 2e-2)
 
 
+# Shapes whose last round of tiles is cut along K (few tiles per XCD, long K): gate/up cut 8 ways,
+# down cut 8 ways, and both GEMMs cut (2 and 4 ways). The cut tiles are summed in piece order by
+# whichever piece finishes last, so repeated runs must agree bit for bit.
+CUT_TAIL = [
+    synth.TINY_F32.with_(name="bf16_cut_gateup_T200_d4096_f512_E2_k2", dtype="bf16", T=200,
+                         d=4096, f=512, E=2, k=2),
+    synth.TINY_F32.with_(name="bf16_cut_down_T200_d512_f4096_E2_k2", dtype="bf16", T=200, d=512,
+                         f=4096, E=2, k=2),
+    synth.TINY_F32.with_(name="bf16_cut_both_T700_d1024_f2048_E4_k2", dtype="bf16", T=700,
+                         d=1024, f=2048, E=4, k=2),
+]
+
+
+@pytest.mark.parametrize("spec", CUT_TAIL, ids=lambda s: s.name)
+def test_cut_tail_tiles(spec):
+    inp = layer_inputs(spec)
+    first = None
+    for layout in ("slots", "acc_f32", "slots"):
+        log(spec.name, layout)
+        res = _run_gpu(spec, inp, layout)
+        _check_layer(spec, inp, res, 2e-2)
+        if layout == "slots":
+            out = to_host(res.out)
+            if first is None:
+                first = out
+            else:
+                np.testing.assert_array_equal(out, first)
+
+
 def test_bf16_prefill_kernel_on_small_batch_shapes():
     # P <= 256 goes to the decode kernels; d not a multiple of 128 forces the tiled kernels.
     spec = synth.TINY_F32.with_(name="bf16_T40_d192_f320_E8_k2", dtype="bf16", T=40, d=192,
