@@ -183,6 +183,9 @@ __device__ __forceinline__ bool map_tile(const int32_t* __restrict__ tile_cum,
 // would leave cpx - tail CUs idle, so each tail tile is cut into S = min(max_split, cpx / tail)
 // contiguous K ranges run by S workgroups. Every piece stores its fp32 partial tile; a second
 // kernel adds the S partials of each cut tile in piece order and runs the tile's epilogue.
+// Tiles are cut only when the XCD has at most kCutMaxRounds whole rounds: over more rounds the
+// CUs finish their tiles at scattered times and the last round is no longer an idle step.
+constexpr int kCutMaxRounds = 4;
 struct XcdShare {
   int base;   // first logical tile of the XCD
   int full;   // tiles run whole (a multiple of cpx)
@@ -197,7 +200,7 @@ __device__ __forceinline__ XcdShare xcd_share(int total, int x, int cpx, int max
   const int n = max(0, min(chunk, total - r.base));
   r.full = n / cpx * cpx;
   r.tail = n - r.full;
-  r.S = r.tail > 0 ? max(1, min(max_split, cpx / r.tail)) : 1;
+  r.S = r.tail > 0 && r.full <= kCutMaxRounds * cpx ? max(1, min(max_split, cpx / r.tail)) : 1;
   return r;
 }
 

@@ -125,25 +125,32 @@ __device__ __forceinline__ void dma_stage(const char* buf, const Dma<32 / NW>& d
     dma16(base + kTile + (wave * IPW + i) * 1024, d.boff[i], wave * IPW < 16 ? d.rb0 : d.rb1, kb);
 }
 
-// Partial tiles of cut tiles: fp32, in the accumulators' register order, so that thread t's
-// 16-byte group g sits at (g * kThreads + t) * 16 bytes of its slot (each wave's accesses are one
-// contiguous 1 KB).
-constexpr int kSlot4 = kBM * kBN / 4;   // f32x4 groups per slot
+// Partial tiles of cut tiles: fp32, row-major [256 rows][256 tile columns]. Tile column c is
+// output column n0 + c for the down GEMM; for gate/up, columns 0..127 are the gate and 128..255
+// the up projections of h columns n0 .. n0+127. Each store instruction writes two 128-byte row
+// segments.
+constexpr int kSlotFloats = kBM * kBN;
 
-template <int MI, int NJ, int kThreads>
-__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[MI][NJ], float* partial,
-                                              int slot, int tid) {
-  f32x4_t* const dst = reinterpret_cast<f32x4_t*>(partial) + static_cast<size_t>(slot) * kSlot4;
+template <int MODE, int WM, int WN>
+__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[kBM / WM / 32][kBN / WN / 32],
+                                              float* partial, int slot, int arow0, int bcol0,
+                                              int lane) {
+  constexpr int MI = kBM / WM / 32;
+  constexpr int NJ = kBN / WN / 32;
+  float* const dst = partial + static_cast<size_t>(slot) * kSlotFloats;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJ; ++j) {
+      const int col = MODE == kGateUp
+                          ? (j < NJ / 2 ? bcol0 + j * 32 : 128 + bcol0 + (j - NJ / 2) * 32)
+                          : bcol0 + j * 32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                           acc[i][j][4 * q + 3]};
-        dst[((i * NJ + j) * 4 + q) * kThreads + tid] = v;
+      for (int r = 0; r < 16; ++r) {
+        const int row = arow0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        dst[row * kBN + col + (lane & 31)] = acc[i][j][r];
       }
+    }
 }
 
 // Row -> pair and routing weight of the down GEMM's output rows (rows past the tile's valid rows
@@ -362,50 +369,84 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
 
   if (nsplit > 1) {
     // a piece of a cut tile: store the partial in register order and leave the rest to the fix-up
-    store_partial<MI, NJ, kThreads>(acc, p.partial, wu.part_slot, tid);
+    store_partial<MODE, WM, WN>(acc, p.partial, wu.part_slot, arow0, bcol0, lane);
     return;
   }
   tile_epilogue<MODE, WM, WN>(acc, p, tc, ring, row_pair, row_w);
 }
 
 
-// Fix-up of the cut tiles: block c sums the partials of one cut tile in piece order and runs the
-// tile's epilogue, with the same thread layout as the GEMM kernel.
-template <int MODE, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void fixup_bf16_kernel(Bf16GemmArgs p) {
-  constexpr int kThreads = 64 * WM * WN;
-  constexpr int MI = kBM / WM / 32;
-  constexpr int NJ = kBN / WN / 32;
+// Fix-up of the cut tiles, element-wise: kFixBlocks blocks of 256 threads per cut-tile slot, each
+// covering 8 tile rows. A thread adds the pieces' partials in piece order (fp32) for 4 columns
+// and applies the same epilogue as the GEMM: gate/up -> SwiGLU -> bf16 h; down -> routing weight
+// -> requested layout.
+constexpr int kFixRows = 8;
+constexpr int kFixBlocks = kBM / kFixRows;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void fixup_bf16_kernel(Bf16GemmArgs p) {
   const int NT = MODE == kGateUp ? (p.N + 127) / 128 : (p.N + kBN - 1) / kBN;
   TileCoord tc;
   int nsplit, slot0;
-  if (!map_cut_tile(p.tile_cum, p.offsets, p.E, kBM, NT, p.cpx, p.max_split, blockIdx.x, tc,
-                    nsplit, slot0))
+  if (!map_cut_tile(p.tile_cum, p.offsets, p.E, kBM, NT, p.cpx, p.max_split,
+                    blockIdx.x / kFixBlocks, tc, nsplit, slot0))
     return;
-  __shared__ __attribute__((aligned(1024))) char lds[69632];
-  __shared__ int row_pair[kBM];
-  __shared__ float row_w[kBM];
   const int tid = threadIdx.x;
-  if (MODE == kDown) load_row_pairs<kThreads>(p, tc, row_pair, row_w, tid);
-  const f32x4_t* const src =
-      reinterpret_cast<const f32x4_t*>(p.partial) + static_cast<size_t>(slot0) * kSlot4;
-  f32x16_t acc[MI][NJ];
+  const float* const src = p.partial + static_cast<size_t>(slot0) * kSlotFloats;
+  if (MODE == kGateUp) {
+    // 8 rows x 128 h columns: thread -> row tid / 32, h columns 4 (tid % 32) .. +3
+    const int row = (blockIdx.x % kFixBlocks) * kFixRows + tid / 32;
+    const int c = (tid % 32) * 4;
+    const int n = tc.ntile * 128 + c;
+    if (row >= tc.rows || n >= p.N) return;
+    const float* q = src + row * kBN + c;
+    f32x4_t g = *reinterpret_cast<const f32x4_t*>(q);
+    f32x4_t u = *reinterpret_cast<const f32x4_t*>(q + 128);
+    for (int t = 1; t < nsplit; ++t) {
+      g += *reinterpret_cast<const f32x4_t*>(q + static_cast<size_t>(t) * kSlotFloats);
+      u += *reinterpret_cast<const f32x4_t*>(q + static_cast<size_t>(t) * kSlotFloats + 128);
+    }
+    const float4 h = make_float4(silu_mul(g[0], u[0]), silu_mul(g[1], u[1]),
+                                 silu_mul(g[2], u[2]), silu_mul(g[3], u[3]));
+    *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(tc.row0 + row) * p.N + n) =
+        pack_bf16x4(h);
+  } else {
+    // 8 rows x 256 output columns in two passes of 4 rows: thread -> column 4 (tid % 64) .. +3
+    const int c = (tid % 64) * 4;
+    const int col = tc.ntile * kBN + c;
+    if (col >= p.N) return;
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const size_t g = static_cast<size_t>(((i * NJ + j) * 4 + q) * kThreads + tid);
-        f32x4_t sum = src[g];
-        for (int t = 1; t < nsplit; ++t) sum += src[g + static_cast<size_t>(t) * kSlot4];
-        acc[i][j][4 * q] = sum[0];
-        acc[i][j][4 * q + 1] = sum[1];
-        acc[i][j][4 * q + 2] = sum[2];
-        acc[i][j][4 * q + 3] = sum[3];
+    for (int pass = 0; pass < 2; ++pass) {
+      const int row = (blockIdx.x % kFixBlocks) * kFixRows + pass * 4 + tid / 64;
+      if (row >= tc.rows) break;
+      const float* q = src + row * kBN + c;
+      f32x4_t a = *reinterpret_cast<const f32x4_t*>(q);
+      for (int t = 1; t < nsplit; ++t)
+        a += *reinterpret_cast<const f32x4_t*>(q + static_cast<size_t>(t) * kSlotFloats);
+      float4 v = make_float4(a[0], a[1], a[2], a[3]);
+      const int pos = tc.row0 + row;
+      if (p.y_layout == MOE_Y_PERMUTED) {
+        const size_t idx = static_cast<size_t>(pos) * p.N + col;
+        if (p.y_bf16) *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = pack_bf16x4(v);
+        else *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
+      } else {
+        const int pair = p.sorted_pair[pos];
+        const float wgt = p.topk_w ? p.topk_w[pair] : 1.0f;
+        v.x *= wgt; v.y *= wgt; v.z *= wgt; v.w *= wgt;
+        if (p.y_layout == MOE_Y_SLOTS) {
+          const size_t idx = static_cast<size_t>(pair) * p.N + col;
+          if (p.y_bf16) *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = pack_bf16x4(v);
+          else *reinterpret_cast<float4*>(static_cast<float*>(p.y) + idx) = v;
+        } else {
+          float* dst = static_cast<float*>(p.y) + static_cast<size_t>(pair / p.k) * p.N + col;
+          atomicAdd(dst + 0, v.x);
+          atomicAdd(dst + 1, v.y);
+          atomicAdd(dst + 2, v.z);
+          atomicAdd(dst + 3, v.w);
+        }
       }
-  __syncthreads();
-  tile_epilogue<MODE, WM, WN>(acc, p, tc, lds, row_pair, row_w);
+    }
+  }
 }
 
 inline long max_tiles(int P, int E, int NT) {
@@ -432,8 +473,8 @@ hipError_t launch_gemm(const Bf16GemmArgs& g, unsigned grid, hipStream_t stream)
                      g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.max_split < 2) return e;
-  hipLaunchKernelGGL((fixup_bf16_kernel<MODE, WM, WN>), dim3(8 * g.cpx), dim3(64 * WM * WN), 0,
-                     stream, g);
+  hipLaunchKernelGGL((fixup_bf16_kernel<MODE>), dim3(8 * g.cpx * kFixBlocks), dim3(256), 0, stream,
+                     g);
   return hipGetLastError();
 }
 

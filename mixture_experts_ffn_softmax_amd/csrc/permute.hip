@@ -28,37 +28,55 @@ __global__ __launch_bounds__(256) void chunk_histogram_kernel(const int32_t* __r
 }
 
 // One block of 1024 threads. counts[e] = sum over chunks; offsets = exclusive scan over experts;
-// chunk_base[c][e] = offsets[e] + pairs of expert e in chunks before c.
+// chunk_base[c][e] = offsets[e] + pairs of expert e in chunks before c. Thread (part, e) with
+// tid = part * EP + e (EP = E rounded up to a power of two) owns a contiguous range of the chunks
+// of expert e, so the G = 1024 / EP parts read the histogram side by side.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ chunk_hist,
-                                                    int nchunks, int E, int P,
+                                                    int nchunks, int E, int EP, int P,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ chunk_base) {
+  __shared__ int part_sum[kMaxExperts];
   __shared__ int s[kMaxExperts];
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) total += chunk_hist[static_cast<size_t>(c) * E + e];
-    counts[e] = total;
-  }
-  s[e] = (e < E) ? total : 0;
+  const int tid = threadIdx.x;
+  const int G = kMaxExperts / EP;
+  const int part = tid / EP, e = tid % EP;
+  const int c0 = static_cast<int>(static_cast<long>(part) * nchunks / G);
+  const int c1 = static_cast<int>(static_cast<long>(part + 1) * nchunks / G);
+  int sum = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c) sum += chunk_hist[static_cast<size_t>(c) * E + e];
+  part_sum[tid] = sum;
   __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 entries.
+  // per expert: total over parts, and each part's exclusive prefix (kept in part_sum)
+  int total = 0;
+  if (tid < EP) {
+    for (int q = 0; q < G; ++q) {
+      const int v = part_sum[q * EP + tid];
+      part_sum[q * EP + tid] = total;
+      total += v;
+    }
+    if (tid < E) counts[tid] = total;
+  }
+  s[tid] = total;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the experts' totals.
   for (int o = 1; o < kMaxExperts; o <<= 1) {
-    int v = (e >= o) ? s[e - o] : 0;
+    int v = (tid >= o) ? s[tid - o] : 0;
     __syncthreads();
-    s[e] += v;
+    s[tid] += v;
     __syncthreads();
   }
   if (e < E) {
-    int run = s[e] - total;  // exclusive
-    offsets[e] = run;
-    for (int c = 0; c < nchunks; ++c) {
+    // start of expert e (inclusive scan of the experts before it) + this part's prefix
+    int run = (e > 0 ? s[e - 1] : 0) + part_sum[tid];
+    if (part == 0) offsets[e] = run;
+    for (int c = c0; c < c1; ++c) {
       chunk_base[static_cast<size_t>(c) * E + e] = run;
       run += chunk_hist[static_cast<size_t>(c) * E + e];
     }
   }
-  if (e == 0) offsets[E] = P;
+  if (tid == 0) offsets[E] = P;
 }
 
 // Stable scatter. The chunk's pairs are taken 256 at a time in flat order; inside a wave, lanes
@@ -140,8 +158,10 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int
   while ((1 << id_bits) < E) ++id_bits;
   hipLaunchKernelGGL(chunk_histogram_kernel, dim3(nchunks), dim3(256), 0, stream, ids, P, E,
                      chunk_hist);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, stream, chunk_hist, nchunks, E, P,
-                     counts, offsets, chunk_base);
+  int EP = 1;
+  while (EP < E) EP <<= 1;
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, stream, chunk_hist, nchunks, E, EP,
+                     P, counts, offsets, chunk_base);
   hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(kScatterThreads), 0, stream, ids, P, E,
                      id_bits, chunk_base, sorted_pair, pair_pos);
   return hipGetLastError();

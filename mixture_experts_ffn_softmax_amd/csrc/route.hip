@@ -21,8 +21,9 @@ __device__ __forceinline__ float load_x<uint16_t>(const uint16_t* p, size_t i) {
   return bf16_bits_to_f32(p[i]);
 }
 
-// One wave computes the logits of 4 tokens against a chunk of 8 experts at a time: every router
-// weight element it loads is used for 4 tokens. Lanes stride over d in runs of 4 elements.
+// Any d and alignment: one wave computes the logits of 4 tokens against a chunk of 8 experts at a
+// time; every router weight element it loads is used for 4 tokens. Lanes stride over d in runs
+// of 4 elements.
 template <typename XT>
 __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict__ x,
                                                             const float* __restrict__ wr, int T,
@@ -69,6 +70,108 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
         if (lane == a * kLogitExpertChunk + b && a < nt && b < ne)
           logits[static_cast<size_t>(t0 + a) * E + e0 + b] = s;
       }
+  }
+}
+
+// Vector path (d % 8 == 0, 16-byte aligned rows): a block of 4 waves computes the logits of
+// kVecTokens tokens against 8 experts at a time. Lane l of wave w covers x[t][i .. i+8) for
+// i = (64 w + l) * 8 + 2048 j, so each wave reads 1 KB contiguous per token and the block splits K
+// four ways. Each lane ends with 64 partial sums (8 tokens x 8 experts); recursive halving over
+// the wave (32 + 16 + ... + 1 exchanges) leaves the full wave sum of entry l in lane l, and the
+// four waves' sums are added through LDS in wave order.
+constexpr int kVecTokens = 8;
+constexpr int kVecExperts = 8;
+
+template <typename XT>
+__device__ __forceinline__ void load_x8(const XT* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load_x8<float>(const float* p, float (&v)[8]) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v[c] = a[c];
+    v[4 + c] = b[c];
+  }
+}
+template <>
+__device__ __forceinline__ void load_x8<uint16_t>(const uint16_t* p, float (&v)[8]) {
+  const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    v[2 * c] = __uint_as_float(w[c] << 16);
+    v[2 * c + 1] = __uint_as_float(w[c] & 0xFFFF0000u);
+  }
+}
+
+// One halving step: lanes with bit H set keep entries [H, 2H), the others [0, H); each adds the
+// partner's copy of the kept half, received in exchange for the half it gives away.
+template <int H>
+__device__ __forceinline__ void halve(float (&v)[64], int lane) {
+  const bool upper = (lane & H) != 0;
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const float send = upper ? v[j] : v[j + H];
+    const float keep = upper ? v[j + H] : v[j];
+    v[j] = keep + __shfl_xor(send, H, 64);
+  }
+}
+
+// After the call lane l holds the sum over the wave of v[l] (all 64 entries reduced at once).
+__device__ __forceinline__ float wave_reduce_scatter64(float (&v)[64], int lane) {
+  halve<32>(v, lane);
+  halve<16>(v, lane);
+  halve<8>(v, lane);
+  halve<4>(v, lane);
+  halve<2>(v, lane);
+  halve<1>(v, lane);
+  return v[0];
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256) void router_logits_vec_kernel(const XT* __restrict__ x,
+                                                                const float* __restrict__ wr,
+                                                                int T, int d, int E,
+                                                                float* __restrict__ logits) {
+  __shared__ float red[4][64];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * kVecTokens;
+  for (int e0 = 0; e0 < E; e0 += kVecExperts) {
+    float acc[64];
+#pragma unroll
+    for (int q = 0; q < 64; ++q) acc[q] = 0.0f;
+    for (int i = (wave * kWave + lane) * 8; i < d; i += 4 * kWave * 8) {
+      float xv[kVecTokens][8];
+#pragma unroll
+      for (int a = 0; a < kVecTokens; ++a) {
+        if (t0 + a < T) {
+          load_x8<XT>(x + static_cast<size_t>(t0 + a) * d + i, xv[a]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) xv[a][c] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kVecExperts; ++b) {
+        if (e0 + b < E) {
+          float wv[8];
+          load_x8<float>(wr + static_cast<size_t>(e0 + b) * d + i, wv);
+#pragma unroll
+          for (int a = 0; a < kVecTokens; ++a)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[a * 8 + b] = fmaf(xv[a][c], wv[c], acc[a * 8 + b]);
+        }
+      }
+    }
+    red[wave][lane] = wave_reduce_scatter64(acc, lane);
+    __syncthreads();
+    if (wave == 0) {
+      const float s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+      const int t = t0 + lane / 8, e = e0 + lane % 8;
+      if (t < T && e < E) logits[static_cast<size_t>(t) * E + e] = s;
+    }
+    __syncthreads();
   }
 }
 
@@ -137,6 +240,18 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 
 hipError_t launch_router_logits(const void* x, moe_dtype x_dtype, const float* wr, int T, int d,
                                 int E, float* logits, hipStream_t stream) {
+  const bool vec = d % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(wr) & 15) == 0;
+  if (vec) {
+    dim3 grid((T + kVecTokens - 1) / kVecTokens), block(256);
+    if (x_dtype == MOE_BF16)
+      hipLaunchKernelGGL(router_logits_vec_kernel<uint16_t>, grid, block, 0, stream,
+                         static_cast<const uint16_t*>(x), wr, T, d, E, logits);
+    else
+      hipLaunchKernelGGL(router_logits_vec_kernel<float>, grid, block, 0, stream,
+                         static_cast<const float*>(x), wr, T, d, E, logits);
+    return hipGetLastError();
+  }
   const int tokens_per_block = 4 * kLogitTokensPerWave;
   dim3 grid((T + tokens_per_block - 1) / tokens_per_block), block(256);
   if (x_dtype == MOE_BF16)
