@@ -88,6 +88,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  // s_waitcnt with vmcnt = N, lgkmcnt = 0 (this wave's LDS reads done), expcnt not waited on
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Buffer resource for raw byte addressing of [base, base + bytes) (out-of-range reads return 0).
 __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);

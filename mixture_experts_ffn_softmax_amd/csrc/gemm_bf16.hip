@@ -55,15 +55,17 @@ __device__ __forceinline__ u32x2_t pack_bf16x4(float4 v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Staging: K is staged 64 at a time (128-byte rows, one whole cache line per row per stage)
-// through two LDS buffers of 64 KB. Each wave-level DMA instruction writes 1 KB = 8 rows x 128 B;
+// Staging: K is staged 64 at a time (128-byte rows, one whole cache line per row per stage). The
+// 160 KB of LDS hold two A buffers and three B buffers of 32 KB: A is fetched one stage ahead,
+// the weight tile B (fewer CUs share it, so more of it misses L2) two stages ahead. Each
+// wave-level DMA instruction writes 1 KB = 8 rows x 128 B;
 // lane l of it fetches the global chunk that belongs at row l / 8, chunk position l % 8. The
 // logical chunk c of row r sits at position c ^ ((r >> 1) & 7), so 16 consecutive rows read at
 // one logical chunk hit 16 distinct 16-byte slots of a 256-byte bank line (conflict free).
 // ---------------------------------------------------------------------------------------------
 constexpr int kBK = 64;
 constexpr int kTile = kBM * kBK * 2;     // bytes per operand per stage (32 KB)
-constexpr int kStage = 2 * kTile;        // A + B (64 KB)
+constexpr int kLds = 5 * kTile;          // A0 A1 B0 B1 B2 (160 KB)
 
 __device__ __forceinline__ int swz(int row, int chunk) {  // byte offset in a 256x128B tile
   return row * (kBK * 2) + ((chunk ^ ((row >> 1) & 7)) << 4);
@@ -106,23 +108,30 @@ __device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[MI][NJ], const Frag<M
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Issues the DMA of stage `st` into one buffer (A tile then B tile). With NW waves, wave w fills
-// rows (IPW w + i) * 8 .. +7 of each operand (i < IPW = 32 / NW); B rows 0..127 come from rb0,
-// rows 128..255 from rb1. A rows at or past the tile's valid rows are skipped (their waves skip
-// the MFMAs). Stages past `last` re-read stage `last` (never used), so every access stays in
-// bounds.
+// DMA of stage `st` of one operand into one buffer. With NW waves, wave w fills rows
+// (IPW w + i) * 8 .. +7 (i < IPW = 32 / NW). A rows at or past the tile's valid rows are skipped
+// (their waves skip the MFMAs); B rows 0..127 come from rb0, rows 128..255 from rb1. Stages past
+// `last` re-read stage `last` (never used), so every access stays in bounds.
 template <int NW>
-__device__ __forceinline__ void dma_stage(const char* buf, const Dma<32 / NW>& d, int st, int last,
-                                          int wave, int rows) {
+__device__ __forceinline__ void dma_a(const char* buf, const Dma<32 / NW>& d, int st, int last,
+                                      int wave, int rows) {
   constexpr int IPW = 32 / NW;
   const uint32_t kb = static_cast<uint32_t>(min(st, last)) * kBK * 2u;
   const uint32_t base = lds_offset(buf);
 #pragma unroll
   for (int i = 0; i < IPW; ++i)
     if ((wave * IPW + i) * 8 < rows) dma16(base + (wave * IPW + i) * 1024, d.aoff[i], d.ra, kb);
+}
+
+template <int NW>
+__device__ __forceinline__ void dma_b(const char* buf, const Dma<32 / NW>& d, int st, int last,
+                                      int wave) {
+  constexpr int IPW = 32 / NW;
+  const uint32_t kb = static_cast<uint32_t>(min(st, last)) * kBK * 2u;
+  const uint32_t base = lds_offset(buf);
 #pragma unroll
   for (int i = 0; i < IPW; ++i)
-    dma16(base + kTile + (wave * IPW + i) * 1024, d.boff[i], wave * IPW < 16 ? d.rb0 : d.rb1, kb);
+    dma16(base + (wave * IPW + i) * 1024, d.boff[i], wave * IPW < 16 ? d.rb0 : d.rb1, kb);
 }
 
 // Partial tiles of cut tiles: fp32, row-major [256 rows][256 tile columns]. Tile column c is
@@ -280,12 +289,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   const int split = __builtin_amdgcn_readfirstlane(wu.split);
   const int nsplit = __builtin_amdgcn_readfirstlane(wu.nsplit);
 
-  // Two stage buffers, contiguous so the epilogue can reuse the whole 128 KB.
-  __shared__ __attribute__((aligned(1024))) char ring[2 * kStage];
-  char* const buf0 = ring;
-  char* const buf1 = ring + kStage;
-  __shared__ int row_pair[kBM];
-  __shared__ float row_w[kBM];
+  // All of LDS: A0 A1 B0 B1 B2; after the main loop the epilogue reuses it (staging from 0,
+  // the down GEMM's row -> pair / weight tables past the staging area).
+  __shared__ __attribute__((aligned(1024))) char ring[kLds];
+  char* const a0 = ring;
+  char* const a1 = ring + kTile;
+  char* const b0 = ring + 2 * kTile;
+  char* const b1 = ring + 3 * kTile;
+  char* const b2 = ring + 4 * kTile;
+  int* const row_pair = reinterpret_cast<int*>(ring + 4 * kTile);
+  float* const row_w = reinterpret_cast<float*>(ring + 4 * kTile + kBM * sizeof(int));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -293,8 +306,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   const int wm = wave / WN, wn = wave % WN;
   const int arow0 = wm * (kBM / WM);
   const int bcol0 = MODE == kGateUp ? wn * (128 / WN) : wn * (kBN / WN);
-
-  if (MODE == kDown) load_row_pairs<kThreads>(p, tc, row_pair, row_w, tid);
 
   // DMA addressing: lane l of instruction i of wave w supplies row (IPW w + i) * 8 + l / 8 at
   // chunk position l % 8.
@@ -329,48 +340,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   const int st0 = split * st_all / nsplit;
   const int nst = (split + 1) * st_all / nsplit - st0;
   const int last = st0 + nst - 1;
-  dma_stage<NW>(buf0, d, st0, last, wave, tc.rows);
-  wait_vmcnt<0>();
+  dma_a<NW>(a0, d, st0, last, wave, tc.rows);
+  dma_b<NW>(b0, d, st0, last, wave);
+  dma_b<NW>(b1, d, st0 + 1, last, wave);
+  wait_vmcnt<IPW>();  // all but this wave's B DMAs of stage 1
   __builtin_amdgcn_s_barrier();
   // Waves whose rows all lie past the tile's valid rows (the short last tile of an expert) skip
   // their fragment reads and MFMAs; the condition is wave-uniform.
   const bool active = arow0 < tc.rows;
   Frag<MI, NJ> fa, fb;
-  if (active) read_frags<MODE, MI, NJ>(fa, buf0, buf0 + kTile, arow0, bcol0, 0, lane);
+  if (active) read_frags<MODE, MI, NJ>(fa, a0, b0, arow0, bcol0, 0, lane);
 
-  // Stage S (from CUR, k-step-0 fragments already in fa): first the DMA of stage S+1 into NXT
-  // (read during stage S-1, which every wave finished before the last barrier), then k-steps
-  // 0..2; then the wait for this wave's DMA of stage S+1 and the barrier after which all of
-  // stage S+1 is in LDS; the next k-step-0 fragments are read while k-step 3 of stage S runs.
-#define MOE_STAGE(CUR, NXT, S)                                                       \
+  // Stage S computes from A buffer AC and B buffer BC, with its k-step-0 fragments already in fa.
+  // It first issues the DMA of A for stage S+1 into AN and of B for stage S+2 into BN2 (both
+  // buffers were last read in stage S-1, which every wave finished, LDS reads included, before
+  // the last barrier), then runs k-steps 0..2. It then waits until only this wave's B DMAs of
+  // stage S+2 are in flight and its LDS reads are done; after the barrier, all of stage S+1 (A in
+  // AN, B in BN1) is in LDS, and its k-step-0 fragments are read while k-step 3 of stage S runs.
+#define MOE_STAGE(AC, BC, AN, BN1, BN2, S)                                           \
   {                                                                                  \
-    dma_stage<NW>(NXT, d, st0 + (S) + 1, last, wave, tc.rows);                       \
+    dma_a<NW>(AN, d, st0 + (S) + 1, last, wave, tc.rows);                            \
+    dma_b<NW>(BN2, d, st0 + (S) + 2, last, wave);                                    \
     if (active) {                                                                    \
-      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 1, lane);         \
+      read_frags<MODE, MI, NJ>(fb, AC, BC, arow0, bcol0, 1, lane);                   \
       mfma_frags<MI, NJ>(acc, fa);                                                   \
-      read_frags<MODE, MI, NJ>(fa, CUR, CUR + kTile, arow0, bcol0, 2, lane);         \
+      read_frags<MODE, MI, NJ>(fa, AC, BC, arow0, bcol0, 2, lane);                   \
       mfma_frags<MI, NJ>(acc, fb);                                                   \
-      read_frags<MODE, MI, NJ>(fb, CUR, CUR + kTile, arow0, bcol0, 3, lane);         \
+      read_frags<MODE, MI, NJ>(fb, AC, BC, arow0, bcol0, 3, lane);                   \
       mfma_frags<MI, NJ>(acc, fa);                                                   \
     }                                                                                \
-    wait_vmcnt<0>();                                                                 \
+    wait_vmcnt_lgkm0<IPW>();                                                         \
     __builtin_amdgcn_s_barrier();                                                    \
     if (active) {                                                                    \
-      read_frags<MODE, MI, NJ>(fa, NXT, NXT + kTile, arow0, bcol0, 0, lane);         \
+      read_frags<MODE, MI, NJ>(fa, AN, BN1, arow0, bcol0, 0, lane);                  \
       mfma_frags<MI, NJ>(acc, fb);                                                   \
     }                                                                                \
   }
-  for (int s = 0; s < nst; s += 2) {
-    MOE_STAGE(buf0, buf1, s)
-    if (s + 1 < nst) MOE_STAGE(buf1, buf0, s + 1)
+  // buffers of stage s: A a[s % 2], B b[s % 3]; the pattern repeats every 6 stages
+  for (int s = 0; s < nst; s += 6) {
+    MOE_STAGE(a0, b0, a1, b1, b2, s)
+    if (s + 1 < nst) MOE_STAGE(a1, b1, a0, b2, b0, s + 1)
+    if (s + 2 < nst) MOE_STAGE(a0, b2, a1, b0, b1, s + 2)
+    if (s + 3 < nst) MOE_STAGE(a1, b0, a0, b1, b2, s + 3)
+    if (s + 4 < nst) MOE_STAGE(a0, b1, a1, b2, b0, s + 4)
+    if (s + 5 < nst) MOE_STAGE(a1, b2, a0, b0, b1, s + 5)
   }
 #undef MOE_STAGE
+  wait_vmcnt<0>();  // the clamped re-reads past the last stage
   __syncthreads();
 
   if (nsplit > 1) {
     // a piece of a cut tile: store the partial in register order and leave the rest to the fix-up
     store_partial<MODE, WM, WN>(acc, p.partial, wu.part_slot, arow0, bcol0, lane);
     return;
+  }
+  if (MODE == kDown) {
+    load_row_pairs<kThreads>(p, tc, row_pair, row_w, tid);
+    __syncthreads();
   }
   tile_epilogue<MODE, WM, WN>(acc, p, tc, ring, row_pair, row_w);
 }
