@@ -27,6 +27,37 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE layer active TFLOP/s (prefill) + tokens/s (decode), % MFMA/HBM peak"
+CSRC = os.path.join(ROOT, "mixture_experts_ffn_softmax_amd", "csrc")
+GEMM_SOURCES = ("common.h", "gemm_bf16.hip")
+DECODE_SOURCES = ("common.h", "decode_bf16.hip")
+
+
+def source_digest(files):
+    """sha256 over the named kernel sources (identifies the kernel build a counter run measured)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(summary_name, files):
+    """HBM bytes per dispatch (FETCH + WRITE, copy-calibrated) from a counter summary under
+    profiles/, or None when the summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", summary_name)
+    try:
+        with open(path) as fh:
+            fields = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("source_sha256") != source_digest(files):
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -318,7 +349,8 @@ def main():
             "kernel": "gemm_bf16_kernel<gate_up> (gate/up grouped GEMM + SwiGLU)",
             "bound": "mfma", "achieved": round(g1_tflops, 2), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(g1_tflops / BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("gemm_bf16_gate_up_mixtral_prefill_hbm_bytes.txt",
+                                        GEMM_SOURCES),
         },
     }
     del layer
@@ -349,7 +381,9 @@ def main():
             "roofline": {
                 "kernel": "decode_bf16_kernel<gate_up> (weight-streaming gate/up GEMM + SwiGLU)",
                 "bound": "hbm", "achieved": round(gbs1, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs1 / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(gbs1 / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("decode_bf16_gate_up_mixtral_decode_hbm_bytes.txt",
+                                            DECODE_SOURCES),
                 "down_ms": round(d2, 4),
             },
         }
