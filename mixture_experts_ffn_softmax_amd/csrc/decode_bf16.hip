@@ -14,6 +14,14 @@
 // (r = l % 16, g = l / 16) loads 64 contiguous bytes (k = 32 g .. 32 g + 31) of its row, and the
 // four MFMAs of the chunk take 8 of those elements each; the token operand uses the same k
 // assignment, so every product pairs matching k.
+//
+// In the gate/up GEMM, experts with at most 16 tokens (the usual decode case) take a streaming
+// kernel instead: one wave per workgroup owns 8 gate rows and the matching 8 up rows for all of
+// K, so no cross-wave reduction and no barrier is needed. Each stage moves 256 K-elements of the
+// 16 rows (512 contiguous bytes per row) from global memory into a four-slot LDS ring by DMA,
+// three stages ahead; the 16 tokens' slices of the same stages are loaded into registers at the
+// same depth, so one in-order vmcnt wait per stage covers both. (For the down GEMM, whose K is
+// 3.5x longer and whose rows are fewer, the K-split kernel above streams as fast or faster.)
 #include "common.h"
 #include "launch.h"
 
@@ -39,6 +47,8 @@ struct DecodeArgs {
   void* y;
   int y_layout, y_bf16;
   const float* topk_w;
+  int small_max;              // experts with at most this many tokens belong to the streaming
+                              // kernel (0: this kernel takes every expert)
 };
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
@@ -57,7 +67,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
   const int rb = blockIdx.x - e * nrb;
   const int row0 = p.offsets[e];
   const int M = p.offsets[e + 1] - row0;
-  if (M == 0) return;
+  if (M <= p.small_max) return;  // empty, or the streaming kernel's expert
 
   __shared__ f32x4_t red[4][4][4][64];  // [wave][row group][token group][lane], 64 KB
 
@@ -187,7 +197,121 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
   }
 }
 
+// ---- streaming kernel for experts with 1..16 tokens ------------------------------------------
+constexpr int kStrRows = 16;                       // weight rows per wave
+constexpr int kStrRing = 4;                        // LDS slots
+constexpr int kStrAhead = kStrRing - 1;            // stages in flight
+
+// Stage `st` (clamped to the last stage) of the wave's 16 rows into `slot` (KS K-elements per
+// row, i.e. CPR = KS / 8 chunks of 16 bytes): instruction i moves rows (64 / CPR) i .. +64/CPR-1;
+// lane l brings logical chunk (l % CPR) ^ (row % CPR) of local row (64 / CPR) i + l / CPR to LDS
+// position l, so chunk q of row r sits at physical chunk q ^ (r % CPR) of that row.
+template <int KS>
+__device__ __forceinline__ void str_dma(const char* slot, const uint32_t (&voff)[KS / 32],
+                                        i32x4_t rsrc0, i32x4_t rsrc1, int st, int nst) {
+  const uint32_t kb = static_cast<uint32_t>(min(st, nst - 1)) * KS * 2u;
+  const uint32_t base = lds_offset(slot);
+#pragma unroll
+  for (int i = 0; i < KS / 32; ++i)
+    dma16(base + i * 1024, voff[i], i >= KS / 64 ? rsrc1 : rsrc0, kb);  // rows 8..15: W_up
+}
+
+template <int KS>
+__global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
+  constexpr int kStage = kStrRows * KS * 2;        // bytes per slot
+  constexpr int kCpr = KS / 8;                     // 16-byte chunks per row per stage
+  constexpr int kNi = KS / 32;                     // DMA instructions (and MFMAs) per stage
+  constexpr int kLoads = 2 * kNi;                  // vector loads per stage (DMA + tokens)
+  constexpr int kOut = 8;                          // h channels per wave (8 gate + 8 up rows)
+  const int nrb = (p.N + kOut - 1) / kOut;
+  const int e = blockIdx.x / nrb;
+  const int rb = blockIdx.x - e * nrb;
+  const int row0 = p.offsets[e];
+  const int M = p.offsets[e + 1] - row0;
+  if (M == 0 || M > 16) return;
+
+  __shared__ __attribute__((aligned(1024))) char ring[kStrRing * kStage];
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15, g = lane >> 4;
+  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  const uint32_t wbytes = static_cast<uint32_t>(p.N) * p.K * 2u;
+  const i32x4_t rs0 = make_rsrc(p.w0 + e * wstride, wbytes);
+  const i32x4_t rs1 = make_rsrc(p.w1 + e * wstride, wbytes);
+  // DMA lane offsets: instruction i, lane l -> local row r (rows 0..7 gate, 8..15 up, both for
+  // h channels rb * 8 + r % 8), logical chunk (l % CPR) ^ (r % CPR).
+  uint32_t voff[kNi];
+#pragma unroll
+  for (int i = 0; i < kNi; ++i) {
+    const int r = i * (64 / kCpr) + lane / kCpr;
+    const int n = rb * 8 + (r & 7);
+    const int c = (lane % kCpr) ^ (r % kCpr);
+    voff[i] = static_cast<uint32_t>(min(n, p.N - 1)) * p.K * 2u + c * 16;
+  }
+  // token operand: lane (t = l % 16, g = l / 16) holds k = 32 u + 8 g .. +7 of token t
+  const int t = min(r16, M - 1);
+  const int pos = row0 + t;
+  const int src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+  const uint16_t* trow = p.a + static_cast<size_t>(src) * p.K + g * 8;
+
+  const int nst = p.K / KS;
+  u32x4_t tok[kStrRing][kNi];
+  auto load_tok = [&](u32x4_t (&tv)[kNi], int st) {
+    const int kb = min(st, nst - 1) * KS;
+#pragma unroll
+    for (int u = 0; u < kNi; ++u) tv[u] = *reinterpret_cast<const u32x4_t*>(trow + kb + u * 32);
+  };
+  // prologue: stages 0 .. kStrAhead - 1
+#pragma unroll
+  for (int q = 0; q < kStrAhead; ++q) {
+    str_dma<KS>(ring + q * kStage, voff, rs0, rs1, q, nst);
+    load_tok(tok[q], q);
+  }
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // Stage S in slot S % 4: wait until stage S has landed (the two newer stages may still be in
+  // flight), issue stage S + 3 into the slot stage S - 1 used (its LDS reads were consumed by that
+  // stage's MFMAs), then KS / 32 MFMAs of 16 weight rows x 16 tokens x 32 K.
+#define MOE_STR_STAGE(Q, S)                                                                   \
+  {                                                                                           \
+    constexpr int QN = (Q + kStrAhead) % kStrRing;                                            \
+    wait_vmcnt<kLoads * (kStrAhead - 1)>();                                                   \
+    str_dma<KS>(ring + QN * kStage, voff, rs0, rs1, (S) + kStrAhead, nst);                    \
+    load_tok(tok[QN], (S) + kStrAhead);                                                       \
+    const char* sl = ring + (Q) * kStage;                                                     \
+    _Pragma("unroll") for (int u = 0; u < kNi; ++u) {                                         \
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(                                  \
+          sl + r16 * (KS * 2) + (((4 * u + g) ^ (r16 % kCpr)) << 4));                          \
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, tok[Q][u]), \
+                                                    acc, 0, 0, 0);                            \
+    }                                                                                         \
+  }
+  for (int s = 0; s < nst; s += kStrRing) {
+    MOE_STR_STAGE(0, s)
+    if (s + 1 < nst) MOE_STR_STAGE(1, s + 1)
+    if (s + 2 < nst) MOE_STR_STAGE(2, s + 2)
+    if (s + 3 < nst) MOE_STR_STAGE(3, s + 3)
+  }
+#undef MOE_STR_STAGE
+  wait_vmcnt<0>();  // the clamped re-reads past the last stage
+
+  // Output layout: lane l holds token l % 16 and local weight rows 4 (l / 16) + i; rows 0..7
+  // (lanes 0..31) are gate, rows 8..15 (lanes 32..63) the matching up rows.
+  f32x4_t up;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32, 64);
+  if (r16 >= M || g >= 2) return;
+  const int n = rb * 8 + 4 * g;
+  if (n >= p.N) return;
+  u32x2_t o;
+  o[0] = f32_to_bf16_bits(silu_mul(acc[0], up[0])) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[1], up[1]))) << 16);
+  o[1] = f32_to_bf16_bits(silu_mul(acc[2], up[2])) |
+         (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[3], up[3]))) << 16);
+  *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(row0 + r16) * p.N + n) = o;
+}
+
 }  // namespace
+
+constexpr int kStrK = 256;  // K per stage of the streaming kernel
 
 int decode_tile_rows() { return 64; }  // unused by the decode kernels; keeps the tile table valid
 
@@ -204,7 +328,13 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   g.offsets = L.offsets;
   g.h = static_cast<uint16_t*>(L.h);
   const unsigned grid1 = static_cast<unsigned>(L.E) * ((L.f + kDecodeGateRows - 1) / kDecodeGateRows);
+  // the streaming kernel needs whole K stages
+  const bool stream_small = L.d % kStrK == 0;
+  g.small_max = stream_small ? 16 : 0;
+  const unsigned grid1s = static_cast<unsigned>(L.E) * ((L.f + 7) / 8);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
+  if (stream_small)
+    hipLaunchKernelGGL(decode_stream_kernel<kStrK>, dim3(grid1s), dim3(64), 0, stream, g);
   hipLaunchKernelGGL(decode_bf16_kernel<kGateUp>, dim3(grid1), dim3(256), 0, stream, g);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
 
@@ -222,6 +352,7 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
   const unsigned grid2 = static_cast<unsigned>(L.E) * ((L.d + kDecodeDownRows - 1) / kDecodeDownRows);
+  dn.small_max = 0;  // the K-split kernel takes every expert of the down GEMM
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
   hipLaunchKernelGGL(decode_bf16_kernel<kDown>, dim3(grid2), dim3(256), 0, stream, dn);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);

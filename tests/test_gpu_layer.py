@@ -126,6 +126,21 @@ def test_decode_kernel_many_tokens_per_expert():
     assert counts.max() > 64
 
 
+def test_decode_mixed_small_and_large_experts():
+    # Skewed routing at a decode-sized batch: some experts get at most 16 tokens (streaming
+    # kernel), others more (the multi-pass kernel); both run in one call, K a multiple of 256.
+    spec = synth.SKEWED_128E.with_(name="bf16_decode_mixed_T100_d512_f1024_E8_k2", T=100, d=512,
+                                   f=1024, E=8, k=2)
+    inp = layer_inputs(spec)
+    ids, _ = oracle.route(inp["logits"], spec.k)
+    counts = np.bincount(ids.reshape(-1), minlength=spec.E)
+    assert counts.max() > 16 and ((counts > 0) & (counts <= 16)).any(), counts
+    for layout in ("slots", "permuted", "acc_f32"):
+        log(spec.name, layout, counts.tolist())
+        res = _run_gpu(spec, inp, layout)
+        _check_layer(spec, inp, res, 2e-2)
+
+
 def test_mixtral_decode_full():
     spec = synth.MIXTRAL_DECODE
     log("generating", spec.name)
