@@ -271,13 +271,15 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   int bm_a, bm_b;
   if (f32) { bm_a = bm_b = f32_tile_rows(); }
   else if (fp8) { bm_a = fp8_tile_rows_gateup(); bm_b = fp8_tile_rows_down(); }
-  else if (decode) { bm_a = bm_b = decode_tile_rows(); }
+  else if (decode) { bm_a = bm_b = 0; }  // no tile table
   else { bm_a = bf16_tile_rows_gateup(); bm_b = bf16_tile_rows_down(); }
 
-  hipError_t e = launch_tile_table(a->offsets, a->E, bm_a, bm_b,
-                                   const_cast<int32_t*>(X.tile_cum_a),
-                                   const_cast<int32_t*>(X.tile_cum_b), stream);
-  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  hipError_t e = hipSuccess;
+  if (!decode) {  // the decode kernels map (expert, row panel) directly and need no tile table
+    e = launch_tile_table(a->offsets, a->E, bm_a, bm_b, const_cast<int32_t*>(X.tile_cum_a),
+                          const_cast<int32_t*>(X.tile_cum_b), stream);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+  }
   if (a->y_layout == MOE_Y_ACC_F32) {
     const size_t n = static_cast<size_t>(a->T) * a->d;
     hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 65536))),

@@ -313,7 +313,6 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
 
 constexpr int kStrK = 256;  // K per stage of the streaming kernel
 
-int decode_tile_rows() { return 64; }  // unused by the decode kernels; keeps the tile table valid
 
 hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream) {
   DecodeArgs g{};

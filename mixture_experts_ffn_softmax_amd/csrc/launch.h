@@ -75,7 +75,6 @@ int bf16_tile_rows_gateup();
 int bf16_tile_rows_down();
 hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream);
 
-int decode_tile_rows();
 hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream);
 
 int fp8_tile_rows_gateup();

@@ -79,23 +79,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (tid == 0) offsets[E] = P;
 }
 
-// Stable scatter. The chunk's pairs are taken 256 at a time in flat order; inside a wave, lanes
-// holding the same expert are found with one ballot per expert-id bit, and a lane's rank is the
-// number of such lanes below it. The four waves then claim their positions one after another from
-// the running per-expert cursor in LDS, so positions follow the flat pair order exactly.
-__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int id_bits,
-    const int32_t* __restrict__ chunk_base, int32_t* __restrict__ sorted_pair,
-    int32_t* __restrict__ pair_pos) {
-  __shared__ int cursor[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    cursor[e] = chunk_base[static_cast<size_t>(blockIdx.x) * E + e];
-  __syncthreads();
+// Stable scatter of pairs [p0, p1) given each expert's next position in `cursor` (LDS). Pairs
+// are taken 256 at a time in flat order; inside a wave, lanes holding the same expert are found
+// with one ballot per expert-id bit, and a lane's rank is the number of such lanes below it. The
+// four waves then claim their positions one after another from the running per-expert cursor, so
+// positions follow the flat pair order exactly. Called by all 256 threads of the block.
+__device__ __forceinline__ void scatter_range(const int32_t* __restrict__ ids, int p0, int p1,
+                                              int id_bits, int* cursor,
+                                              int32_t* __restrict__ sorted_pair,
+                                              int32_t* __restrict__ pair_pos) {
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int p0 = blockIdx.x * kChunk;
-  const int p1 = min(P, p0 + kChunk);
   for (int base = p0; base < p1; base += kScatterThreads) {
     const int p = base + threadIdx.x;
     const bool valid = p < p1;
@@ -118,6 +113,58 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
       __syncthreads();
     }
   }
+}
+
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int id_bits,
+    const int32_t* __restrict__ chunk_base, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_pos) {
+  __shared__ int cursor[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    cursor[e] = chunk_base[static_cast<size_t>(blockIdx.x) * E + e];
+  __syncthreads();
+  scatter_range(ids, blockIdx.x * kChunk, min(P, (blockIdx.x + 1) * kChunk), id_bits, cursor,
+                sorted_pair, pair_pos);
+}
+
+// All of the above in one workgroup when the pairs fit in one chunk (P <= kChunk, e.g. decode):
+// histogram, exclusive scan over the experts, stable scatter.
+__global__ __launch_bounds__(kScatterThreads) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int id_bits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_pos) {
+  __shared__ int cursor[kMaxExperts];
+  __shared__ int part[kScatterThreads];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kScatterThreads) cursor[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kScatterThreads) atomicAdd(&cursor[ids[p]], 1);
+  __syncthreads();
+  // thread t scans experts [t per, (t + 1) per); a block scan of the 256 partial sums gives each
+  // run's start
+  const int per = (E + kScatterThreads - 1) / kScatterThreads;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int sum = 0;
+  for (int e = e0; e < e1; ++e) sum += cursor[e];
+  part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < kScatterThreads; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  for (int e = e0; e < e1; ++e) {
+    const int c = cursor[e];
+    counts[e] = c;
+    offsets[e] = run;
+    cursor[e] = run;
+    run += c;
+  }
+  if (tid == 0) offsets[E] = P;
+  __syncthreads();
+  scatter_range(ids, 0, P, id_bits, cursor, sorted_pair, pair_pos);
 }
 
 // x_perm[r] = x[sorted_pair[r] / k]; one wave per row, 16-byte vectors when the row allows it.
@@ -156,6 +203,11 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int
   int32_t* chunk_base = chunk_hist + static_cast<size_t>(nchunks) * E;
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
+  if (nchunks == 1) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kScatterThreads), 0, stream, ids, P, E,
+                       id_bits, counts, offsets, sorted_pair, pair_pos);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(chunk_histogram_kernel, dim3(nchunks), dim3(256), 0, stream, ids, P, E,
                      chunk_hist);
   int EP = 1;
