@@ -49,6 +49,17 @@ def _check_layer(spec, inp, res, rel, tokens=None):
     return counts
 
 
+def test_f32_layer_odd_sizes():
+    # d and f not multiples of 8 or of the tiles: the fp32 GEMMs' edge guards and the general
+    # (4-element) combine path
+    spec = synth.TINY_F32.with_(name="f32_T50_d100_f60_E4_k2", T=50, d=100, f=60, E=4)
+    inp = layer_inputs(spec)
+    for layout in ("slots", "permuted", "acc_f32"):
+        log(spec.name, layout)
+        res = _run_gpu(spec, inp, layout)
+        _check_layer(spec, inp, res, 1e-4)
+
+
 def test_tiny_f32_layer():
     spec = synth.TINY_F32
     inp = layer_inputs(spec)

@@ -77,6 +77,32 @@ def test_route_router_gemm(T):
         assert srt[1] - srt[2] < 1e-4
 
 
+# The vector router path needs d % 8 == 0 (16-byte rows); other d take the general kernel.
+ROUTER_SHAPES = [
+    ("bf16_d100_scalar", "bf16", 37, 100, 8),
+    ("f32_d256_vector", "f32", 41, 256, 8),
+    ("f32_d60_scalar", "f32", 19, 60, 5),
+    ("bf16_d512_E20_vector", "bf16", 70, 512, 20),
+]
+
+
+@pytest.mark.parametrize("name,xdt,T,d,E", ROUTER_SHAPES, ids=[c[0] for c in ROUTER_SHAPES])
+def test_route_router_gemm_shapes(name, xdt, T, d, E):
+    spec = synth.MIXTRAL_PREFILL.with_(T=T, d=d, E=E)
+    x = synth.gen_x(spec)
+    if xdt == "f32":
+        x = synth.bf16_bits_to_f32(x)
+    Wr = synth.gen_router_weight(spec)
+    log("router gemm", name)
+    ids, w, lg = moe.moe_route(2, x=to_dev(x), w_router=to_dev(Wr))
+    torch.cuda.synchronize()
+    lg_h = to_host(lg)
+    np.testing.assert_allclose(lg_h, oracle.router_logits(x, Wr), rtol=0, atol=1e-4)
+    ids_rep, w_rep = oracle.route(lg_h, 2)
+    np.testing.assert_array_equal(to_host(ids), ids_rep)
+    np.testing.assert_allclose(to_host(w), w_rep, rtol=0, atol=4e-7)
+
+
 PERMUTE_CASES = [
     ("tiny", 64, 2, 8, None),
     ("mixtral_prefill", 4096, 2, 8, None),
@@ -87,6 +113,9 @@ PERMUTE_CASES = [
     ("all_one_expert", 3000, 1, 64, "one"),
     ("max_E_k", 700, 32, 1024, None),
     ("ragged_chunk", 1025, 3, 7, None),
+    # one-workgroup path (P <= 1024): many experts per thread in its scan, and its exact limit
+    ("small_many_experts", 30, 32, 1024, None),
+    ("small_limit", 512, 2, 8, None),
 ]
 
 
