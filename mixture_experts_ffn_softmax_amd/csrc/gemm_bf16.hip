@@ -489,6 +489,14 @@ inline long max_tiles(int P, int E, int NT) {
 // K pieces a tail tile may be cut into: at least 8 stages (512 of K) per piece, at most 8 pieces.
 inline int max_split_for(int K) { return std::max(1, std::min(8, K / kBK / 8)); }
 
+// Tiles are cut only on XCDs with at most kCutMaxRounds whole rounds. An XCD holds at least
+// (total - 49) / 8 tiles, and total >= NT * ceil(P / kBM); when even that bound leaves every XCD
+// more rounds, no tile can be cut and neither cutting nor the fix-up launch is needed.
+inline bool may_cut(int P, int NT, int cpx) {
+  const long min_tiles = static_cast<long>(NT) * ((P + kBM - 1) / kBM);
+  return (min_tiles - 49) / 8 < static_cast<long>(kCutMaxRounds + 1) * cpx;
+}
+
 }  // namespace
 
 int bf16_tile_rows_gateup() { return kBM; }
@@ -528,7 +536,8 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   g.E = L.E;
   g.h = static_cast<uint16_t*>(L.h);
   g.cpx = L.cpx;
-  g.max_split = L.split_partial ? max_split_for(L.d) : 1;
+  g.max_split =
+      L.split_partial && may_cut(P, (L.f + 127) / 128, L.cpx) ? max_split_for(L.d) : 1;
   g.partial = L.split_partial;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
   hipError_t e =
@@ -554,7 +563,8 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
   dn.cpx = L.cpx;
-  dn.max_split = L.split_partial ? max_split_for(L.f) : 1;
+  dn.max_split =
+      L.split_partial && may_cut(P, (L.d + kBN - 1) / kBN, L.cpx) ? max_split_for(L.f) : 1;
   dn.partial = L.split_partial;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
   e = launch_gemm<kDown, MOE_BF16_WAVES>(dn, work_grid(max_tiles(P, L.E, (L.d + kBN - 1) / kBN), L.cpx),

@@ -183,10 +183,11 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Top-k + renormalised softmax weights. A group of G lanes (G a power of two, G = 64 when E > 64)
-// handles one token; each lane holds VPL logits (expert e = lane_in_group + G * v). k rounds of a
-// butterfly argmax inside the group pick the experts in descending order; the lane whose slot
-// index equals the round keeps the winner, so lane j of the group ends with the j-th selection.
+// Top-k + renormalised softmax weights. A group of G lanes (a power of two: pow2(E) up to 16 lanes,
+// more only when k > 16 so that every pick has its own lane) handles one token; each lane holds
+// VPL logits (expert e = lane_in_group + G * v). k rounds of a lane-local scan plus a butterfly
+// argmax inside the group pick the experts in descending order; the lane whose slot index equals
+// the round keeps the winner, so lane j of the group ends with the j-th selection.
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
                                                            int E, int k, int G,
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
                 lane / G;
   const bool tok_ok = t < T;
   float v[VPL];
-  unsigned taken = 0;
+  uint64_t taken = 0;
 #pragma unroll
   for (int q = 0; q < VPL; ++q) {
     int e = gl + G * q;
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 #pragma unroll
     for (int q = 0; q < VPL; ++q) {
       int e = gl + G * q;
-      bool cand = e < E && !((taken >> q) & 1u);
+      bool cand = e < E && !((taken >> q) & 1ull);
       if (cand && better(v[q], e, bv, bi)) { bv = v[q]; bi = e; }
     }
     for (int o = G >> 1; o >= 1; o >>= 1) {
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     if (j == 0) vmax = bv;
 #pragma unroll
     for (int q = 0; q < VPL; ++q)
-      if (gl + G * q == bi) taken |= 1u << q;
+      if (gl + G * q == bi) taken |= 1ull << q;
     if (gl == j) { my_v = bv; my_i = bi; }
   }
   float a = (gl < k) ? expf(my_v - vmax) : 0.0f;
@@ -266,7 +267,8 @@ hipError_t launch_router_logits(const void* x, moe_dtype x_dtype, const float* w
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                                hipStream_t stream) {
   int G = 1;
-  while (G < E && G < kWave) G <<= 1;
+  while (G < E && G < 16) G <<= 1;
+  while (G < k) G <<= 1;  // k <= 32 <= kWave
   const int vpl = (E + G - 1) / G;
   const int tokens_per_block = 4 * (kWave / G);
   dim3 grid((T + tokens_per_block - 1) / tokens_per_block), block(256);
@@ -275,12 +277,14 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t
     hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, block, 0, stream, logits, T, E, k, G, ids, \
                        w);                                                                    \
     break;
-  switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : 16) {
+  switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : vpl <= 16 ? 16 : vpl <= 32 ? 32 : 64) {
     MOE_TOPK_CASE(1)
     MOE_TOPK_CASE(2)
     MOE_TOPK_CASE(4)
     MOE_TOPK_CASE(8)
     MOE_TOPK_CASE(16)
+    MOE_TOPK_CASE(32)
+    MOE_TOPK_CASE(64)
   }
 #undef MOE_TOPK_CASE
   return hipGetLastError();
