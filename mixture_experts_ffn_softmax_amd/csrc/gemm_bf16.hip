@@ -77,35 +77,59 @@ struct Dma {
   uint32_t aoff[IPW], boff[IPW];   // per-lane byte offsets of the thread's A and B rows
 };
 
+// MFMA block edge ME: 32 (v_mfma_f32_32x32x16_bf16, a k-step covers 16 of K) or 16
+// (v_mfma_f32_16x16x32_bf16, a k-step covers 32 of K). Operand fragments: lane l holds row (or
+// weight row) l % ME and 16-byte chunk l / ME of the k-step. Accumulator element e of block
+// (i, j) in lane l: row acc_row<ME>(e, l), column acc_col<ME>(l) inside the block.
+template <int ME> struct AccOf;
+template <> struct AccOf<32> { using type = f32x16_t; static constexpr int n = 16; };
+template <> struct AccOf<16> { using type = f32x4_t; static constexpr int n = 4; };
+template <int ME> using acc_t = typename AccOf<ME>::type;
+
+template <int ME>
+__device__ __forceinline__ int acc_row(int e, int lane) {
+  return ME == 32 ? (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3) : (lane >> 4) * 4 + e;
+}
+template <int ME>
+__device__ __forceinline__ int acc_col(int lane) { return lane & (ME - 1); }
+
 template <int MI, int NJ>
 struct Frag {
   bf16x8_t a[MI], b[NJ];
 };
 
-template <int MODE, int MI, int NJ>
-__device__ __forceinline__ void read_frags(Frag<MI, NJ>& f, const char* As, const char* Bs,
-                                           int arow0, int bcol0, int ks, int lane) {
-  const int ch = 2 * ks + (lane >> 5);
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-    f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + swz(arow0 + i * 32 + (lane & 31), ch));
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    // gate/up: the first NJ/2 column blocks are gate rows, the rest the matching up rows
-    const int brow = MODE == kGateUp
-                         ? (j < NJ / 2 ? bcol0 + j * 32 : 128 + bcol0 + (j - NJ / 2) * 32)
-                         : bcol0 + j * 32;
-    f.b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(brow + (lane & 31), ch));
-  }
+// First tile column of column block j: gate/up puts the first NJ/2 blocks on gate rows and the
+// rest on the matching up rows.
+template <int MODE, int ME, int NJ>
+__device__ __forceinline__ int col_base(int bcol0, int j) {
+  return MODE == kGateUp ? (j < NJ / 2 ? bcol0 + j * ME : 128 + bcol0 + (j - NJ / 2) * ME)
+                         : bcol0 + j * ME;
 }
 
-template <int MI, int NJ>
-__device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[MI][NJ], const Frag<MI, NJ>& f) {
+template <int MODE, int ME, int MI, int NJ>
+__device__ __forceinline__ void read_frags(Frag<MI, NJ>& f, const char* As, const char* Bs,
+                                           int arow0, int bcol0, int ks, int lane) {
+  const int ch = (ME == 32 ? 2 : 4) * ks + lane / ME;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8_t*>(As + swz(arow0 + i * ME + (lane & (ME - 1)), ch));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    f.b[j] = *reinterpret_cast<const bf16x8_t*>(
+        Bs + swz(col_base<MODE, ME, NJ>(bcol0, j) + (lane & (ME - 1)), ch));
+}
+
+template <int ME, int MI, int NJ>
+__device__ __forceinline__ void mfma_frags(acc_t<ME> (&acc)[MI][NJ], const Frag<MI, NJ>& f) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (ME == 32)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    }
 }
 
 // DMA of stage `st` of one operand into one buffer. The first DW waves issue all of it: wave
@@ -143,25 +167,18 @@ __device__ __forceinline__ void dma_b(const char* buf, const Dma<32 / DW>& d, in
 // segments.
 constexpr int kSlotFloats = kBM * kBN;
 
-template <int MODE, int WM, int WN>
-__device__ __forceinline__ void store_partial(const f32x16_t (&acc)[kBM / WM / 32][kBN / WN / 32],
-                                              float* partial, int slot, int arow0, int bcol0,
-                                              int lane) {
-  constexpr int MI = kBM / WM / 32;
-  constexpr int NJ = kBN / WN / 32;
+template <int MODE, int ME, int MI, int NJ>
+__device__ __forceinline__ void store_partial(const acc_t<ME> (&acc)[MI][NJ], float* partial,
+                                              int slot, int arow0, int bcol0, int lane) {
   float* const dst = partial + static_cast<size_t>(slot) * kSlotFloats;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int col = MODE == kGateUp
-                          ? (j < NJ / 2 ? bcol0 + j * 32 : 128 + bcol0 + (j - NJ / 2) * 32)
-                          : bcol0 + j * 32;
+      const int col = col_base<MODE, ME, NJ>(bcol0, j) + acc_col<ME>(lane);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = arow0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        dst[row * kBN + col + (lane & 31)] = acc[i][j][r];
-      }
+      for (int e = 0; e < AccOf<ME>::n; ++e)
+        dst[(arow0 + i * ME + acc_row<ME>(e, lane)) * kBN + col] = acc[i][j][e];
     }
 }
 
@@ -181,14 +198,14 @@ __device__ __forceinline__ void load_row_pairs(const Bf16GemmArgs& p, const Tile
 // Epilogue of one finished 256 x 256 tile held in the accumulators: gate/up applies SwiGLU and
 // stores the 256 x 128 h tile in bf16; down applies the routing weight and writes the requested
 // output layout. `lds` is at least 69632 bytes; row_pair / row_w are filled for the down GEMM.
-template <int MODE, int WM, int WN>
-__device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[kBM / WM / 32][kBN / WN / 32],
+template <int MODE, int WM, int WN, int ME>
+__device__ __forceinline__ void tile_epilogue(acc_t<ME> (&acc)[kBM / WM / ME][kBN / WN / ME],
                                               const Bf16GemmArgs& p, const TileCoord& tc,
                                               char* lds, const int* row_pair,
                                               const float* row_w) {
   constexpr int kThreads = 64 * WM * WN;
-  constexpr int MI = kBM / WM / 32;
-  constexpr int NJ = kBN / WN / 32;
+  constexpr int MI = kBM / WM / ME;
+  constexpr int NJ = kBN / WN / ME;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -204,10 +221,10 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[kBM / WM / 32][kBN
 #pragma unroll
       for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = arow0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = bcol0 + j * 32 + (lane & 31);
-          hs[row * kHS + col] = f32_to_bf16_bits(silu_mul(acc[i][j][r], acc[i][j + NJ / 2][r]));
+        for (int e = 0; e < AccOf<ME>::n; ++e) {
+          const int row = arow0 + i * ME + acc_row<ME>(e, lane);
+          const int col = bcol0 + j * ME + acc_col<ME>(lane);
+          hs[row * kHS + col] = f32_to_bf16_bits(silu_mul(acc[i][j][e], acc[i][j + NJ / 2][e]));
         }
     __syncthreads();
     const int n0 = tc.ntile * 128;
@@ -226,15 +243,15 @@ __device__ __forceinline__ void tile_epilogue(f32x16_t (&acc)[kBM / WM / 32][kBN
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const int rbase = arow0 + i * 32;
+        const int rbase = arow0 + i * ME;
         if (rbase >= q * 64 && rbase < q * 64 + 64) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = rbase - q * 64 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-              const int col = bcol0 + j * 32 + (lane & 31);
-              ys[row * kYS + col] = acc[i][j][r];
+            for (int e = 0; e < AccOf<ME>::n; ++e) {
+              const int row = rbase - q * 64 + acc_row<ME>(e, lane);
+              const int col = bcol0 + j * ME + acc_col<ME>(lane);
+              ys[row * kYS + col] = acc[i][j][e];
             }
         }
       }
@@ -282,8 +299,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   constexpr int DW = MODE == kGateUp ? NW / 2 : NW;
   constexpr int IPW = 32 / DW;     // DMA instructions per DMA wave per operand per stage
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  constexpr int MI = kBM / WM / 32;
-  constexpr int NJ = kBN / WN / 32;
+  // MFMA shape: 16x16x32 for gate/up, 32x32x16 for down (each measured the faster there)
+  constexpr int ME = MODE == kGateUp ? 16 : 32;
+  constexpr int MI = kBM / WM / ME;
+  constexpr int NJ = kBN / WN / ME;
   const int NT = MODE == kGateUp ? (p.N + 127) / 128 : (p.N + kBN - 1) / kBN;
   WorkUnit wu;
   if (!map_work(p.tile_cum, p.offsets, p.E, kBM, NT, p.cpx, p.max_split, wu)) return;
@@ -334,13 +353,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
     d.boff[i] = static_cast<uint32_t>(n) * p.K * 2u + c * 16;
   }
 
-  f32x16_t acc[MI][NJ];
+  acc_t<ME> acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int e = 0; e < AccOf<ME>::n; ++e) acc[i][j][e] = 0.0f;
 
   // this piece's stages: [st0, st0 + nst) of the K / kBK stages
   const int st_all = p.K / kBK;
@@ -356,31 +375,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   // their fragment reads and MFMAs; the condition is wave-uniform.
   const bool active = arow0 < tc.rows;
   Frag<MI, NJ> fa, fb;
-  if (active) read_frags<MODE, MI, NJ>(fa, a0, b0, arow0, bcol0, 0, lane);
+  if (active) read_frags<MODE, ME, MI, NJ>(fa, a0, b0, arow0, bcol0, 0, lane);
 
   // Stage S computes from A buffer AC and B buffer BC, with its k-step-0 fragments already in fa.
   // It first issues the DMA of A for stage S+1 into AN and of B for stage S+2 into BN2 (both
   // buffers were last read in stage S-1, which every wave finished, LDS reads included, before
-  // the last barrier), then runs k-steps 0..2. It then waits until only this wave's B DMAs of
-  // stage S+2 are in flight and its LDS reads are done; after the barrier, all of stage S+1 (A in
-  // AN, B in BN1) is in LDS, and its k-step-0 fragments are read while k-step 3 of stage S runs.
+  // the last barrier), then runs its k-steps but the last (4 of 16 K for ME = 32, 2 of 32 K for
+  // ME = 16), reading each k-step's fragments during the previous one's MFMAs. It then waits until
+  // only this wave's B DMAs of stage S+2 are in flight and its LDS reads are done; after the
+  // barrier, all of stage S+1 (A in AN, B in BN1) is in LDS, and its k-step-0 fragments are read
+  // while the last k-step of stage S runs.
 #define MOE_STAGE(AC, BC, AN, BN1, BN2, S)                                           \
   {                                                                                  \
     dma_a<DW>(AN, d, st0 + (S) + 1, last, wave, tc.rows);                            \
     dma_b<DW>(BN2, d, st0 + (S) + 2, last, wave);                                    \
     if (active) {                                                                    \
-      read_frags<MODE, MI, NJ>(fb, AC, BC, arow0, bcol0, 1, lane);                   \
-      mfma_frags<MI, NJ>(acc, fa);                                                   \
-      read_frags<MODE, MI, NJ>(fa, AC, BC, arow0, bcol0, 2, lane);                   \
-      mfma_frags<MI, NJ>(acc, fb);                                                   \
-      read_frags<MODE, MI, NJ>(fb, AC, BC, arow0, bcol0, 3, lane);                   \
-      mfma_frags<MI, NJ>(acc, fa);                                                   \
+      read_frags<MODE, ME, MI, NJ>(fb, AC, BC, arow0, bcol0, 1, lane);               \
+      mfma_frags<ME, MI, NJ>(acc, fa);                                               \
+      if constexpr (ME == 32) {                                                      \
+        read_frags<MODE, ME, MI, NJ>(fa, AC, BC, arow0, bcol0, 2, lane);             \
+        mfma_frags<ME, MI, NJ>(acc, fb);                                             \
+        read_frags<MODE, ME, MI, NJ>(fb, AC, BC, arow0, bcol0, 3, lane);             \
+        mfma_frags<ME, MI, NJ>(acc, fa);                                             \
+      }                                                                              \
     }                                                                                \
     wait_vmcnt_lgkm0<IPW>();                                                         \
     __builtin_amdgcn_s_barrier();                                                    \
     if (active) {                                                                    \
-      read_frags<MODE, MI, NJ>(fa, AN, BN1, arow0, bcol0, 0, lane);                  \
-      mfma_frags<MI, NJ>(acc, fb);                                                   \
+      read_frags<MODE, ME, MI, NJ>(fa, AN, BN1, arow0, bcol0, 0, lane);              \
+      mfma_frags<ME, MI, NJ>(acc, fb);                                               \
     }                                                                                \
   }
   // buffers of stage s: A a[s % 2], B b[s % 3]; the pattern repeats every 6 stages
@@ -398,14 +421,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
 
   if (nsplit > 1) {
     // a piece of a cut tile: store the partial in register order and leave the rest to the fix-up
-    store_partial<MODE, WM, WN>(acc, p.partial, wu.part_slot, arow0, bcol0, lane);
+    store_partial<MODE, ME, MI, NJ>(acc, p.partial, wu.part_slot, arow0, bcol0, lane);
     return;
   }
   if (MODE == kDown) {
     load_row_pairs<kThreads>(p, tc, row_pair, row_w, tid);
     __syncthreads();
   }
-  tile_epilogue<MODE, WM, WN>(acc, p, tc, ring, row_pair, row_w);
+  tile_epilogue<MODE, WM, WN, ME>(acc, p, tc, ring, row_pair, row_w);
 }
 
 
