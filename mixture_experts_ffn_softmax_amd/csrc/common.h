@@ -30,10 +30,8 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 
 // Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs; NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  // gfx950 converts in hardware (v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN)
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // OCP E4M3FN encode: round to nearest even, saturate to +-448 (0x7E / 0xFE); zero keeps its sign.
@@ -77,7 +75,9 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  // the hardware reciprocal (1 ulp) instead of an IEEE division: the result is rounded to bf16
+  // or quantised afterwards, far coarser than either
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---- global -> LDS DMA ---------------------------------------------------------------------------
