@@ -195,9 +195,14 @@ __device__ __forceinline__ void load_row_pairs(const Bf16GemmArgs& p, const Tile
   }
 }
 
+// LDS staging of the epilogue: gate/up h [256][136] bf16 (69632 B); down with bf16 output
+// [256][264] bf16 (135168 B); down with fp32 output [64][260] fp32 per pass (66560 B).
+constexpr int kStageBytes = kBM * 264 * 2;
+static_assert(kStageBytes + kBM * 8 <= kLds, "row tables past the staging area");
+
 // Epilogue of one finished 256 x 256 tile held in the accumulators: gate/up applies SwiGLU and
 // stores the 256 x 128 h tile in bf16; down applies the routing weight and writes the requested
-// output layout. `lds` is at least 69632 bytes; row_pair / row_w are filled for the down GEMM.
+// output layout. row_pair / row_w are filled for the down GEMM.
 template <int MODE, int WM, int WN, int ME>
 __device__ __forceinline__ void tile_epilogue(acc_t<ME> (&acc)[kBM / WM / ME][kBN / WN / ME],
                                               const Bf16GemmArgs& p, const TileCoord& tc,
@@ -233,6 +238,38 @@ __device__ __forceinline__ void tile_epilogue(acc_t<ME> (&acc)[kBM / WM / ME][kB
       if (row < tc.rows && n0 + ch * 8 < p.N)
         *reinterpret_cast<u32x4_t*>(p.h + static_cast<size_t>(tc.row0 + row) * p.N + n0 + ch * 8) =
             *reinterpret_cast<const u32x4_t*>(hs + row * kHS + ch * 8);
+    }
+  } else if (p.y_bf16 && p.y_layout != MOE_Y_ACC_F32) {
+    // bf16 rows (weighted for the slot layout): the whole tile staged once as [256][264] bf16,
+    // every wave writing its rows, then 16-byte row segments to the output row of each pair
+    // (slots) or sorted position (permuted). The 528-byte row stride puts the two 64-byte row
+    // segments of one write instruction (rows r and r + 4) in different banks.
+    constexpr int kYS = 264;
+    uint16_t* ys = reinterpret_cast<uint16_t*>(lds);
+    const bool weighted = p.y_layout == MOE_Y_SLOTS;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int e = 0; e < AccOf<ME>::n; ++e) {
+        const int row = arow0 + i * ME + acc_row<ME>(e, lane);
+        const float wgt = weighted ? row_w[row] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          ys[row * kYS + bcol0 + j * ME + acc_col<ME>(lane)] = f32_to_bf16_bits(acc[i][j][e] * wgt);
+      }
+    }
+    __syncthreads();
+    const int n0 = tc.ntile * kBN;
+    uint16_t* const y = static_cast<uint16_t*>(p.y);
+    for (int q = tid; q < kBM * (kBN / 8); q += kThreads) {
+      const int row = q / (kBN / 8), ch = q % (kBN / 8);
+      const int col = n0 + ch * 8;
+      if (row < tc.rows && col < p.N) {
+        const size_t orow = weighted ? static_cast<size_t>(row_pair[row])
+                                     : static_cast<size_t>(tc.row0 + row);
+        *reinterpret_cast<u32x4_t*>(y + orow * p.N + col) =
+            *reinterpret_cast<const u32x4_t*>(ys + row * kYS + ch * 8);
+      }
     }
   } else {
     // Passes of 64 rows staged as fp32 [64][260] (66560 B of the ring).
@@ -323,8 +360,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   char* const b0 = ring + 2 * kTile;
   char* const b1 = ring + 3 * kTile;
   char* const b2 = ring + 4 * kTile;
-  int* const row_pair = reinterpret_cast<int*>(ring + 4 * kTile);
-  float* const row_w = reinterpret_cast<float*>(ring + 4 * kTile + kBM * sizeof(int));
+  // the down GEMM's row tables sit past the epilogue's staging area (at most kStageBytes)
+  int* const row_pair = reinterpret_cast<int*>(ring + kStageBytes);
+  float* const row_w = reinterpret_cast<float*>(ring + kStageBytes + kBM * sizeof(int));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
