@@ -175,6 +175,49 @@ __global__ __launch_bounds__(256) void router_logits_vec_kernel(const XT* __rest
   }
 }
 
+// Few tokens (a decode step): one block per token, so the router weights are read by many CUs at
+// once instead of a handful. Thread j covers x[t][i .. i+8) for i = 8 j + 2048 n against 8 experts
+// at a time; the 8 sums are reduced over each wave and then over the 4 waves in wave order.
+template <typename XT>
+__global__ __launch_bounds__(256) void router_logits_tok_kernel(const XT* __restrict__ x,
+                                                                const float* __restrict__ wr,
+                                                                int d, int E,
+                                                                float* __restrict__ logits) {
+  __shared__ float red[4][kVecExperts];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int t = blockIdx.x;
+  for (int e0 = 0; e0 < E; e0 += kVecExperts) {
+    float acc[kVecExperts];
+#pragma unroll
+    for (int b = 0; b < kVecExperts; ++b) acc[b] = 0.0f;
+    for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
+      float xv[8];
+      load_x8<XT>(x + static_cast<size_t>(t) * d + i, xv);
+#pragma unroll
+      for (int b = 0; b < kVecExperts; ++b) {
+        if (e0 + b < E) {
+          float wv[8];
+          load_x8<float>(wr + static_cast<size_t>(e0 + b) * d + i, wv);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[b] = fmaf(xv[c], wv[c], acc[b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kVecExperts; ++b) {
+      const float v = wave_sum(acc[b]);
+      if (lane == b) red[wave][b] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < kVecExperts && e0 + threadIdx.x < E) {
+      const int b = threadIdx.x;
+      logits[static_cast<size_t>(t) * E + e0 + b] = ((red[0][b] + red[1][b]) + red[2][b]) + red[3][b];
+    }
+    __syncthreads();
+  }
+}
+
 // "a is a better candidate than b": larger logit, equal logits -> lower expert index;
 // index < 0 means "no candidate".
 __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
@@ -243,6 +286,16 @@ hipError_t launch_router_logits(const void* x, moe_dtype x_dtype, const float* w
                                 int E, float* logits, hipStream_t stream) {
   const bool vec = d % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(wr) & 15) == 0;
+  if (vec && T < 256) {
+    // fewer than 32 blocks of the token-group kernel would leave most CUs idle
+    if (x_dtype == MOE_BF16)
+      hipLaunchKernelGGL(router_logits_tok_kernel<uint16_t>, dim3(T), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(x), wr, d, E, logits);
+    else
+      hipLaunchKernelGGL(router_logits_tok_kernel<float>, dim3(T), dim3(256), 0, stream,
+                         static_cast<const float*>(x), wr, d, E, logits);
+    return hipGetLastError();
+  }
   if (vec) {
     dim3 grid((T + kVecTokens - 1) / kVecTokens), block(256);
     if (x_dtype == MOE_BF16)

@@ -82,7 +82,8 @@ ROUTER_SHAPES = [
     ("bf16_d100_scalar", "bf16", 37, 100, 8),
     ("f32_d256_vector", "f32", 41, 256, 8),
     ("f32_d60_scalar", "f32", 19, 60, 5),
-    ("bf16_d512_E20_vector", "bf16", 70, 512, 20),
+    ("bf16_d512_E20_vector", "bf16", 70, 512, 20),      # one block per token (T < 256)
+    ("bf16_d256_T300_E12_vector_groups", "bf16", 300, 256, 12),  # 8-token groups (T >= 256)
 ]
 
 
