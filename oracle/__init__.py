@@ -20,6 +20,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16, E4M3 = 0, 1, 2
+SCALE_FMTS = {"f32": 0, "ue8m0": 1}   # block scales: fp32 values, or UE8M0 bytes (2^(b-127))
 
 
 def build(force: bool = True) -> str:
@@ -46,17 +47,24 @@ def _load():
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [f32]
         lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_ue8m0_scale.argtypes = [f32]
+        lib.oracle_ue8m0_scale.restype = ctypes.c_uint8
         lib.oracle_quantize_act.argtypes = [vp, i32, i32, i32, i32, vp, vp]
         lib.oracle_quantize_weight.argtypes = [vp, i32, i32, i32, vp, vp]
+        lib.oracle_quantize_act_ue8m0.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        lib.oracle_quantize_weight_ue8m0.argtypes = [vp, i32, i32, i32, vp, vp]
         lib.oracle_router_logits.argtypes = [vp, i32, vp, i32, i32, i32, vp]
         lib.oracle_route.argtypes = [vp, i32, i32, i32, vp, vp]
         lib.oracle_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         lib.oracle_expert_pairs.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, i32,
-                                            i32, vp, vp, vp, vp]
+                                            i32, i32, vp, vp, vp, vp]
         lib.oracle_moe_forward.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
-                                           vp, i32, vp, vp, i32, vp, vp]
+                                           vp, i32, i32, vp, vp, i32, vp, vp]
         lib.oracle_combine_permuted.argtypes = [vp, vp, vp, i32, i32, i32, vp]
-        for fn in ("oracle_quantize_act", "oracle_quantize_weight", "oracle_router_logits",
+        for fn in ("oracle_quantize_act", "oracle_quantize_weight", "oracle_quantize_act_ue8m0",
+                   "oracle_quantize_weight_ue8m0", "oracle_router_logits",
                    "oracle_route", "oracle_permute", "oracle_expert_pairs", "oracle_moe_forward",
                    "oracle_combine_permuted"):
             getattr(lib, fn).restype = None
@@ -101,32 +109,59 @@ def e4m3_decode_array(q: np.ndarray) -> np.ndarray:
     return table[np.asarray(q, dtype=np.uint8)]
 
 
+def e8m0_value(b: int) -> float:
+    return _load().oracle_e8m0_value(b)
+
+
+def ue8m0_scale(amax: float) -> int:
+    return _load().oracle_ue8m0_scale(amax)
+
+
+def e8m0_decode_array(b: np.ndarray) -> np.ndarray:
+    table = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(b, dtype=np.uint8)]
+
+
+def scale_values(s: np.ndarray, scale_fmt: str = "f32") -> np.ndarray:
+    """Block scales as float64 values (fp32 scales as they are, UE8M0 bytes decoded)."""
+    return e8m0_decode_array(s) if scale_fmt == "ue8m0" else np.asarray(s, np.float64)
+
+
 # ---- fine-grained FP8 rule --------------------------------------------------------------------
 
-def quantize_act(x: np.ndarray, group: int = 128):
-    """x [M, K] fp32 or bf16 bits -> (q [M, K] uint8 e4m3, s [M, K/group] fp32)."""
+def quantize_act(x: np.ndarray, group: int = 128, scale_fmt: str = "f32"):
+    """x [M, K] fp32 or bf16 bits -> (q [M, K] uint8 e4m3, s [M, K/group]): fp32 scales, or
+    UE8M0 bytes for scale_fmt="ue8m0"."""
     x = _c(x)
     M, K = x.shape
     assert K % group == 0
     q = np.empty((M, K), np.uint8)
-    s = np.empty((M, K // group), np.float32)
-    _load().oracle_quantize_act(x.ctypes.data, _dtype_code(x), M, K, group, q.ctypes.data,
+    lib = _load()
+    if scale_fmt == "ue8m0":
+        s = np.empty((M, K // group), np.uint8)
+        lib.oracle_quantize_act_ue8m0(x.ctypes.data, _dtype_code(x), M, K, group, q.ctypes.data,
+                                      s.ctypes.data)
+    else:
+        s = np.empty((M, K // group), np.float32)
+        lib.oracle_quantize_act(x.ctypes.data, _dtype_code(x), M, K, group, q.ctypes.data,
                                 s.ctypes.data)
     return q, s
 
 
-def quantize_weight(W: np.ndarray, block: int = 128):
-    """W [..., N, K] fp32 -> (q [..., N, K] e4m3, s [..., N/block, K/block] fp32)."""
+def quantize_weight(W: np.ndarray, block: int = 128, scale_fmt: str = "f32"):
+    """W [..., N, K] fp32 -> (q [..., N, K] e4m3, s [..., N/block, K/block]): fp32 scales, or
+    UE8M0 bytes for scale_fmt="ue8m0"."""
     W = _c(W, np.float32)
     lead, (N, K) = W.shape[:-2], W.shape[-2:]
     assert N % block == 0 and K % block == 0
     Wf = W.reshape(-1, N, K)
     q = np.empty(Wf.shape, np.uint8)
-    s = np.empty((Wf.shape[0], N // block, K // block), np.float32)
+    ue = scale_fmt == "ue8m0"
+    s = np.empty((Wf.shape[0], N // block, K // block), np.uint8 if ue else np.float32)
     lib = _load()
+    fn = lib.oracle_quantize_weight_ue8m0 if ue else lib.oracle_quantize_weight
     for e in range(Wf.shape[0]):
-        lib.oracle_quantize_weight(Wf[e].ctypes.data, N, K, block, q[e].ctypes.data,
-                                   s[e].ctypes.data)
+        fn(Wf[e].ctypes.data, N, K, block, q[e].ctypes.data, s[e].ctypes.data)
     return q.reshape(W.shape), s.reshape(lead + (N // block, K // block))
 
 
@@ -173,27 +208,32 @@ def permute(ids: np.ndarray, E: int):
 class Experts:
     """Expert weights: W_gate, W_up [E, f, d]; W_down [E, d, f] (fp32, bf16 bits or e4m3 codes).
 
-    For e4m3 weights the fp32 block scales s_gate, s_up [E, f/128, d/128] and s_down
-    [E, d/128, f/128] are required. ``quant_act`` applies the fp8 activation rule to x and h.
+    For e4m3 weights the block scales s_gate, s_up [E, f/128, d/128] and s_down
+    [E, d/128, f/128] are required: fp32, or UE8M0 bytes with ``scale_fmt="ue8m0"`` (then the
+    activation rule uses UE8M0 scales too). ``quant_act`` applies the fp8 activation rule to x
+    and h.
     """
 
     def __init__(self, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
-                 quant_act=False):
+                 quant_act=False, scale_fmt="f32"):
         self.w_gate, self.w_up, self.w_down = _c(w_gate), _c(w_up), _c(w_down)
         self.E, self.f, self.d = self.w_gate.shape
         assert self.w_up.shape == self.w_gate.shape
         assert self.w_down.shape == (self.E, self.d, self.f)
         self.w_dtype = _dtype_code(self.w_gate)
-        self.s_gate = None if s_gate is None else _c(s_gate, np.float32)
-        self.s_up = None if s_up is None else _c(s_up, np.float32)
-        self.s_down = None if s_down is None else _c(s_down, np.float32)
+        self.scale_fmt = scale_fmt
+        sdt = np.uint8 if scale_fmt == "ue8m0" else np.float32
+        self.s_gate = None if s_gate is None else _c(s_gate, sdt)
+        self.s_up = None if s_up is None else _c(s_up, sdt)
+        self.s_down = None if s_down is None else _c(s_down, sdt)
         if self.w_dtype == E4M3:
             assert self.s_gate is not None and self.s_up is not None and self.s_down is not None
         self.quant_act = bool(quant_act)
 
     def _wargs(self):
         return (self.w_dtype, _ptr(self.w_gate), _ptr(self.w_up), _ptr(self.w_down),
-                _ptr(self.s_gate), _ptr(self.s_up), _ptr(self.s_down), int(self.quant_act))
+                _ptr(self.s_gate), _ptr(self.s_up), _ptr(self.s_down), int(self.quant_act),
+                SCALE_FMTS[self.scale_fmt])
 
 
 def expert_pairs(x: np.ndarray, experts: Experts, tok: np.ndarray, exp_of: np.ndarray,

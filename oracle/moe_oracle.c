@@ -30,7 +30,12 @@
  *     expert hidden activation h is quantised by the same per-token 128-group rule before the down
  *     projection;
  *   - the stable permutation orders (token, slot) pairs by expert, and by flat index t*k + j within
- *     an expert.
+ *     an expert;
+ *   - UE8M0 scale format (p2, section "UE8M0 scale format"; its note on Blackwell): every block
+ *     scale is a power of two stored as one float8_e8m0fnu byte b (value 2^(b-127)). The pages give
+ *     no rule for choosing it; here the scale of a group is the smallest power of two 2^e with
+ *     448 * 2^e >= amax (so no code saturates; e = 0 for an all-zero group), for weight blocks and
+ *     for the dynamic activation groups alike, and codes are E4M3(v * 2^-e), an exact scaling.
  */
 #include <math.h>
 #include <stdint.h>
@@ -106,6 +111,36 @@ static double load_value(const void* p, int dtype, size_t i) {
  * Fine-grained FP8 quantisation rule (p2 intro)
  * ------------------------------------------------------------------------------------------- */
 
+/* UE8M0 (float8_e8m0fnu): byte b encodes 2^(b - 127); 255 encodes NaN. */
+double oracle_e8m0_value(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* UE8M0 scale byte of a group with absolute maximum amax: the smallest e with 448 * 2^e >= amax,
+ * e = 0 when amax is 0, as b = e + 127 clamped to 0..254. */
+uint8_t oracle_ue8m0_scale(float amax) {
+  if (!(amax > 0.0f)) return 127;
+  int e = (int)ceil(log2((double)amax / 448.0));
+  while (ldexp(448.0, e) < (double)amax) ++e;
+  while (ldexp(448.0, e - 1) >= (double)amax) --e;
+  int b = e + 127;
+  if (b < 0) b = 0;
+  if (b > 254) b = 254;
+  return (uint8_t)b;
+}
+
+/* Quantise one group with a UE8M0 scale: b = oracle_ue8m0_scale(amax), q_i = E4M3(v_i * 2^-e). */
+static void quantize_group_ue8m0(const float* v, int n, size_t stride, uint8_t* q, size_t qstride,
+                                 uint8_t* b_out) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = fabsf(v[(size_t)i * stride]);
+    if (a > amax) amax = a;
+  }
+  uint8_t b = oracle_ue8m0_scale(amax);
+  float inv = ldexpf(1.0f, 127 - (int)b);
+  for (int i = 0; i < n; ++i) q[(size_t)i * qstride] = oracle_e4m3_encode(v[(size_t)i * stride] * inv);
+  *b_out = b;
+}
+
 /* Quantise one group of n fp32 values: s = amax/448 (fp32), q_i = E4M3(v_i / s). */
 static void quantize_group(const float* v, int n, size_t stride, uint8_t* q, size_t qstride,
                            float* s_out) {
@@ -130,6 +165,21 @@ void oracle_quantize_act(const void* x, int x_dtype, int M, int K, int group, ui
     for (int g = 0; g < G; ++g)
       quantize_group(row + (size_t)g * group, group, 1, q + (size_t)m * K + (size_t)g * group, 1,
                      s + (size_t)m * G + g);
+    free(row);
+  }
+}
+
+/* The same with UE8M0 scales: s [M, K/group] e8m0 bytes. */
+void oracle_quantize_act_ue8m0(const void* x, int x_dtype, int M, int K, int group, uint8_t* q,
+                               uint8_t* s) {
+  int G = K / group;
+#pragma omp parallel for schedule(static)
+  for (int m = 0; m < M; ++m) {
+    float* row = (float*)malloc(sizeof(float) * (size_t)K);
+    for (int i = 0; i < K; ++i) row[i] = (float)load_value(x, x_dtype, (size_t)m * K + i);
+    for (int g = 0; g < G; ++g)
+      quantize_group_ue8m0(row + (size_t)g * group, group, 1, q + (size_t)m * K + (size_t)g * group,
+                           1, s + (size_t)m * G + g);
     free(row);
   }
 }
@@ -222,6 +272,30 @@ void oracle_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, in
   for (int q = 0; q < P; ++q) pair_pos[sorted_pair[q]] = q;
 }
 
+/* The same with UE8M0 scales: s [N/block, K/block] e8m0 bytes. */
+void oracle_quantize_weight_ue8m0(const float* W, int N, int K, int block, uint8_t* q, uint8_t* s) {
+  int NB = N / block, KB = K / block;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int nb = 0; nb < NB; ++nb) {
+    for (int kb = 0; kb < KB; ++kb) {
+      float amax = 0.0f;
+      for (int r = 0; r < block; ++r)
+        for (int c = 0; c < block; ++c) {
+          float a = fabsf(W[(size_t)(nb * block + r) * K + (size_t)kb * block + c]);
+          if (a > amax) amax = a;
+        }
+      uint8_t b = oracle_ue8m0_scale(amax);
+      float inv = ldexpf(1.0f, 127 - (int)b);
+      for (int r = 0; r < block; ++r)
+        for (int c = 0; c < block; ++c) {
+          size_t i = (size_t)(nb * block + r) * K + (size_t)kb * block + c;
+          q[i] = oracle_e4m3_encode(W[i] * inv);
+        }
+      s[(size_t)nb * KB + kb] = b;
+    }
+  }
+}
+
 /* ---------------------------------------------------------------------------------------------
  * Experts (gated MLP with SwiGLU) and the weighted combine (p1 intro; p4 section 5)
  * ------------------------------------------------------------------------------------------- */
@@ -230,31 +304,44 @@ typedef struct {
   int d, f;
   int w_dtype;                       /* ORACLE_F32 / ORACLE_BF16 / ORACLE_E4M3 */
   const void *w_gate, *w_up, *w_down; /* [E,f,d], [E,f,d], [E,d,f] */
-  const float *s_gate, *s_up, *s_down; /* e4m3 only: [E,f/128,d/128], [E,d/128,f/128] */
+  const void *s_gate, *s_up, *s_down; /* e4m3 only: [E,f/128,d/128], [E,d/128,f/128] */
   int quant_act;                     /* 1: activations (x and h) follow the fp8 group rule */
+  int scale_fmt;                     /* 0: fp32 scales; 1: UE8M0 bytes (weights and activations) */
 } oracle_experts;
 
+static double scale_value(const void* s, int scale_fmt, size_t i) {
+  return scale_fmt ? oracle_e8m0_value(((const uint8_t*)s)[i]) : (double)((const float*)s)[i];
+}
+
 /* Dequantised weight element W[e][r][c] of an [E, R, C] tensor. */
-static double weight_value(const void* w, const float* s, int dtype, int e, int r, int c, int R,
-                           int C) {
+static double weight_value(const void* w, const void* s, int scale_fmt, int dtype, int e, int r,
+                           int c, int R, int C) {
   size_t i = ((size_t)e * R + r) * C + c;
   double v = load_value(w, dtype, i);
   if (dtype == ORACLE_E4M3) {
     int CB = C / 128;
-    v *= (double)s[((size_t)e * (R / 128) + r / 128) * CB + c / 128];
+    v *= scale_value(s, scale_fmt, ((size_t)e * (R / 128) + r / 128) * CB + c / 128);
   }
   return v;
 }
 
 /* Apply the activation rule to one fp32 row of length n (in place on the dequantised value). */
-static void fake_quant_row(double* v, int n) {
+static void fake_quant_row(double* v, int n, int scale_fmt) {
   float* tmp = (float*)malloc(sizeof(float) * (size_t)n);
   uint8_t* q = (uint8_t*)malloc((size_t)n);
   for (int i = 0; i < n; ++i) tmp[i] = (float)v[i];
   for (int g = 0; g < n / 128; ++g) {
-    float s;
-    quantize_group(tmp + g * 128, 128, 1, q + g * 128, 1, &s);
-    for (int i = 0; i < 128; ++i) v[g * 128 + i] = oracle_e4m3_value(q[g * 128 + i]) * (double)s;
+    double s;
+    if (scale_fmt) {
+      uint8_t b;
+      quantize_group_ue8m0(tmp + g * 128, 128, 1, q + g * 128, 1, &b);
+      s = oracle_e8m0_value(b);
+    } else {
+      float sf;
+      quantize_group(tmp + g * 128, 128, 1, q + g * 128, 1, &sf);
+      s = (double)sf;
+    }
+    for (int i = 0; i < 128; ++i) v[g * 128 + i] = oracle_e4m3_value(q[g * 128 + i]) * s;
   }
   free(tmp);
   free(q);
@@ -270,41 +357,44 @@ static void expert_row(const oracle_experts* X, int e, const double* xr, double*
   for (int n = 0; n < f; ++n) {
     double g = 0.0, u = 0.0;
     for (int i = 0; i < d; ++i) {
-      g += xr[i] * weight_value(X->w_gate, X->s_gate, X->w_dtype, e, n, i, f, d);
-      u += xr[i] * weight_value(X->w_up, X->s_up, X->w_dtype, e, n, i, f, d);
+      g += xr[i] * weight_value(X->w_gate, X->s_gate, X->scale_fmt, X->w_dtype, e, n, i, f, d);
+      u += xr[i] * weight_value(X->w_up, X->s_up, X->scale_fmt, X->w_dtype, e, n, i, f, d);
     }
     h[n] = g / (1.0 + exp(-g)) * u;
   }
   if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)f);
-  if (X->quant_act) fake_quant_row(h, f);
+  if (X->quant_act) fake_quant_row(h, f, X->scale_fmt);
   if (y_out)
     for (int o = 0; o < d; ++o) {
       double acc = 0.0;
       for (int n = 0; n < f; ++n)
-        acc += h[n] * weight_value(X->w_down, X->s_down, X->w_dtype, e, o, n, d, f);
+        acc += h[n] * weight_value(X->w_down, X->s_down, X->scale_fmt, X->w_dtype, e, o, n, d, f);
       y_out[o] = acc;
     }
   free(h);
 }
 
 /* The input row of token t as the experts see it (dequantised if quant_act). */
-static void input_row(const void* x, int x_dtype, int d, int t, int quant_act, double* xr) {
+static void input_row(const void* x, int x_dtype, int d, int t, int quant_act, int scale_fmt,
+                      double* xr) {
   for (int i = 0; i < d; ++i) xr[i] = load_value(x, x_dtype, (size_t)t * d + i);
-  if (quant_act) fake_quant_row(xr, d);
+  if (quant_act) fake_quant_row(xr, d, scale_fmt);
 }
 
 /* Per-pair expert outputs (for checking the two projections separately).
  * For each listed pair (token tok[n], expert exp_of[n]): h[n][0..f) (before any h quantisation)
  * and y[n][0..d) (unweighted expert output). Either output may be NULL. */
 void oracle_expert_pairs(int d, int f, int x_dtype, const void* x, int w_dtype, const void* w_gate,
-                         const void* w_up, const void* w_down, const float* s_gate,
-                         const float* s_up, const float* s_down, int quant_act, int n_pairs,
-                         const int32_t* tok, const int32_t* exp_of, double* h, double* y) {
-  oracle_experts X = {d, f, w_dtype, w_gate, w_up, w_down, s_gate, s_up, s_down, quant_act};
+                         const void* w_up, const void* w_down, const void* s_gate,
+                         const void* s_up, const void* s_down, int quant_act, int scale_fmt,
+                         int n_pairs, const int32_t* tok, const int32_t* exp_of, double* h,
+                         double* y) {
+  oracle_experts X = {d, f, w_dtype, w_gate, w_up, w_down, s_gate, s_up, s_down, quant_act,
+                      scale_fmt};
 #pragma omp parallel for schedule(dynamic, 1)
   for (int n = 0; n < n_pairs; ++n) {
     double* xr = (double*)malloc(sizeof(double) * (size_t)d);
-    input_row(x, x_dtype, d, tok[n], quant_act, xr);
+    input_row(x, x_dtype, d, tok[n], quant_act, scale_fmt, xr);
     expert_row(&X, exp_of[n], xr, h ? h + (size_t)n * f : NULL, y ? y + (size_t)n * d : NULL);
     free(xr);
   }
@@ -316,10 +406,11 @@ void oracle_expert_pairs(int d, int f, int x_dtype, const void* x, int w_dtype, 
  * out is [n_tok, d] in the order of tok_list. */
 void oracle_moe_forward(int T, int d, int f, int k, int x_dtype, const void* x, int w_dtype,
                         const void* w_gate, const void* w_up, const void* w_down,
-                        const float* s_gate, const float* s_up, const float* s_down, int quant_act,
-                        const int32_t* ids, const float* topk_w, int n_tok,
+                        const void* s_gate, const void* s_up, const void* s_down, int quant_act,
+                        int scale_fmt, const int32_t* ids, const float* topk_w, int n_tok,
                         const int32_t* tok_list, double* out) {
-  oracle_experts X = {d, f, w_dtype, w_gate, w_up, w_down, s_gate, s_up, s_down, quant_act};
+  oracle_experts X = {d, f, w_dtype, w_gate, w_up, w_down, s_gate, s_up, s_down, quant_act,
+                      scale_fmt};
   if (!tok_list) n_tok = T;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int n = 0; n < n_tok; ++n) {
@@ -328,7 +419,7 @@ void oracle_moe_forward(int T, int d, int f, int k, int x_dtype, const void* x, 
     double* y = (double*)malloc(sizeof(double) * (size_t)d);
     double* o = out + (size_t)n * d;
     for (int i = 0; i < d; ++i) o[i] = 0.0;
-    input_row(x, x_dtype, d, t, quant_act, xr);
+    input_row(x, x_dtype, d, t, quant_act, scale_fmt, xr);
     for (int j = 0; j < k; ++j) {
       expert_row(&X, ids[(size_t)t * k + j], xr, NULL, y);
       double wj = (double)topk_w[(size_t)t * k + j];

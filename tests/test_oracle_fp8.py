@@ -177,3 +177,133 @@ def test_fp8_layer_quantises_h():
     y = np.einsum("pn,pon->po", hdq, Wd_deq[ids.reshape(-1)])
     ref = (y.reshape(6, 2, -1) * w[:, :, None].astype(np.float64)).sum(1)
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+# ---- UE8M0 scale format ----------------------------------------------------------------------
+# Transformers "Fine-grained FP8" page, section "UE8M0 scale format": block scales stored as
+# float8_e8m0fnu bytes (powers of two). The choice of the power (the smallest 2^e with
+# 448 * 2^e >= amax, for weight blocks and activation groups alike) is this project's reading.
+
+
+def test_e8m0_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = oracle.e8m0_decode_array(codes)
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    np.testing.assert_array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[0] == 2.0 ** -127 and got[254] == 2.0 ** 127
+
+
+def test_ue8m0_scale_is_smallest_covering_power_of_two():
+    # exact rational check of 448 * s >= amax > 448 * s / 2, on random magnitudes, on the exact
+    # boundaries 448 * 2^e and on their fp32 neighbours
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    amaxes = list(rng.lognormal(0.0, 8.0, 2000).astype(np.float32))
+    for e in range(-30, 30):
+        b = np.float32(448.0 * 2.0 ** e)
+        amaxes += [b, np.nextafter(b, np.float32(np.inf)), np.nextafter(b, np.float32(0))]
+    for a in amaxes:
+        b = oracle.ue8m0_scale(np.float32(a))
+        s = Fraction(2) ** (b - 127)
+        A = Fraction(float(a))
+        assert 448 * s >= A and 448 * s / 2 < A, (float(a), b)
+    assert oracle.ue8m0_scale(np.float32(0.0)) == 127
+    assert oracle.ue8m0_scale(np.float32(448.0)) == 127
+    assert oracle.ue8m0_scale(np.float32(448.00003)) == 128
+    assert oracle.ue8m0_scale(np.float32(224.0)) == 126
+
+
+def test_quantize_act_ue8m0_closed_forms():
+    # amax 448 * 2^-7: the scale is exactly 2^-7 (byte 120), codes equal the plain e4m3 encoding
+    # of 128 v and values on the e4m3 grid times 2^-7 come back exactly.
+    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)], np.float64)
+    rng = np.random.default_rng(23)
+    vals = rng.choice(grid[grid <= 448], size=(4, 256)) * rng.choice([-1, 1], size=(4, 256))
+    vals[:, 0] = 448.0
+    vals[:, 128] = -448.0
+    x = (vals * 2.0 ** -7).astype(np.float32)
+    q, s = oracle.quantize_act(x, scale_fmt="ue8m0")
+    assert s.dtype == np.uint8 and np.all(s == 120)
+    np.testing.assert_array_equal(oracle.e4m3_decode_array(q) * 2.0 ** -7, x)
+    # an amax just above 448 * 2^-7 moves to the next power: scale 2^-6, the amax maps to 224
+    x2 = x.copy()
+    x2[:, 0] = np.nextafter(np.float32(3.5), np.float32(4))
+    q2, s2 = oracle.quantize_act(x2, scale_fmt="ue8m0")
+    assert np.all(s2[:, 0] == 121) and np.all(s2[:, 1] == 120)
+    assert np.all(oracle.e4m3_decode_array(q2[:, 0]) == 224.0)
+    # an all-zero group: byte 127 (scale 1) and zero codes
+    qz, sz = oracle.quantize_act(np.zeros((2, 128), np.float32), scale_fmt="ue8m0")
+    assert np.all(sz == 127) and np.all(qz == 0)
+
+
+def test_quantize_act_ue8m0_error_bound_and_torch_codes():
+    x = synth.normal_bf16(5010, (64, 512))
+    q, s = oracle.quantize_act(x, scale_fmt="ue8m0")
+    xf = synth.bf16_bits_to_f32(x)
+    sv = oracle.e8m0_decode_array(s).repeat(128, 1)
+    # codes: torch's fp32 -> e4m3fn cast of the exactly scaled values (no value exceeds 448)
+    scaled = (xf.astype(np.float64) / sv).astype(np.float32)
+    assert np.abs(scaled).max() <= 448
+    ref = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(q, ref)
+    # error: <= 2^-4 relative in the normal range, half a subnormal step times s below it
+    deq = oracle.e4m3_decode_array(q) * sv
+    err = np.abs(deq - xf)
+    bound = np.maximum(np.abs(xf) * 2.0 ** -4, 2.0 ** -10 * sv)
+    assert np.all(err <= bound * (1 + 1e-6))
+    # every group's scaled amax lies in (224, 448] (its code may round down to 224)
+    smax = np.abs(scaled).reshape(64, 4, 128).max(-1)
+    assert np.all((smax > 224) & (smax <= 448))
+    top = np.abs(oracle.e4m3_decode_array(q).reshape(64, 4, 128)).max(-1)
+    assert np.all((top >= 224) & (top <= 448))
+
+
+def test_quantize_weight_ue8m0_blocks():
+    W = synth.normal_f32(5011, (256, 384), 1 / 16)
+    q, s = oracle.quantize_weight(W, scale_fmt="ue8m0")
+    assert q.shape == (256, 384) and s.shape == (2, 3) and s.dtype == np.uint8
+    from fractions import Fraction
+    for nb in range(2):
+        for kb in range(3):
+            blk = W[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128]
+            A = Fraction(float(np.abs(blk).max()))
+            sc = Fraction(2) ** (int(s[nb, kb]) - 127)
+            assert 448 * sc >= A > 224 * sc
+            scaled = (blk.astype(np.float64) / float(sc)).astype(np.float32)
+            ref = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8)
+            np.testing.assert_array_equal(
+                q[nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128], ref.numpy())
+
+
+def test_fp8_ue8m0_layer_vs_numpy():
+    # The layer with UE8M0 scales against a numpy evaluation: scale bytes decoded as 2^(b-127)
+    # (the pinned decode), x and h quantised by the pinned UE8M0 group rule, fp64 matmuls.
+    spec = synth.DSV3_FP8.with_(T=6, d=256, f=256, E=4, k=2)
+    x = synth.gen_x(spec)
+    Wg, Wu, Wd = (synth.gen_expert_weight(spec, n) for n in ("gate", "up", "down"))
+    (qg, sg), (qu, su), (qd, sd) = (oracle.quantize_weight(a, scale_fmt="ue8m0")
+                                    for a in (Wg, Wu, Wd))
+    ex = oracle.Experts(qg, qu, qd, sg, su, sd, quant_act=True, scale_fmt="ue8m0")
+    ids, w = oracle.route(synth.gen_logits(spec), 2)
+    out = oracle.moe_forward(x, ex, ids, w)
+
+    def deq_w(q, s):
+        return oracle.e4m3_decode_array(q) * np.repeat(np.repeat(oracle.e8m0_decode_array(s), 128,
+                                                                 -2), 128, -1)
+
+    def fq(v):
+        qq, ss = oracle.quantize_act(v.astype(np.float32), scale_fmt="ue8m0")
+        return oracle.e4m3_decode_array(qq) * oracle.e8m0_decode_array(ss).repeat(128, 1)
+
+    xq = fq(synth.bf16_bits_to_f32(x))
+    G, U, D = deq_w(qg, sg), deq_w(qu, su), deq_w(qd, sd)
+    ref = np.zeros((6, 256))
+    for t in range(6):
+        for j in range(2):
+            e = ids[t, j]
+            g = G[e] @ xq[t]
+            u = U[e] @ xq[t]
+            h = fq((g / (1 + np.exp(-g)) * u)[None, :])[0]
+            ref[t] += float(w[t, j]) * (D[e] @ h)
+    np.testing.assert_allclose(out, ref, rtol=1e-9, atol=1e-11 * np.abs(ref).max())
