@@ -56,6 +56,13 @@ typedef enum {
   MOE_FP8_E4M3 = 2   /* OCP E4M3FN: bias 7, max 448, no infinities */
 } moe_dtype;
 
+/* Format of fp8 block scales (Transformers "Fine-grained FP8" page, section "UE8M0 scale
+ * format": checkpoints that store weight scales as packed float8_e8m0fnu instead of float32). */
+typedef enum {
+  MOE_SCALE_F32 = 0,   /* one fp32 value per block */
+  MOE_SCALE_UE8M0 = 1  /* one byte b per block, value 2^(b - 127) (255 = NaN, never produced) */
+} moe_scale_fmt;
+
 /* Layout of the expert outputs that moe_experts_forward writes and moe_combine reads. */
 typedef enum {
   MOE_Y_PERMUTED = 0, /* y [P, d]: unweighted expert outputs, rows in sorted-pair order */
@@ -130,6 +137,19 @@ moe_status fp8_quantize_act(const void* x, moe_dtype x_dtype, int M, int K, int 
                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * fp8_quantize_act_ue8m0 - the same with UE8M0 scales (Transformers "Fine-grained FP8" page,
+ * section "UE8M0 scale format": power-of-two scales stored as e8m0 bytes).
+ *
+ *  Arguments as fp8_quantize_act; scales [M, K/group] uint8 e8m0 bytes out.
+ *  Per group: b is the byte of the smallest power of two 2^e with 448 * 2^e >= amax (b = 127 for
+ *  an all-zero group; b clamped to 0..254), q = e4m3(v * 2^-e), round-to-nearest-even (the
+ *  scaling is exact and no value exceeds 448). Errors as fp8_quantize_act.
+ * ------------------------------------------------------------------------------------------ */
+moe_status fp8_quantize_act_ue8m0(const void* x, moe_dtype x_dtype, int M, int K, int group,
+                                  const int32_t* row_index, uint8_t* q, uint8_t* scales,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * fp8_quantize_weight - offline 128x128 block quantisation of expert weights to e4m3.
  * (Transformers "Fine-grained FP8" page, introduction: weights are quantised to 8 bits per
  * two-dimensional block, weight_block_size = (128, 128).)
@@ -140,6 +160,16 @@ moe_status fp8_quantize_act(const void* x, moe_dtype x_dtype, int M, int K, int 
  * ------------------------------------------------------------------------------------------ */
 moe_status fp8_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
                                int block, uint8_t* q, float* scales, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * fp8_quantize_weight_ue8m0 - 128x128 block quantisation with UE8M0 scales (Transformers
+ * "Fine-grained FP8" page, section "UE8M0 scale format").
+ *
+ *  Arguments as fp8_quantize_weight; scales [batch, N/128, K/128] uint8 e8m0 bytes out, chosen
+ *  by the fp8_quantize_act_ue8m0 rule with the block's absmax. Errors as fp8_quantize_weight.
+ * ------------------------------------------------------------------------------------------ */
+moe_status fp8_quantize_weight_ue8m0(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                                     int block, uint8_t* q, uint8_t* scales, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * moe_experts_forward - both grouped projections of every selected expert.
@@ -160,6 +190,11 @@ moe_status fp8_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int 
  *        x = e4m3 codes [T, d] with x_scales [T, d/128] (from fp8_quantize_act); weights e4m3
  *        with block scales; fp32 accumulation with per-128-K scale promotion; h is re-quantised
  *        per pair per 128 channels. d % 128 == f % 128 == 0.
+ *        With scale_fmt = MOE_SCALE_UE8M0 every scale (x_scales from fp8_quantize_act_ue8m0,
+ *        s_gate / s_up / s_down from fp8_quantize_weight_ue8m0) is an e8m0 byte; the matrix unit
+ *        applies them as its per-row / per-column block scales (no promotion step) and h is
+ *        re-quantised with UE8M0 scales. scale_fmt other than MOE_SCALE_F32 on a non-fp8 path,
+ *        or an unknown value, is MOE_ERR_INVALID_ARGUMENT.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int T, d, f, E, k;
@@ -168,13 +203,13 @@ typedef struct {
   moe_dtype y_dtype;             /* element type of y for MOE_Y_PERMUTED / MOE_Y_SLOTS */
   moe_y_layout y_layout;
   const void* x;                 /* [T, d] token activations */
-  const float* x_scales;         /* FP8: [T, d/128] */
+  const void* x_scales;          /* FP8: [T, d/128], fp32 or e8m0 bytes (scale_fmt) */
   const void* w_gate;            /* [E, f, d] */
   const void* w_up;              /* [E, f, d] */
   const void* w_down;            /* [E, d, f] */
-  const float* s_gate;           /* FP8: [E, f/128, d/128] */
-  const float* s_up;             /* FP8: [E, f/128, d/128] */
-  const float* s_down;           /* FP8: [E, d/128, f/128] */
+  const void* s_gate;            /* FP8: [E, f/128, d/128], fp32 or e8m0 bytes (scale_fmt) */
+  const void* s_up;              /* FP8: [E, f/128, d/128] */
+  const void* s_down;            /* FP8: [E, d/128, f/128] */
   const int32_t* offsets;        /* [E+1] from moe_permute */
   const int32_t* sorted_pair;    /* [P] from moe_permute */
   const float* topk_w;           /* [T, k] routing weights (MOE_Y_SLOTS, MOE_Y_ACC_F32) */
@@ -183,6 +218,7 @@ typedef struct {
   size_t workspace_bytes;
   void** events;                 /* nullable: 4 hipEvent_t recorded on `stream` before/after the
                                     gate/up GEMM and before/after the down GEMM (for timing) */
+  moe_scale_fmt scale_fmt;       /* FP8 block-scale format (MOE_SCALE_F32 elsewhere) */
 } moe_experts_args;
 
 moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream);

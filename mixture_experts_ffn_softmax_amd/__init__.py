@@ -29,7 +29,8 @@ _LAYOUTS = {"permuted": MOE_Y_PERMUTED, "slots": MOE_Y_SLOTS, "acc_f32": MOE_Y_A
 # Every symbol include/moe.h declares.
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_route", "moe_permute", "moe_permute_workspace_size",
-    "fp8_quantize_act", "fp8_quantize_weight", "moe_experts_forward",
+    "fp8_quantize_act", "fp8_quantize_weight", "fp8_quantize_act_ue8m0",
+    "fp8_quantize_weight_ue8m0", "moe_experts_forward",
     "moe_experts_workspace_size", "moe_combine", "moe_event_create", "moe_event_destroy",
     "moe_event_record", "moe_event_elapsed_ms",
 )
@@ -52,7 +53,12 @@ class moe_experts_args(ctypes.Structure):
         ("topk_w", ctypes.c_void_p), ("y", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("events", ctypes.c_void_p),
+        ("scale_fmt", ctypes.c_int),
     ]
+
+
+_SCALE_FMTS = {"f32": 0, "ue8m0": 1}   # moe_scale_fmt
+MOE_SCALE_F32, MOE_SCALE_UE8M0 = 0, 1
 
 
 _lib = None
@@ -77,6 +83,8 @@ def load_library(path: str = LIB_PATH):
         "moe_permute_workspace_size": ([i32, i32, i32], sz),
         "fp8_quantize_act": ([vp, i32, i32, i32, i32, vp, vp, vp, vp], st),
         "fp8_quantize_weight": ([vp, i32, i32, i32, i32, i32, vp, vp, vp], st),
+        "fp8_quantize_act_ue8m0": ([vp, i32, i32, i32, i32, vp, vp, vp, vp], st),
+        "fp8_quantize_weight_ue8m0": ([vp, i32, i32, i32, i32, i32, vp, vp, vp], st),
         "moe_experts_forward": ([ctypes.POINTER(moe_experts_args), vp], st),
         "moe_experts_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "moe_combine": ([vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp], st),
@@ -199,31 +207,36 @@ def moe_permute(topk_ids: torch.Tensor, E: int, x=None, x_scales=None, workspace
     return Permutation(counts, offsets, sp, pp, x_perm, xps)
 
 
-def fp8_quantize_act(x: torch.Tensor, group: int = 128, row_index=None):
-    """Per-row, per-128-channel dynamic e4m3 quantisation. Returns (q uint8 [M,K], scales fp32)."""
+def fp8_quantize_act(x: torch.Tensor, group: int = 128, row_index=None, scale_fmt: str = "f32"):
+    """Per-row, per-128-channel dynamic e4m3 quantisation. Returns (q uint8 [M,K], scales):
+    fp32 scales, or e8m0 bytes (uint8) for scale_fmt="ue8m0"."""
     lib = load_library()
     _contig(x)
     M = row_index.numel() if row_index is not None else x.shape[0]
     K = x.shape[1]
+    ue = _SCALE_FMTS[scale_fmt] == 1
     q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
-    s = torch.empty((M, max(K // group, 1)), dtype=torch.float32, device=x.device)
-    _check(lib.fp8_quantize_act(_ptr(x), _dtype_code(x), M, K, group, _ptr(row_index), _ptr(q),
-                                _ptr(s), _stream()))
+    s = torch.empty((M, max(K // group, 1)), dtype=torch.uint8 if ue else torch.float32,
+                    device=x.device)
+    fn = lib.fp8_quantize_act_ue8m0 if ue else lib.fp8_quantize_act
+    _check(fn(_ptr(x), _dtype_code(x), M, K, group, _ptr(row_index), _ptr(q), _ptr(s), _stream()))
     return q, s
 
 
-def fp8_quantize_weight(w: torch.Tensor, block: int = 128):
-    """128x128 block e4m3 quantisation of [batch, N, K] (or [N, K]) weights."""
+def fp8_quantize_weight(w: torch.Tensor, block: int = 128, scale_fmt: str = "f32"):
+    """128x128 block e4m3 quantisation of [batch, N, K] (or [N, K]) weights; scales fp32, or
+    e8m0 bytes for scale_fmt="ue8m0"."""
     lib = load_library()
     _contig(w)
     shape = w.shape
     batch = 1 if w.dim() == 2 else int(torch.tensor(shape[:-2]).prod())
     N, K = shape[-2], shape[-1]
+    ue = _SCALE_FMTS[scale_fmt] == 1
     q = torch.empty(shape, dtype=torch.uint8, device=w.device)
     s = torch.empty(tuple(shape[:-2]) + (max(N // block, 1), max(K // block, 1)),
-                    dtype=torch.float32, device=w.device)
-    _check(lib.fp8_quantize_weight(_ptr(w), _dtype_code(w), batch, N, K, block, _ptr(q), _ptr(s),
-                                   _stream()))
+                    dtype=torch.uint8 if ue else torch.float32, device=w.device)
+    fn = lib.fp8_quantize_weight_ue8m0 if ue else lib.fp8_quantize_weight
+    _check(fn(_ptr(w), _dtype_code(w), batch, N, K, block, _ptr(q), _ptr(s), _stream()))
     return q, s
 
 
@@ -233,9 +246,11 @@ def experts_workspace_bytes(T, d, f, E, k, act_dtype: int, w_dtype: int) -> int:
 
 def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k: int,
                         y_layout: str = "slots", y_dtype=None, x_scales=None, s_gate=None,
-                        s_up=None, s_down=None, y=None, workspace=None, events=None):
+                        s_up=None, s_down=None, y=None, workspace=None, events=None,
+                        scale_fmt: str = "f32"):
     """Both grouped projections. Returns y in ``y_layout`` ("permuted" [P,d], "slots" [T,k,d],
-    "acc_f32" [T,d] fp32). ``events``: optional 4 event handles (see moe_event_create)."""
+    "acc_f32" [T,d] fp32). ``events``: optional 4 event handles (see moe_event_create).
+    ``scale_fmt``: fp8 block scales as fp32 values ("f32") or e8m0 bytes ("ue8m0")."""
     lib = load_library()
     for t in (x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, x_scales, s_gate, s_up,
               s_down):
@@ -268,7 +283,8 @@ def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k
                          offsets.data_ptr(), sorted_pair.data_ptr(),
                          topk_w.data_ptr() if topk_w is not None else None, y.data_ptr(),
                          workspace.data_ptr(), workspace.numel(),
-                         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
+                         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
+                         _SCALE_FMTS[scale_fmt])
     _check(lib.moe_experts_forward(ctypes.byref(a), _stream()))
     return y
 
@@ -323,7 +339,7 @@ def moe_layer(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, y_lay
     """route -> permute -> (fp8: quantise x) -> experts -> combine, all on the device.
 
     For fp8 weights (uint8 e4m3 codes with block scales s_*), x is given in bf16/fp32 and quantised
-    per token per 128 channels here.
+    per token per 128 channels here; uint8 scales select the UE8M0 scale format.
     """
     E = w_gate.shape[0]
     T, d = x.shape
@@ -333,12 +349,14 @@ def moe_layer(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, y_lay
     if out_dtype is None:
         out_dtype = torch.float32 if x.dtype == torch.float32 else torch.bfloat16
     x_in, xs = x, None
+    fmt = "ue8m0" if s_gate is not None and s_gate.dtype == torch.uint8 else "f32"
     if w_gate.dtype in (torch.uint8, torch.float8_e4m3fn):
-        x_in, xs = fp8_quantize_act(x)
+        x_in, xs = fp8_quantize_act(x, scale_fmt=fmt)
     y = moe_experts_forward(x_in, w_gate, w_up, w_down, perm.offsets, perm.sorted_pair, w, k,
                             y_layout=y_layout, x_scales=xs, s_gate=s_gate, s_up=s_up,
                             s_down=s_down, events=events,
-                            y_dtype=torch.float32 if out_dtype == torch.float32 else None)
+                            y_dtype=torch.float32 if out_dtype == torch.float32 else None,
+                            scale_fmt=fmt)
     out = moe_combine(y, y_layout, T, k, d, pair_pos=perm.pair_pos, topk_w=w,
                       out_dtype=out_dtype)
     return LayerResult(out, ids, w, lg, perm)

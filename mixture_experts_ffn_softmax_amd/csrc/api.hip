@@ -47,7 +47,7 @@ inline bool uses_split(moe_dtype act, moe_dtype w, long long P, int d, int f) {
 }
 
 struct ExpertsLayout {
-  size_t cum_a, cum_b, h, h_scales, split_partial, total;
+  size_t cum_a, cum_b, h, h_scales, x_scales, split_partial, total;
 };
 
 ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, moe_dtype w) {
@@ -63,6 +63,9 @@ ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, m
   off = align_up(off + P * f * h_elem);
   L.h_scales = off;
   if (w == MOE_FP8_E4M3) off = align_up(off + P * (f / kFp8Group) * sizeof(float));
+  // fp8 with UE8M0 scales: x_scales expanded from e8m0 bytes to fp32 values
+  L.x_scales = off;
+  if (w == MOE_FP8_E4M3) off = align_up(off + static_cast<size_t>(T) * (d / kFp8Group) * sizeof(float));
   L.split_partial = 0;
   if (uses_split(act, w, static_cast<long long>(P), d, f)) {
     L.split_partial = off;
@@ -184,7 +187,17 @@ moe_status fp8_quantize_act(const void* x, moe_dtype x_dtype, int M, int K, int 
   if (!is_float_type(x_dtype)) return MOE_ERR_INVALID_ARGUMENT;
   if (group != kFp8Group || K % kFp8Group) return MOE_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(q, 8)) return MOE_ERR_UNSUPPORTED;
-  return dev(launch_quantize_act(x, x_dtype, M, K, row_index, q, scales, stream));
+  return dev(launch_quantize_act(x, x_dtype, M, K, row_index, q, scales, false, stream));
+}
+
+moe_status fp8_quantize_act_ue8m0(const void* x, moe_dtype x_dtype, int M, int K, int group,
+                                  const int32_t* row_index, uint8_t* q, uint8_t* scales,
+                                  hipStream_t stream) {
+  if (!x || !q || !scales || M < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!is_float_type(x_dtype)) return MOE_ERR_INVALID_ARGUMENT;
+  if (group != kFp8Group || K % kFp8Group) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 8)) return MOE_ERR_UNSUPPORTED;
+  return dev(launch_quantize_act(x, x_dtype, M, K, row_index, q, scales, true, stream));
 }
 
 moe_status fp8_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
@@ -195,7 +208,18 @@ moe_status fp8_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int 
   if (!aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
   if (static_cast<long long>(batch) * (N / kFp8Group) * (K / kFp8Group) > INT_MAX)
     return MOE_ERR_UNSUPPORTED;
-  return dev(launch_quantize_weight(w, w_dtype, batch, N, K, q, scales, stream));
+  return dev(launch_quantize_weight(w, w_dtype, batch, N, K, q, scales, false, stream));
+}
+
+moe_status fp8_quantize_weight_ue8m0(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                                     int block, uint8_t* q, uint8_t* scales, hipStream_t stream) {
+  if (!w || !q || !scales || batch < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!is_float_type(w_dtype)) return MOE_ERR_INVALID_ARGUMENT;
+  if (block != kFp8Group || N % kFp8Group || K % kFp8Group) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(q, 4)) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(batch) * (N / kFp8Group) * (K / kFp8Group) > INT_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  return dev(launch_quantize_weight(w, w_dtype, batch, N, K, q, scales, true, stream));
 }
 
 size_t moe_experts_workspace_size(int T, int d, int f, int E, int k, moe_dtype act_dtype,
@@ -222,6 +246,10 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   if (!f32 && !bf16 && !fp8) return MOE_ERR_UNSUPPORTED;
   if (f32 && a->y_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (bf16 && (a->d % 64 || a->f % 64)) return MOE_ERR_UNSUPPORTED;
+  if (a->scale_fmt != MOE_SCALE_F32 && a->scale_fmt != MOE_SCALE_UE8M0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const bool ue8m0 = a->scale_fmt == MOE_SCALE_UE8M0;
+  if (ue8m0 && !fp8) return MOE_ERR_INVALID_ARGUMENT;  // scales exist only on the fp8 path
   if (fp8) {
     if (a->d % kFp8Group || a->f % kFp8Group) return MOE_ERR_UNSUPPORTED;
     if (a->d > 32768 || a->f > 32768) return MOE_ERR_UNSUPPORTED;
@@ -245,7 +273,7 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   X.k = a->k;
   X.a = a->x;
   X.a_gather = 1;
-  X.a_scales = a->x_scales;
+  X.a_scales = static_cast<const float*>(a->x_scales);
   X.sorted_pair = a->sorted_pair;
   X.w_gate = a->w_gate;
   X.w_up = a->w_up;
@@ -253,6 +281,7 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   X.s_gate = a->s_gate;
   X.s_up = a->s_up;
   X.s_down = a->s_down;
+  X.scale_ue8m0 = ue8m0 ? 1 : 0;
   X.offsets = a->offsets;
   X.tile_cum_a = reinterpret_cast<int32_t*>(ws + L.cum_a);
   X.tile_cum_b = reinterpret_cast<int32_t*>(ws + L.cum_b);
@@ -285,6 +314,14 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
     hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 65536))),
                        dim3(256), 0, stream, static_cast<float*>(a->y), n);
     if ((e = hipGetLastError()) != hipSuccess) return MOE_ERR_DEVICE;
+  }
+  if (ue8m0) {
+    // the GEMMs read activation scales as fp32 values; e8m0 bytes expand exactly
+    float* xs = reinterpret_cast<float*>(ws + L.x_scales);
+    e = launch_e8m0_expand(static_cast<const uint8_t*>(a->x_scales),
+                           static_cast<size_t>(a->T) * (a->d / kFp8Group), xs, stream);
+    if (e != hipSuccess) return MOE_ERR_DEVICE;
+    X.a_scales = xs;
   }
   if (f32) e = launch_experts_f32(X, stream);
   else if (fp8) e = launch_experts_fp8(X, stream);

@@ -34,6 +34,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// UE8M0 scale byte b (value 2^(b - 127)) of a group with absolute maximum amax: the smallest e
+// with 448 * 2^e >= amax, e = 0 for amax = 0, clamped to 0..254. With amax = fr * 2^ex,
+// fr in [0.5, 1) (frexp, exact also for subnormals) and 448 = 0.875 * 2^9, the condition reads
+// 2^(e + 9 - ex) >= fr / 0.875, whose least solution is e = ex - 9, plus one when fr > 0.875.
+__device__ __forceinline__ int ue8m0_byte(float amax) {
+  if (!(amax > 0.0f)) return 127;
+  const int ex = __builtin_amdgcn_frexp_expf(amax);
+  const float fr = __builtin_amdgcn_frexp_mantf(amax);
+  const int e = ex - 9 + (fr > 0.875f ? 1 : 0);
+  return min(254, max(0, e + 127));
+}
+
 // OCP E4M3FN encode: round to nearest even, saturate to +-448 (0x7E / 0xFE); zero keeps its sign.
 // Normal range: round the fp32 mantissa from 23 to 3 bits with the add-half-minus-one-plus-lsb
 // trick, then rebias the exponent (fp32 bias 127 -> e4m3 bias 7). Below 2^-6 the e4m3 grid is the

@@ -6,6 +6,10 @@
 //     y[r][n] = sum_kb  sa[r][kb] * sw[n/128][kb] * sum_{k in kb} qa[r][k] * qw[n][k].
 // One v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales) computes exactly the inner sum of one
 // 16x16 block for one kb; its fp32 result is scaled by sa * sw and added to the accumulator.
+// With UE8M0 scales (same page, "UE8M0 scale format": every scale a power of two, stored as an
+// e8m0 byte) the MFMA applies sa and sw itself as its per-row and per-column block scales and
+// accumulates across kb directly: no per-block promotion. Activation scales reach the kernel as
+// fp32 powers of two; the e8m0 byte of one is its exponent field.
 // The gate/up GEMM applies SwiGLU and re-quantises h per (pair, 128 channels) in its epilogue,
 // since h is the input of the down projection, a quantised linear too; the down GEMM writes y in
 // the requested layout (Transformers "Experts backends" page: gated MLP, weighted combine).
@@ -39,8 +43,8 @@ struct Fp8GemmArgs {
   int k;
   const uint8_t* b0;         // gate/up: W_gate [E, N, K]; down: W_down [E, N, K]
   const uint8_t* b1;         // gate/up: W_up
-  const float* s0;           // block scales of b0 [E, N/128, K/128]
-  const float* s1;           // block scales of b1
+  const void* s0;            // block scales of b0 [E, N/128, K/128]: fp32, or e8m0 bytes (UE8M0)
+  const void* s1;            // block scales of b1
   int K, N;
   const int32_t* offsets;
   const int32_t* tile_cum;
@@ -92,7 +96,7 @@ __device__ __forceinline__ i32x8_t ld32(const char* p0, const char* p1) {
   return r;
 }
 
-template <int MODE>
+template <int MODE, bool kUE>
 __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
   constexpr int MI = 4, NJ = 4;   // 16x16 blocks per wave
   const int NT = MODE == kGateUp ? p.N / 128 : (p.N + kBNf - 1) / kBNf;
@@ -154,17 +158,20 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
   // Weight scales of the tile for every K block, staged in LDS before the pipeline starts (the
   // main loop issues no vector memory instructions besides its DMA): gate/up -> block ntile of
   // s_gate and of s_up; down -> the two 128-column blocks of the 256-column tile.
-  __shared__ float wsc[2][kMaxKBlocks];
+  // fp32 scales are kept as their bit patterns, UE8M0 scales as the e8m0 byte.
+  __shared__ uint32_t wsc[2][kMaxKBlocks];
   for (int i = tid; i < 2 * KB; i += 512) {
     const int which = i >= KB, kb = i - which * KB;
     const size_t blk = MODE == kGateUp ? static_cast<size_t>(tc.ntile)
                                        : static_cast<size_t>(min(tc.ntile * 2 + which, p.N / 128 - 1));
-    const float* src = (MODE == kGateUp && which) ? p.s1 : p.s0;
-    wsc[which][kb] = src[(static_cast<size_t>(tc.e) * (p.N / 128) + blk) * KB + kb];
+    const void* src = (MODE == kGateUp && which) ? p.s1 : p.s0;
+    const size_t idx = (static_cast<size_t>(tc.e) * (p.N / 128) + blk) * KB + kb;
+    wsc[which][kb] = kUE ? static_cast<uint32_t>(static_cast<const uint8_t*>(src)[idx])
+                         : __float_as_uint(static_cast<const float*>(src)[idx]);
   }
   __syncthreads();
-  const float* sw0 = wsc[MODE == kGateUp ? 0 : (brow0 >> 7)];
-  const float* sw1 = wsc[MODE == kGateUp ? 1 : (brow0 >> 7)];
+  const uint32_t* sw0 = wsc[MODE == kGateUp ? 0 : (brow0 >> 7)];
+  const uint32_t* sw1 = wsc[MODE == kGateUp ? 1 : (brow0 >> 7)];
 
   f32x4_t acc[MI][NJ];
 #pragma unroll
@@ -186,27 +193,42 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
     wait_vmcnt<13>(); /* this wave's DMA of stage S is done (S+1's 13 may be pending) */     \
     __builtin_amdgcn_s_barrier();                                                             \
     dmaf(NXT2, d, (S) + 2, nst, wave, lane);                                                  \
-    const float w0 = sw0[S], w1 = sw1[S];                                                     \
     i32x8_t fa[MI], fb[NJ];                                                                   \
     f32x4_t sa[MI];                                                                           \
+    int ea[MI];                                                                               \
     _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                          \
       const int row = arow0 + i * 16 + lr;                                                    \
       fa[i] = ld32(CUR + swzf(row, 2 * lk), CUR + swzf(row, 2 * lk + 1));                     \
-      sa[i] = *reinterpret_cast<const f32x4_t*>(CUR + kAf + kBf +                             \
-                                                (arow0 + i * 16 + 4 * lk) * 4);               \
+      if constexpr (kUE) {                                                                    \
+        /* the e8m0 byte of the lane's row: exponent field of its power-of-two fp32 scale */  \
+        ea[i] = (*reinterpret_cast<const uint32_t*>(CUR + kAf + kBf + row * 4) >> 23) & 0xFF; \
+      } else {                                                                                \
+        sa[i] = *reinterpret_cast<const f32x4_t*>(CUR + kAf + kBf +                           \
+                                                  (arow0 + i * 16 + 4 * lk) * 4);             \
+      }                                                                                       \
     }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                          \
       const int row = MODE == kGateUp ? (j < 2 ? brow0 + j * 16 : 128 + brow0 + (j - 2) * 16) \
                                       : brow0 + j * 16;                                       \
       fb[j] = ld32(CUR + kAf + swzf(row + lr, 2 * lk), CUR + kAf + swzf(row + lr, 2 * lk + 1)); \
     }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                          \
-      const f32x4_t s0v = sa[i] * w0, s1v = sa[i] * w1;                                       \
-      _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                        \
-        const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                \
-            fa[i], fb[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);             \
-        const f32x4_t sc = (MODE == kGateUp && j >= 2) ? s1v : s0v;                           \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(part[q], sc[q], acc[i][j][q]); \
+    if constexpr (kUE) {                                                                      \
+      const int eb0 = static_cast<int>(sw0[S]), eb1 = static_cast<int>(sw1[S]);              \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                          \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                        \
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                       \
+              fa[i], fb[j], acc[i][j], 0, 0, 0, ea[i], 0,                                     \
+              (MODE == kGateUp && j >= 2) ? eb1 : eb0);                                       \
+    } else {                                                                                  \
+      const float w0 = __uint_as_float(sw0[S]), w1 = __uint_as_float(sw1[S]);                 \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                        \
+        const f32x4_t s0v = sa[i] * w0, s1v = sa[i] * w1;                                     \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                      \
+          const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(              \
+              fa[i], fb[j], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);           \
+          const f32x4_t sc = (MODE == kGateUp && j >= 2) ? s1v : s0v;                         \
+          _Pragma("unroll") for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(part[q], sc[q], acc[i][j][q]); \
+        }                                                                                     \
       }                                                                                       \
     }                                                                                         \
   }
@@ -249,7 +271,10 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
     }
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    // fp32 rule: s = amax / 448, codes of v / s; UE8M0: s = 2^e, codes of v * 2^-e (exact)
+    const int eb = ue8m0_byte(amax);
+    const float s = kUE ? ldexpf(1.0f, eb - 127) : (amax > 0.0f ? amax / 448.0f : 1.0f);
+    const float inv = ldexpf(1.0f, 127 - eb);
     if (row < tc.rows) {
       const size_t prow = static_cast<size_t>(tc.row0 + row);
       u32x4_t o[2];
@@ -257,7 +282,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
       for (int w = 0; w < 8; ++w) {
         uint32_t word = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) word |= e4m3_encode(v[w * 4 + b] / s) << (8 * b);
+        for (int b = 0; b < 4; ++b)
+          word |= e4m3_encode(kUE ? v[w * 4 + b] * inv : v[w * 4 + b] / s) << (8 * b);
         o[w >> 2][w & 3] = word;
       }
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(p.hq + prow * p.N + tc.ntile * 128 + part * 32);
@@ -358,8 +384,12 @@ hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream) {
   g.hq = static_cast<uint8_t*>(L.h);
   g.hs = L.h_scales;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipLaunchKernelGGL(gemm_fp8_kernel<kGateUp>, dim3(grid_for(P, L.E, L.f / 128)), dim3(512), 0,
-                     stream, g);
+  if (L.scale_ue8m0)
+    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true>), dim3(grid_for(P, L.E, L.f / 128)),
+                       dim3(512), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, false>), dim3(grid_for(P, L.E, L.f / 128)),
+                       dim3(512), 0, stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
@@ -383,8 +413,12 @@ hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream) {
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  hipLaunchKernelGGL(gemm_fp8_kernel<kDown>, dim3(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf)),
-                     dim3(512), 0, stream, dn);
+  if (L.scale_ue8m0)
+    hipLaunchKernelGGL((gemm_fp8_kernel<kDown, true>),
+                       dim3(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf)), dim3(512), 0, stream, dn);
+  else
+    hipLaunchKernelGGL((gemm_fp8_kernel<kDown, false>),
+                       dim3(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf)), dim3(512), 0, stream, dn);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return hipGetLastError();
 }

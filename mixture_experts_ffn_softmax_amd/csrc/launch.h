@@ -23,10 +23,12 @@ hipError_t launch_gather_rows(const void* x, size_t row_bytes, const int32_t* so
                               int k, void* x_perm, hipStream_t stream);
 
 hipError_t launch_quantize_act(const void* x, moe_dtype x_dtype, int M, int K,
-                               const int32_t* row_index, uint8_t* q, float* scales,
+                               const int32_t* row_index, uint8_t* q, void* scales, bool ue8m0,
                                hipStream_t stream);
 hipError_t launch_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
-                                  uint8_t* q, float* scales, hipStream_t stream);
+                                  uint8_t* q, void* scales, bool ue8m0, hipStream_t stream);
+// e8m0 bytes -> fp32 values 2^(b - 127)
+hipError_t launch_e8m0_expand(const uint8_t* b, size_t n, float* out, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
                           const int32_t* pair_pos, const float* topk_w, int T, int k, int d,
@@ -45,14 +47,16 @@ struct ExpertsLaunch {
   int T, d, f, E, k;
   const void* a;              // x [T, d] (a_gather = 1: row of pair = sorted_pair[pos] / k) or
   int a_gather;               // x_perm [P, d] in sorted order (a_gather = 0)
-  const float* a_scales;      // fp8: [T, d/128] (gather) or [P, d/128]
+  const float* a_scales;      // fp8: [T, d/128] (gather) or [P, d/128], fp32 values (powers of
+                              // two with UE8M0 weight scales)
   const int32_t* sorted_pair;
   const void* w_gate;
   const void* w_up;
   const void* w_down;
-  const float* s_gate;
-  const float* s_up;
-  const float* s_down;
+  const void* s_gate;         // fp8 block scales: fp32, or e8m0 bytes when scale_ue8m0
+  const void* s_up;
+  const void* s_down;
+  int scale_ue8m0;            // fp8: UE8M0 scales, applied by the block-scaled MFMA
   const int32_t* offsets;
   const int32_t* tile_cum_a;  // row tiles of the gate/up GEMM
   const int32_t* tile_cum_b;  // row tiles of the down GEMM
@@ -61,7 +65,7 @@ struct ExpertsLaunch {
   int y_bf16;
   void* y;
   void* h;                    // workspace: hidden activations [P, f]
-  float* h_scales;            // fp8: [P, f/128]
+  float* h_scales;            // fp8: [P, f/128] fp32 (powers of two when scale_ue8m0)
   int cpx;                    // CUs per XCD (<= kSplitSlots / 8)
   float* split_partial;       // bf16 GEMMs: [kSplitSlots][256 * 256] fp32, or null (no cutting;
                               // the two GEMMs use it one after the other)

@@ -1,7 +1,11 @@
 // Fine-grained FP8 quantisation (Transformers "Fine-grained FP8" page, introduction): activations
 // per token per 128 input channels with run-time scales, weights per 128x128 block.
 // Rule for one group/block: s = amax / 448 (fp32, IEEE division; s = 1 if all zero),
-// q = e4m3(v / s), round-to-nearest-even, saturating at +-448.
+// q = e4m3(v / s), round-to-nearest-even, saturating at +-448. With UE8M0 scales (same page,
+// "UE8M0 scale format": scales stored as float8_e8m0fnu bytes, powers of two): the byte b of the
+// smallest power of two 2^e with 448 * 2^e >= amax, q = e4m3(v * 2^-e) (an exact scaling).
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -29,11 +33,11 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
 }
 
 // One wave covers 4 groups of one row: 16 lanes per group, 8 consecutive elements per lane.
-template <typename XT>
+template <typename XT, bool kUe8m0>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const XT* __restrict__ x, int M, int K,
                                                            const int32_t* __restrict__ row_index,
                                                            uint8_t* __restrict__ q,
-                                                           float* __restrict__ scales) {
+                                                           void* __restrict__ scales) {
   const int G = K / kFp8Group;
   const int waves_per_row = (G + 3) / 4;
   const int wid = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -56,23 +60,34 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const XT* __restrict_
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (!active) return;
   uint32_t lo = 0, hi = 0;
+  if constexpr (kUe8m0) {
+    const int b = ue8m0_byte(amax);
+    const float inv = ldexpf(1.0f, 127 - b);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / s) << (8 * i);
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] * inv) << (8 * i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / s) << (8 * i);
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] * inv) << (8 * i);
+    if ((lane & 15) == 0)
+      static_cast<uint8_t*>(scales)[static_cast<size_t>(row) * G + g] = static_cast<uint8_t>(b);
+  } else {
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / s) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / s) << (8 * i);
+    if ((lane & 15) == 0) static_cast<float*>(scales)[static_cast<size_t>(row) * G + g] = s;
+  }
   *reinterpret_cast<uint2*>(q + static_cast<size_t>(row) * K + col) = make_uint2(lo, hi);
-  if ((lane & 15) == 0) scales[static_cast<size_t>(row) * G + g] = s;
 }
 
 // One block of 256 threads per 128x128 block: each thread owns 64 elements (16 rows x 4 columns
 // per pass, 4 bytes of output each), block-wide amax through LDS.
-template <typename WT>
+template <typename WT, bool kUe8m0>
 __global__ __launch_bounds__(256) void quantize_weight_kernel(const WT* __restrict__ w, int N,
                                                               int K, uint8_t* __restrict__ q,
-                                                              float* __restrict__ scales) {
+                                                              void* __restrict__ scales) {
   const int KB = K / kFp8Group, NB = N / kFp8Group;
   const int kb = blockIdx.x % KB;
   const int nb = (blockIdx.x / KB) % NB;
@@ -100,45 +115,79 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const WT* __restri
   if (lane_id() == 0) red[threadIdx.x / kWave] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  // fp32 rule: divide by s; UE8M0: multiply by 2^-e
+  const int b = ue8m0_byte(amax);
+  const float s = kUe8m0 ? ldexpf(1.0f, 127 - b) : (amax > 0.0f ? amax / 448.0f : 1.0f);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const size_t off = static_cast<size_t>(nb * kFp8Group + r0 + 8 * i) * K + kb * kFp8Group + c4;
     uint32_t packed = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) packed |= e4m3_encode(v[i][c] / s) << (8 * c);
+    for (int c = 0; c < 4; ++c)
+      packed |= e4m3_encode(kUe8m0 ? v[i][c] * s : v[i][c] / s) << (8 * c);
     *reinterpret_cast<uint32_t*>(dst + off) = packed;
   }
-  if (threadIdx.x == 0) scales[(mat * NB + nb) * KB + kb] = s;
+  if (threadIdx.x == 0) {
+    if constexpr (kUe8m0) static_cast<uint8_t*>(scales)[(mat * NB + nb) * KB + kb] = static_cast<uint8_t>(b);
+    else static_cast<float*>(scales)[(mat * NB + nb) * KB + kb] = s;
+  }
+}
+
+// e8m0 bytes -> their fp32 values 2^(b - 127) (exact).
+__global__ __launch_bounds__(256) void e8m0_expand_kernel(const uint8_t* __restrict__ b, size_t n,
+                                                          float* __restrict__ out) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    out[i] = ldexpf(1.0f, static_cast<int>(b[i]) - 127);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_act(const void* x, moe_dtype x_dtype, int M, int K,
-                               const int32_t* row_index, uint8_t* q, float* scales,
+                               const int32_t* row_index, uint8_t* q, void* scales, bool ue8m0,
                                hipStream_t stream) {
   const int G = K / kFp8Group;
   const long waves = static_cast<long>(M) * ((G + 3) / 4);
   dim3 grid(static_cast<unsigned>((waves + 3) / 4)), block(256);
-  if (x_dtype == MOE_BF16)
-    hipLaunchKernelGGL(quantize_act_kernel<uint16_t>, grid, block, 0, stream,
+  const bool bf16 = x_dtype == MOE_BF16;
+  if (bf16 && ue8m0)
+    hipLaunchKernelGGL((quantize_act_kernel<uint16_t, true>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(x), M, K, row_index, q, scales);
+  else if (bf16)
+    hipLaunchKernelGGL((quantize_act_kernel<uint16_t, false>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), M, K, row_index, q, scales);
+  else if (ue8m0)
+    hipLaunchKernelGGL((quantize_act_kernel<float, true>), grid, block, 0, stream,
+                       static_cast<const float*>(x), M, K, row_index, q, scales);
   else
-    hipLaunchKernelGGL(quantize_act_kernel<float>, grid, block, 0, stream,
+    hipLaunchKernelGGL((quantize_act_kernel<float, false>), grid, block, 0, stream,
                        static_cast<const float*>(x), M, K, row_index, q, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
-                                  uint8_t* q, float* scales, hipStream_t stream) {
+                                  uint8_t* q, void* scales, bool ue8m0, hipStream_t stream) {
   const long blocks = static_cast<long>(batch) * (N / kFp8Group) * (K / kFp8Group);
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  if (w_dtype == MOE_BF16)
-    hipLaunchKernelGGL(quantize_weight_kernel<uint16_t>, grid, block, 0, stream,
+  const bool bf16 = w_dtype == MOE_BF16;
+  if (bf16 && ue8m0)
+    hipLaunchKernelGGL((quantize_weight_kernel<uint16_t, true>), grid, block, 0, stream,
                        static_cast<const uint16_t*>(w), N, K, q, scales);
-  else
-    hipLaunchKernelGGL(quantize_weight_kernel<float>, grid, block, 0, stream,
+  else if (bf16)
+    hipLaunchKernelGGL((quantize_weight_kernel<uint16_t, false>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(w), N, K, q, scales);
+  else if (ue8m0)
+    hipLaunchKernelGGL((quantize_weight_kernel<float, true>), grid, block, 0, stream,
                        static_cast<const float*>(w), N, K, q, scales);
+  else
+    hipLaunchKernelGGL((quantize_weight_kernel<float, false>), grid, block, 0, stream,
+                       static_cast<const float*>(w), N, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_e8m0_expand(const uint8_t* b, size_t n, float* out, hipStream_t stream) {
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096));
+  hipLaunchKernelGGL(e8m0_expand_kernel, dim3(blocks), dim3(256), 0, stream, b, n, out);
   return hipGetLastError();
 }
 

@@ -106,6 +106,17 @@ def test_quantize_validation(lib):
                                 FAKE, None) == UNS  # misaligned
     assert lib.fp8_quantize_weight(FAKE, moe.MOE_F32, 2, 128, 200, 128, FAKE, FAKE, None) == UNS
     assert lib.fp8_quantize_weight(FAKE, moe.MOE_F32, 0, 128, 256, 128, FAKE, FAKE, None) == INV
+    # the UE8M0 variants validate the same way
+    assert lib.fp8_quantize_act_ue8m0(FAKE, moe.MOE_BF16, 4, 100, 128, None, FAKE, FAKE,
+                                      None) == UNS
+    assert lib.fp8_quantize_act_ue8m0(FAKE, moe.MOE_FP8_E4M3, 4, 256, 128, None, FAKE, FAKE,
+                                      None) == INV
+    assert lib.fp8_quantize_act_ue8m0(FAKE, moe.MOE_BF16, 4, 256, 128, None, FAKE, None,
+                                      None) == INV
+    assert lib.fp8_quantize_weight_ue8m0(FAKE, moe.MOE_F32, 2, 128, 200, 128, FAKE, FAKE,
+                                         None) == UNS
+    assert lib.fp8_quantize_weight_ue8m0(FAKE, moe.MOE_F32, 0, 128, 256, 128, FAKE, FAKE,
+                                         None) == INV
 
 
 def _args(**kw):
@@ -113,7 +124,7 @@ def _args(**kw):
                 y_dtype=moe.MOE_BF16, y_layout=moe.MOE_Y_SLOTS, x=0x1000, x_scales=None,
                 w_gate=0x1000, w_up=0x1000, w_down=0x1000, s_gate=None, s_up=None, s_down=None,
                 offsets=0x1000, sorted_pair=0x1000, topk_w=0x1000, y=0x1000, workspace=0x1000,
-                workspace_bytes=1 << 40, events=None)
+                workspace_bytes=1 << 40, events=None, scale_fmt=moe.MOE_SCALE_F32)
     base.update(kw)
     return moe.moe_experts_args(**base)
 
@@ -137,6 +148,8 @@ def test_experts_validation(lib):
     fp8 = dict(act_dtype=moe.MOE_FP8_E4M3, w_dtype=moe.MOE_FP8_E4M3)
     assert _fwd(lib, d=192, **fp8) == UNS                      # fp8 needs d % 128 == 0
     assert _fwd(lib, **fp8) == INV                             # fp8 needs the scales
+    assert _fwd(lib, scale_fmt=moe.MOE_SCALE_UE8M0) == INV     # UE8M0 scales only on fp8
+    assert _fwd(lib, scale_fmt=7, **fp8) == INV                # unknown scale format
     need = lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_BF16, moe.MOE_BF16)
     assert need >= 32 * 2 * 512 * 2
     assert _fwd(lib, workspace_bytes=need - 1) == moe.MOE_ERR_WORKSPACE_TOO_SMALL

@@ -5,6 +5,9 @@ Weights: fp32 masters from the generator, quantised to e4m3 with 128x128 block s
 bit-exactly, and the oracle then uses its own quantised weights. Activations: x is quantised per
 token per 128 channels by fp8_quantize_act inside the layer; the oracle applies the same rule to x
 and to h. Output bound: max|err| <= 6e-2 * max|ref| (the oracle of the quantised rule).
+Every test runs with fp32 block scales and with UE8M0 scales (e8m0 bytes, powers of two; the
+Transformers "Fine-grained FP8" page, section "UE8M0 scale format"), which the matrix unit applies
+itself.
 """
 import numpy as np
 import pytest
@@ -18,8 +21,11 @@ from gpu_util import assert_close_rel_max, log, out_to_f64, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _quantise_on_gpu(masters):
-    q, s = moe.fp8_quantize_weight(to_dev(masters))
+FMTS = ("f32", "ue8m0")
+
+
+def _quantise_on_gpu(masters, fmt="f32"):
+    q, s = moe.fp8_quantize_weight(to_dev(masters), scale_fmt=fmt)
     return q, s
 
 
@@ -38,56 +44,84 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("spec", SMALL, ids=lambda s: s.name)
-def test_small_fp8_layers(spec):
-    log(spec.name)
+def test_small_fp8_layers(spec, fmt):
+    log(spec.name, fmt)
     x = synth.gen_x(spec)
     logits = synth.gen_logits(spec)
     masters = [synth.gen_expert_weight(spec, n) for n in ("gate", "up", "down")]
-    wq = [_quantise_on_gpu(m) for m in masters]
-    wq_ref = [oracle.quantize_weight(m) for m in masters]
+    wq = [_quantise_on_gpu(m, fmt) for m in masters]
+    wq_ref = [oracle.quantize_weight(m, scale_fmt=fmt) for m in masters]
     for (q, s), (qr, sr) in zip(wq, wq_ref):
         np.testing.assert_array_equal(to_host(s), sr)
         np.testing.assert_array_equal(to_host(q), qr)
     ids_ref, w_ref = oracle.route(logits, spec.k)
-    ex = oracle.Experts(*(q for q, _ in wq_ref), *(s for _, s in wq_ref), quant_act=True)
+    ex = oracle.Experts(*(q for q, _ in wq_ref), *(s for _, s in wq_ref), quant_act=True,
+                        scale_fmt=fmt)
     ref = oracle.moe_forward(x, ex, ids_ref, w_ref)
     for layout in ("slots", "permuted", "acc_f32"):
         res = _run_layer(x, logits, wq, spec.k, layout)
         np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
         got = out_to_f64(res.out)
         assert np.all(np.isfinite(got))
-        assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, layout))
+        assert_close_rel_max(got, ref, 6e-2, "%s %s %s" % (spec.name, fmt, layout))
 
 
-def test_fp8_hidden_codes_match_oracle_rule():
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xdt", ("bf16", "f32"))
+def test_quantize_act_bit_exact(fmt, xdt):
+    # codes and scales of the activation rule, with and without the row gather, against the
+    # oracle's quantiser on the same inputs (bit for bit)
+    spec = synth.DSV3_FP8.with_(T=333, d=640)
+    x = synth.gen_x(spec)
+    if xdt == "f32":
+        x = synth.bf16_bits_to_f32(x) * np.float32(37.5)
+    rows = np.random.default_rng(9).integers(0, spec.T, 500).astype(np.int32)
+    log("quantize_act", fmt, xdt)
+    for idx in (None, rows):
+        q, s = moe.fp8_quantize_act(to_dev(x), row_index=None if idx is None else to_dev(idx),
+                                    scale_fmt=fmt)
+        torch.cuda.synchronize()
+        xr = x if idx is None else x[idx]
+        qr, sr = oracle.quantize_act(xr, scale_fmt=fmt)
+        np.testing.assert_array_equal(to_host(s), sr)
+        np.testing.assert_array_equal(to_host(q), qr)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_hidden_codes_match_oracle_rule(fmt):
     # The gate/up GEMM's h codes/scales, dequantised, stay within one e4m3 rounding step of the
     # oracle's h (computed in fp64 before quantisation) for every pair.
     spec = SMALL[0]
     x = synth.gen_x(spec)
     logits = synth.gen_logits(spec)
     masters = [synth.gen_expert_weight(spec, n) for n in ("gate", "up", "down")]
-    wq = [_quantise_on_gpu(m) for m in masters]
+    wq = [_quantise_on_gpu(m, fmt) for m in masters]
     (qg, sg), (qu, su), (qd, sd) = wq
     ids, w, _ = moe.moe_route(spec.k, logits=to_dev(logits))
     perm = moe.moe_permute(ids, spec.E)
-    xq, xs = moe.fp8_quantize_act(to_dev(x))
+    xq, xs = moe.fp8_quantize_act(to_dev(x), scale_fmt=fmt)
     ws = torch.empty(moe.experts_workspace_bytes(spec.T, spec.d, spec.f, spec.E, spec.k,
                                                  moe.MOE_FP8_E4M3, moe.MOE_FP8_E4M3),
                      dtype=torch.uint8, device="cuda")
     moe.moe_experts_forward(xq, qg, qu, qd, perm.offsets, perm.sorted_pair, w, spec.k,
-                            x_scales=xs, s_gate=sg, s_up=su, s_down=sd, workspace=ws)
+                            x_scales=xs, s_gate=sg, s_up=su, s_down=sd, workspace=ws,
+                            scale_fmt=fmt)
     torch.cuda.synchronize()
     P, f = spec.P, spec.f
     # workspace layout: two 256-byte-aligned tile tables, then h codes [P, f], then h scales
     off_h = 2 * ((spec.E + 1) * 4 + 255) // 256 * 256
     hq = to_host(ws[off_h:off_h + P * f]).reshape(P, f)
     off_s = off_h + (P * f + 255) // 256 * 256
+    # (fp32 scale values in both formats; with UE8M0 they are powers of two)
     hs = to_host(ws[off_s:off_s + P * (f // 128) * 4].view(torch.float32)).reshape(P, f // 128)
+    if fmt == "ue8m0":
+        assert np.all(np.frexp(hs)[0] == 0.5)
     h_gpu = oracle.e4m3_decode_array(hq) * np.repeat(hs.astype(np.float64), 128, axis=1)
     sp = to_host(perm.sorted_pair)
-    ex = oracle.Experts(*(oracle.quantize_weight(m)[0] for m in masters),
-                        *(oracle.quantize_weight(m)[1] for m in masters), quant_act=True)
+    wr = [oracle.quantize_weight(m, scale_fmt=fmt) for m in masters]
+    ex = oracle.Experts(*(q for q, _ in wr), *(s for _, s in wr), quant_act=True, scale_fmt=fmt)
     ids_h = to_host(ids).reshape(-1)
     h_ref, _ = oracle.expert_pairs(x, ex, sp // spec.k, ids_h[sp], want_y=False)
     # one e4m3 step is 2^-3 relative (normal range) plus the group scale's subnormal step
@@ -95,7 +129,8 @@ def test_fp8_hidden_codes_match_oracle_rule():
     assert np.all(np.abs(h_gpu - h_ref) <= bound + 1e-3 * np.abs(h_ref).max())
 
 
-def test_dsv3_fp8_full_sampled():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dsv3_fp8_full_sampled(fmt):
     spec = synth.DSV3_FP8
     T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
     log("generating", spec.name)
@@ -112,18 +147,19 @@ def test_dsv3_fp8_full_sampled():
     for which in ("gate", "up", "down"):
         rows, cols = (f, d) if which != "down" else (d, f)
         qt = torch.empty((E, rows, cols), dtype=torch.uint8, device="cuda")
-        st = torch.empty((E, rows // 128, cols // 128), dtype=torch.float32, device="cuda")
+        sdt = (torch.uint8, np.uint8) if fmt == "ue8m0" else (torch.float32, np.float32)
+        st = torch.empty((E, rows // 128, cols // 128), dtype=sdt[0], device="cuda")
         rq = np.empty((len(need), rows, cols), np.uint8)
-        rs = np.empty((len(need), rows // 128, cols // 128), np.float32)
+        rs = np.empty((len(need), rows // 128, cols // 128), sdt[1])
         for e0 in range(0, E, 16):
             chunk = list(range(e0, e0 + 16))
             m = synth.gen_expert_weight(spec, which, experts=chunk)
-            q, s = moe.fp8_quantize_weight(to_dev(m))
+            q, s = moe.fp8_quantize_weight(to_dev(m), scale_fmt=fmt)
             qt[e0:e0 + 16] = q
             st[e0:e0 + 16] = s
             sel = [e for e in chunk if e in remap]
             if sel:
-                oq, os_ = oracle.quantize_weight(m[[e - e0 for e in sel]])
+                oq, os_ = oracle.quantize_weight(m[[e - e0 for e in sel]], scale_fmt=fmt)
                 for i, e in enumerate(sel):
                     rq[remap[e]] = oq[i]
                     rs[remap[e]] = os_[i]
@@ -139,7 +175,7 @@ def test_dsv3_fp8_full_sampled():
     np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
     got = out_to_f64(res.out)[tokens]
     ex = oracle.Experts(ref_q["gate"], ref_q["up"], ref_q["down"], ref_s["gate"], ref_s["up"],
-                        ref_s["down"], quant_act=True)
+                        ref_s["down"], quant_act=True, scale_fmt=fmt)
     ids_sub = np.vectorize(remap.get)(ids_ref[tokens]).astype(np.int32)
     ref = oracle.moe_forward(x[tokens], ex, ids_sub, w_ref[tokens])
-    assert_close_rel_max(got, ref, 6e-2, spec.name)
+    assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, fmt))
