@@ -69,7 +69,8 @@ class Layer:
     moe_route (given logits, or the fp32 router GEMM), moe_permute, fp8_quantize_act (fp8
     layers), moe_experts_forward, moe_combine."""
 
-    def __init__(self, moe, spec, x, W, n_ev_steps, logits=None, Wr=None, scales=None):
+    def __init__(self, moe, spec, x, W, n_ev_steps, logits=None, Wr=None, scales=None,
+                 scale_fmt="f32"):
         import torch
         self.moe, self.spec = moe, spec
         self.lib = moe.load_library()
@@ -103,9 +104,12 @@ class Layer:
         p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
         self._quant = None
         x_in, xs = x, None
+        ue = scale_fmt == "ue8m0"
+        self._quant_fn = self.lib.fp8_quantize_act_ue8m0 if ue else self.lib.fp8_quantize_act
         if spec.dtype == "fp8":
             self.xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
-            self.xs = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
+            self.xs = torch.empty((T, d // 128), dtype=torch.uint8 if ue else torch.float32,
+                                  device=dev)
             self._quant = (p(x), moe.MOE_BF16, T, d, 128, None, p(self.xq), p(self.xs),
                            self.stream)
             x_in, xs = self.xq, self.xs
@@ -118,7 +122,8 @@ class Layer:
             Wd.data_ptr(), sg.data_ptr() if sg is not None else None,
             su.data_ptr() if su is not None else None, sd.data_ptr() if sd is not None else None,
             self.offsets.data_ptr(), self.sp.data_ptr(), self.w.data_ptr(), self.y.data_ptr(),
-            self.ews.data_ptr(), self.ews.numel(), None)
+            self.ews.data_ptr(), self.ews.numel(), None,
+            moe.MOE_SCALE_UE8M0 if ue else moe.MOE_SCALE_F32)
         if logits is None:
             self._route = (None, p(x), act, p(Wr), T, d, E, k, p(self.logits), p(self.ids),
                            p(self.w), self.stream)
@@ -136,7 +141,7 @@ class Layer:
         chk(lib.moe_route(*self._route))
         chk(lib.moe_permute(*self._perm))
         if self._quant is not None:
-            chk(lib.fp8_quantize_act(*self._quant))
+            chk(self._quant_fn(*self._quant))
         self.args.events = (ctypes.cast(self.ev_arrays[ev_index], ctypes.c_void_p)
                             if ev_index is not None else None)
         chk(lib.moe_experts_forward(ctypes.byref(self.args), self.stream))
@@ -194,8 +199,9 @@ def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
     }
 
 
-def measure_other(moe, synth, spec, steps, warmup):
-    """Times one extra workload (given router logits) and returns its figures."""
+def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
+    """Times one extra workload (given router logits) and returns its figures. fp8 layers take
+    fp32 block scales, or UE8M0 (e8m0 byte) scales with scale_fmt="ue8m0"."""
     import numpy as np
     import torch
 
@@ -214,10 +220,11 @@ def measure_other(moe, synth, spec, steps, warmup):
         for which in ("gate", "up", "down"):
             rows, cols = (spec.f, spec.d) if which != "down" else (spec.d, spec.f)
             q = torch.empty((spec.E, rows, cols), dtype=torch.uint8, device="cuda")
-            sc = torch.empty((spec.E, rows // 128, cols // 128), dtype=torch.float32, device="cuda")
+            sc = torch.empty((spec.E, rows // 128, cols // 128), device="cuda",
+                             dtype=torch.uint8 if scale_fmt == "ue8m0" else torch.float32)
             for e0 in range(0, spec.E, 16):
                 m = up(synth.gen_expert_weight(spec, which, experts=range(e0, min(e0 + 16, spec.E))))
-                qq, ss = moe.fp8_quantize_weight(m)
+                qq, ss = moe.fp8_quantize_weight(m, scale_fmt=scale_fmt)
                 q[e0:e0 + 16] = qq
                 sc[e0:e0 + 16] = ss
                 del m
@@ -226,8 +233,10 @@ def measure_other(moe, synth, spec, steps, warmup):
         scales = tuple(S)
     else:
         W = [up(synth.gen_expert_weight(spec, n)) for n in ("gate", "up", "down")]
-    log("%s inputs ready in %.1fs" % (spec.name, time.perf_counter() - t0))
-    layer = Layer(moe, spec, x, tuple(W), steps, logits=logits, scales=scales)
+    name = spec.name + ("_ue8m0" if scale_fmt == "ue8m0" else "")
+    log("%s inputs ready in %.1fs" % (name, time.perf_counter() - t0))
+    layer = Layer(moe, spec, x, tuple(W), steps, logits=logits, scales=scales,
+                  scale_fmt=scale_fmt)
     el = time_steps(layer, steps, warmup)
     g1, g2 = layer.kernel_ms(steps)
     counts = layer.counts.cpu().numpy()
@@ -236,7 +245,7 @@ def measure_other(moe, synth, spec, steps, warmup):
     w_bytes = touched * 3 * spec.d * spec.f * wbytes
     ms = el / steps * 1e3
     r = {
-        "workload": spec.name, "ms_per_step": round(ms, 4),
+        "workload": name, "ms_per_step": round(ms, 4),
         "active_tflops": round(spec.active_flops() / (ms * 1e-3) / 1e12, 2),
         "tokens_per_s": round(spec.T / (ms * 1e-3), 1),
         "gate_up_ms": round(g1, 4), "down_ms": round(g2, 4),
@@ -247,7 +256,7 @@ def measure_other(moe, synth, spec, steps, warmup):
         "experts_empty": int((counts == 0).sum()),
     }
     log("%s: %.3f ms/step, %.1f TFLOP/s (gate/up %.3f ms, down %.3f ms)" % (
-        spec.name, ms, r["active_tflops"], g1, g2))
+        name, ms, r["active_tflops"], g1, g2))
     del layer
     torch.cuda.empty_cache()
     return r
@@ -265,7 +274,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--report", default="",
                     help="also time the skewed 128-expert bf16 layer, the DeepSeek-V3-shaped fp8 "
-                         "layer and the tiny fp32 layer; write their figures to this JSON file")
+                         "layer (fp32 and UE8M0 block scales) and the tiny fp32 layer; write their "
+                         "figures to this JSON file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain fp32 copy kernel (out = in * 1) over this many MiB, "
                          "3 times, to calibrate HBM byte counters")
@@ -393,8 +403,9 @@ def main():
         del Wg, Wu, Wd
         torch.cuda.empty_cache()
         rep = [result.get("decode")]
-        for spec_o in (synth.SKEWED_128E, synth.DSV3_FP8, synth.TINY_F32):
-            rep.append(measure_other(moe, synth, spec_o, max(args.steps, 5), args.warmup))
+        for spec_o, fmt in ((synth.SKEWED_128E, "f32"), (synth.DSV3_FP8, "f32"),
+                            (synth.DSV3_FP8, "ue8m0"), (synth.TINY_F32, "f32")):
+            rep.append(measure_other(moe, synth, spec_o, max(args.steps, 5), args.warmup, fmt))
         with open(args.report, "w") as fh:
             json.dump({"prefill": {k: result[k] for k in ("value", "ms_per_step", "config",
                                                           "roofline")},
