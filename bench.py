@@ -262,6 +262,38 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
     return r
 
 
+def measure_decode_fp8(moe, synth, W, Wr, steps, warmup, scale_fmt):
+    """The Mixtral-shaped decode layer with its bf16 weights quantised to e4m3 (128x128 blocks,
+    fp32 or UE8M0 scales) on the device: the weight-streaming fp8 kernels."""
+    import torch
+    dspec = synth.MIXTRAL_DECODE.with_(dtype="fp8")
+    name = "mixtral_decode_fp8_T%d_d%d_f%d_E%d_k%d%s" % (
+        dspec.T, dspec.d, dspec.f, dspec.E, dspec.k, "_ue8m0" if scale_fmt == "ue8m0" else "")
+    Q, S = [], []
+    for w in W:
+        q, s_ = moe.fp8_quantize_weight(w, scale_fmt=scale_fmt)
+        Q.append(q)
+        S.append(s_)
+    xd = torch.from_numpy(synth.gen_x(synth.MIXTRAL_DECODE).view("int16")).cuda().view(torch.bfloat16)
+    layer = Layer(moe, dspec, xd, tuple(Q), steps, Wr=Wr, scales=tuple(S), scale_fmt=scale_fmt)
+    el = time_steps(layer, steps, warmup)
+    g1, g2 = layer.kernel_ms(steps)
+    touched = int((layer.counts.cpu().numpy() > 0).sum())
+    ms = el / steps * 1e3
+    wb = touched * 3 * dspec.d * dspec.f
+    r = {"workload": name, "ms_per_step": round(ms, 4),
+         "tokens_per_s": round(dspec.T / (ms * 1e-3), 1),
+         "gate_up_ms": round(g1, 4), "down_ms": round(g2, 4),
+         "gate_up_weight_GBps": round(touched * 2 * dspec.d * dspec.f / (g1 * 1e-3) / 1e9, 1),
+         "weight_GBps_layer": round(wb / (ms * 1e-3) / 1e9, 1), "experts_touched": touched}
+    log("%s: %.3f ms/step, %.0f tokens/s; gate/up %.3f ms (%.0f GB/s of e4m3 weights), down "
+        "%.3f ms (incl. h quantisation)" % (name, ms, r["tokens_per_s"], g1,
+                                            r["gate_up_weight_GBps"], g2))
+    del layer, Q, S
+    torch.cuda.empty_cache()
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,9 +432,12 @@ def main():
         del dl
 
     if args.report:
+        rep = [result.get("decode")]
+        for fmt in ("f32", "ue8m0"):
+            rep.append(measure_decode_fp8(moe, synth, (Wg, Wu, Wd), Wr, max(args.decode_steps, 5),
+                                          5, fmt))
         del Wg, Wu, Wd
         torch.cuda.empty_cache()
-        rep = [result.get("decode")]
         for spec_o, fmt in ((synth.SKEWED_128E, "f32"), (synth.DSV3_FP8, "f32"),
                             (synth.DSV3_FP8, "ue8m0"), (synth.TINY_F32, "f32")):
             rep.append(measure_other(moe, synth, spec_o, max(args.steps, 5), args.warmup, fmt))

@@ -41,13 +41,18 @@ inline bool uses_decode(moe_dtype act, moe_dtype w, long long P, int d, int f) {
          f % 128 == 0;
 }
 
+// fp8 layers with few pairs take the weight-streaming fp8 kernels.
+inline bool uses_fp8_decode(moe_dtype act, moe_dtype w, long long P) {
+  return act == MOE_FP8_E4M3 && w == MOE_FP8_E4M3 && P <= kDecodeMaxPairs;
+}
+
 // bf16 tiled GEMMs cut their tail tiles; they need partial-tile slots and counters.
 inline bool uses_split(moe_dtype act, moe_dtype w, long long P, int d, int f) {
   return act == MOE_BF16 && w == MOE_BF16 && !uses_decode(act, w, P, d, f);
 }
 
 struct ExpertsLayout {
-  size_t cum_a, cum_b, h, h_scales, x_scales, split_partial, total;
+  size_t cum_a, cum_b, h, h_scales, x_scales, h32, h_scale_bytes, split_partial, total;
 };
 
 ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, moe_dtype w) {
@@ -66,6 +71,14 @@ ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, m
   // fp8 with UE8M0 scales: x_scales expanded from e8m0 bytes to fp32 values
   L.x_scales = off;
   if (w == MOE_FP8_E4M3) off = align_up(off + static_cast<size_t>(T) * (d / kFp8Group) * sizeof(float));
+  // fp8 decode: fp32 h before its quantisation, and its e8m0 scale bytes
+  L.h32 = L.h_scale_bytes = 0;
+  if (uses_fp8_decode(act, w, static_cast<long long>(P))) {
+    L.h32 = off;
+    off = align_up(off + P * f * sizeof(float));
+    L.h_scale_bytes = off;
+    off = align_up(off + P * (f / kFp8Group));
+  }
   L.split_partial = 0;
   if (uses_split(act, w, static_cast<long long>(P), d, f)) {
     L.split_partial = off;
@@ -291,6 +304,9 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   X.y = a->y;
   X.h = ws + L.h;
   X.h_scales = reinterpret_cast<float*>(ws + L.h_scales);
+  const bool fp8_decode = fp8 && uses_fp8_decode(act, w, P);
+  X.h32 = fp8_decode ? reinterpret_cast<float*>(ws + L.h32) : nullptr;
+  X.h_scale_bytes = fp8_decode ? reinterpret_cast<uint8_t*>(ws + L.h_scale_bytes) : nullptr;
   X.cpx = cus_per_xcd();
   const bool split = uses_split(act, w, P, a->d, a->f);
   X.split_partial = split ? reinterpret_cast<float*>(ws + L.split_partial) : nullptr;
@@ -299,12 +315,13 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   const bool decode = uses_decode(act, w, P, a->d, a->f);
   int bm_a, bm_b;
   if (f32) { bm_a = bm_b = f32_tile_rows(); }
+  else if (fp8_decode) { bm_a = bm_b = 0; }  // no tile table
   else if (fp8) { bm_a = fp8_tile_rows_gateup(); bm_b = fp8_tile_rows_down(); }
   else if (decode) { bm_a = bm_b = 0; }  // no tile table
   else { bm_a = bf16_tile_rows_gateup(); bm_b = bf16_tile_rows_down(); }
 
   hipError_t e = hipSuccess;
-  if (!decode) {  // the decode kernels map (expert, row panel) directly and need no tile table
+  if (!decode && !fp8_decode) {  // decode kernels map (expert, row panel) directly: no tile table
     e = launch_tile_table(a->offsets, a->E, bm_a, bm_b, const_cast<int32_t*>(X.tile_cum_a),
                           const_cast<int32_t*>(X.tile_cum_b), stream);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
@@ -324,6 +341,7 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
     X.a_scales = xs;
   }
   if (f32) e = launch_experts_f32(X, stream);
+  else if (fp8_decode) e = launch_experts_fp8_decode(X, stream);
   else if (fp8) e = launch_experts_fp8(X, stream);
   else if (decode) e = launch_experts_bf16_decode(X, stream);
   else e = launch_experts_bf16(X, stream);

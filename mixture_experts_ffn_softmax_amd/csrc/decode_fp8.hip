@@ -1,0 +1,293 @@
+// Small-batch (decode) fine-grained FP8 expert GEMMs: e4m3 weight streaming with the weight rows
+// on the matrix unit's M side.
+//
+// The swap-AB idea of the bf16 decode kernels (AWS fused-MoE news page, sections on reordering the
+// product for WGMMA and on swap-AB in MoE workloads; Transformers "Experts backends" page,
+// decode-time switch to a small-batch kernel) with the e4m3 operands of the Transformers
+// "Fine-grained FP8" page: weights in 128x128 blocks with one scale each, activations per token
+// per 128 channels. One v_mfma_scale_f32_16x16x128_f8f6f4 takes 16 weight rows (A) and 16 tokens
+// (B) over one 128-wide K block, i.e. exactly one weight scale per row group and one activation
+// scale per token. With fp32 scales its result is promoted by w_scale * x_scale; with UE8M0
+// scales (same page, "UE8M0 scale format") the bytes go to the instruction, which accumulates
+// across K blocks. The streamed weight bytes are half those of the bf16 kernels.
+//
+// Work split as in the bf16 K-split kernel: a workgroup owns 64 weight rows of one expert (gate/up:
+// 32 gate rows and the matching 32 up rows; down: 64 rows) for all of that expert's tokens, in
+// passes of 64 tokens; its 4 waves take the 128-wide K blocks in turn and reduce through LDS. The
+// gate/up kernel writes h in fp32, since one 128-channel group of h spans four workgroups; the
+// caller quantises it per (pair, 128 channels) before the down kernel.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kFdGateRows = 32;   // gate rows (and as many up rows) per gate/up workgroup
+constexpr int kFdDownRows = 64;   // W_down rows per down workgroup
+constexpr int kFdTokens = 64;     // tokens per pass (4 groups of 16)
+constexpr int kGateUp = 0;
+constexpr int kDown = 1;
+
+struct Fp8DecodeArgs {
+  const uint8_t* a;           // gate/up: x codes [T, K] (gathered); down: h codes [P, K]
+  const float* a_s;           // activation scales [rows, K/128] (fp32; powers of two for UE8M0)
+  int a_gather;
+  const int32_t* sorted_pair;
+  int k;
+  const uint8_t* w0;          // W_gate or W_down [E, N, K] e4m3
+  const uint8_t* w1;          // W_up
+  const void* s0;             // block scales of w0 [E, N/128, K/128]: fp32, or e8m0 bytes
+  const void* s1;
+  int K, N;
+  const int32_t* offsets;
+  float* h32;                 // gate/up output h [P, N] fp32
+  void* y;                    // down output
+  int y_layout, y_bf16;
+  const float* topk_w;
+};
+
+__device__ __forceinline__ i32x8_t ld32g(const uint8_t* p) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 16);
+  i32x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+template <int MODE, bool kUE>
+__global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
+  constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
+  const int nrb = (p.N + kRows - 1) / kRows;
+  const int e = blockIdx.x / nrb;
+  const int rb = blockIdx.x - e * nrb;
+  const int row0 = p.offsets[e];
+  const int M = p.offsets[e + 1] - row0;
+  if (M <= 0) return;
+
+  __shared__ f32x4_t red[4][4][4][64];  // [wave][row group][token group][lane], 64 KB
+  // UE8M0: the row groups' scale bytes for every K block, loaded once (byte loads in the K loop
+  // would be vector loads, and waiting for one waits for the weight stream issued before it)
+  __shared__ uint8_t wsb[4][256];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  const int KB = p.K / 128, NB = p.N / 128;
+
+  // A rows (4 groups of 16 weight rows); a group lies inside one 128-row scale block.
+  const uint8_t* arow[4];
+  const void* ascale[4];   // this expert's scale row of the group's 128-row block
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    int n;
+    const uint8_t* base;
+    const void* sbase;
+    if (MODE == kGateUp) {
+      n = rb * kRows + (rg & 1) * 16;
+      base = (rg < 2 ? p.w0 : p.w1) + e * wstride;
+      sbase = rg < 2 ? p.s0 : p.s1;
+    } else {
+      n = rb * kRows + rg * 16;
+      base = p.w0 + e * wstride;
+      sbase = p.s0;
+    }
+    const int nb = min(n, p.N - 1) / 128;
+    const size_t sidx = (static_cast<size_t>(e) * NB + nb) * KB;
+    ascale[rg] = kUE ? static_cast<const void*>(static_cast<const uint8_t*>(sbase) + sidx)
+                     : static_cast<const void*>(static_cast<const float*>(sbase) + sidx);
+    arow[rg] = base + static_cast<size_t>(min(n + r16, p.N - 1)) * p.K + g * 32;
+  }
+  if constexpr (kUE) {
+    for (int i = tid; i < 4 * KB; i += 256)
+      wsb[i / KB][i % KB] = static_cast<const uint8_t*>(ascale[i / KB])[i % KB];
+    __syncthreads();
+  }
+
+  for (int tc0 = 0; tc0 < M; tc0 += kFdTokens) {
+    const int ntg = min(4, (M - tc0 + 15) / 16);
+    const uint8_t* brow[4];
+    const float* bscale[4];
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const int ti = min(tc0 + tg * 16 + r16, M - 1);
+      const int pos = row0 + ti;
+      const int src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+      brow[tg] = p.a + static_cast<size_t>(src) * p.K + g * 32;
+      bscale[tg] = p.a_s + static_cast<size_t>(src) * KB;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int c = wave; c < KB; c += 4) {
+      const int kb = c * 128;
+      i32x8_t av[4], bv[4];
+      float bs[4];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) av[rg] = ld32g(arow[rg] + kb);
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg)
+        if (tg < ntg) {
+          bv[tg] = ld32g(brow[tg] + kb);
+          bs[tg] = bscale[tg][c];
+        }
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) {
+        if (tg >= ntg) continue;
+        if constexpr (kUE) {
+          // the token's e8m0 byte: exponent field of its power-of-two fp32 scale. Each block's
+          // product starts from zero and is added afterwards: with a token group or two the
+          // few accumulators would otherwise chain every MFMA to the previous K block's.
+          const int ex = (__float_as_uint(bs[tg]) >> 23) & 0xFF;
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const int ew = wsb[rg][c];
+            acc[rg][tg] += __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                av[rg], bv[tg], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, ew, 0, ex);
+          }
+        } else {
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            const float sc = static_cast<const float*>(ascale[rg])[c] * bs[tg];
+            const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                av[rg], bv[tg], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[rg][tg][q] = fmaf(part[q], sc, acc[rg][tg][q]);
+          }
+        }
+      }
+    }
+
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) red[wave][rg][tg][lane] = acc[rg][tg];
+    __syncthreads();
+
+    // Wave w finishes token group w. Output layout of a 16x16 block: lane l holds token l % 16
+    // and weight rows 4 * (l / 16) + i, i = 0..3.
+    const int tg = wave;
+    const int ti = tc0 + tg * 16 + r16;
+    if (tg < ntg && ti < M) {
+      f32x4_t s[4];
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        s[rg] = red[0][rg][tg][lane] + red[1][rg][tg][lane] + red[2][rg][tg][lane] +
+                red[3][rg][tg][lane];
+      const int pos = row0 + ti;
+      if (MODE == kGateUp) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int n = rb * kRows + half * 16 + 4 * g;
+          if (n < p.N) {
+            f32x4_t hv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = silu_mul(s[half][i], s[half + 2][i]);
+            *reinterpret_cast<f32x4_t*>(p.h32 + static_cast<size_t>(pos) * p.N + n) = hv;
+          }
+        }
+      } else {
+        const int pair = p.sorted_pair[pos];
+        const float wgt = p.topk_w ? p.topk_w[pair] : 1.0f;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int n = rb * kRows + rg * 16 + 4 * g;
+          if (n >= p.N) continue;
+          f32x4_t v = s[rg];
+          if (p.y_layout == MOE_Y_ACC_F32) {
+            float* dst = static_cast<float*>(p.y) + static_cast<size_t>(pair / p.k) * p.N + n;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) atomicAdd(dst + i, wgt * v[i]);
+            continue;
+          }
+          size_t idx;
+          if (p.y_layout == MOE_Y_PERMUTED) {
+            idx = static_cast<size_t>(pos) * p.N + n;
+          } else {
+            idx = static_cast<size_t>(pair) * p.N + n;
+            v = v * wgt;
+          }
+          if (p.y_bf16) {
+            u32x2_t o;
+            o[0] = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+            o[1] = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.y) + idx) = o;
+          } else {
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + idx) = v;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int MODE>
+hipError_t launch_one(const Fp8DecodeArgs& a, int E, bool ue, hipStream_t stream) {
+  constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
+  const dim3 grid(static_cast<unsigned>(E * ((a.N + kRows - 1) / kRows))), block(256);
+  if (ue) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((decode_fp8_kernel<MODE, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream) {
+  const int P = L.T * L.k;
+  Fp8DecodeArgs g{};
+  g.a = static_cast<const uint8_t*>(L.a);
+  g.a_s = L.a_scales;
+  g.a_gather = L.a_gather;
+  g.sorted_pair = L.sorted_pair;
+  g.k = L.k;
+  g.w0 = static_cast<const uint8_t*>(L.w_gate);
+  g.w1 = static_cast<const uint8_t*>(L.w_up);
+  g.s0 = L.s_gate;
+  g.s1 = L.s_up;
+  g.K = L.d;
+  g.N = L.f;
+  g.offsets = L.offsets;
+  g.h32 = L.h32;
+  const bool ue = L.scale_ue8m0 != 0;
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
+  hipError_t e = launch_one<kGateUp>(g, L.E, ue, stream);
+  if (e != hipSuccess) return e;
+  // h -> e4m3 codes with per-(pair, 128-channel) scales, as fp32 values for the down kernel
+  uint8_t* hq = static_cast<uint8_t*>(L.h);
+  if (ue) {
+    e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, L.h_scale_bytes, true, stream);
+    if (e == hipSuccess)
+      e = launch_e8m0_expand(L.h_scale_bytes, static_cast<size_t>(P) * (L.f / 128), L.h_scales,
+                             stream);
+  } else {
+    e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, L.h_scales, false, stream);
+  }
+  if (e != hipSuccess) return e;
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+
+  Fp8DecodeArgs dn{};
+  dn.a = hq;
+  dn.a_s = L.h_scales;
+  dn.a_gather = 0;
+  dn.sorted_pair = L.sorted_pair;
+  dn.k = L.k;
+  dn.w0 = static_cast<const uint8_t*>(L.w_down);
+  dn.s0 = L.s_down;
+  dn.K = L.f;
+  dn.N = L.d;
+  dn.offsets = L.offsets;
+  dn.y = L.y;
+  dn.y_layout = L.y_layout;
+  dn.y_bf16 = L.y_bf16;
+  dn.topk_w = L.topk_w;
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
+  e = launch_one<kDown>(dn, L.E, ue, stream);
+  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
+  return e;
+}
+
+}  // namespace moe

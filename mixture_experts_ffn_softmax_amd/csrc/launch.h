@@ -66,6 +66,8 @@ struct ExpertsLaunch {
   void* y;
   void* h;                    // workspace: hidden activations [P, f]
   float* h_scales;            // fp8: [P, f/128] fp32 (powers of two when scale_ue8m0)
+  float* h32;                 // fp8 decode: h [P, f] fp32 before its quantisation
+  uint8_t* h_scale_bytes;     // fp8 decode with UE8M0 scales: [P, f/128] e8m0 bytes
   int cpx;                    // CUs per XCD (<= kSplitSlots / 8)
   float* split_partial;       // bf16 GEMMs: [kSplitSlots][256 * 256] fp32, or null (no cutting;
                               // the two GEMMs use it one after the other)
@@ -84,5 +86,6 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
 int fp8_tile_rows_gateup();
 int fp8_tile_rows_down();
 hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream);
+hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream);
 
 }  // namespace moe

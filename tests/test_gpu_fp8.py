@@ -179,3 +179,61 @@ def test_dsv3_fp8_full_sampled(fmt):
     ids_sub = np.vectorize(remap.get)(ids_ref[tokens]).astype(np.int32)
     ref = oracle.moe_forward(x[tokens], ex, ids_sub, w_ref[tokens])
     assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, fmt))
+
+
+# ---- small batches: the weight-streaming fp8 kernels (P <= 256 pairs) ------------------------
+
+DECODE = [
+    synth.DSV3_FP8.with_(name="fp8dec_T32_d512_f384_E8_k2", T=32, d=512, f=384, E=8, k=2),
+    # about 100 tokens per expert: several 64-token passes
+    synth.DSV3_FP8.with_(name="fp8dec_T200_d256_f256_E2_k1", T=200, d=256, f=256, E=2, k=1),
+    # P = 256, the largest batch the streaming kernels take
+    synth.DSV3_FP8.with_(name="fp8dec_T64_d384_f640_E16_k4", T=64, d=384, f=640, E=16, k=4),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("spec", DECODE, ids=lambda s: s.name)
+def test_fp8_decode_layers(spec, fmt):
+    assert spec.P <= 256
+    test_small_fp8_layers(spec, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mixtral_fp8_decode_full_sampled(fmt):
+    # the Mixtral-shaped decode layer (T=32, d=4096, f=14336, E=8, k=2) with its weights
+    # quantised to e4m3 on the GPU (codes and scales checked bit-exactly against the oracle's);
+    # the oracle runs on 8 sampled tokens
+    spec = synth.MIXTRAL_DECODE
+    T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
+    x = synth.gen_x(spec)
+    lg = oracle.router_logits(x, synth.gen_router_weight(spec))
+    ids_ref, w_ref = oracle.route(lg, k)
+    dev_q, dev_s, ref_q, ref_s = {}, {}, {}, {}
+    for which in ("gate", "up", "down"):
+        rows, cols = (f, d) if which != "down" else (d, f)
+        sdt = (torch.uint8, np.uint8) if fmt == "ue8m0" else (torch.float32, np.float32)
+        qt = torch.empty((E, rows, cols), dtype=torch.uint8, device="cuda")
+        st = torch.empty((E, rows // 128, cols // 128), dtype=sdt[0], device="cuda")
+        rq = np.empty((E, rows, cols), np.uint8)
+        rs = np.empty((E, rows // 128, cols // 128), sdt[1])
+        for e in range(E):
+            m = synth.bf16_bits_to_f32(synth.gen_expert_weight(spec, which, experts=[e]))
+            q, s = moe.fp8_quantize_weight(to_dev(m), scale_fmt=fmt)
+            oq, os_ = oracle.quantize_weight(m, scale_fmt=fmt)
+            np.testing.assert_array_equal(to_host(q), oq)
+            np.testing.assert_array_equal(to_host(s), os_)
+            qt[e], st[e], rq[e], rs[e] = q[0], s[0], oq[0], os_[0]
+        dev_q[which], dev_s[which] = qt, st
+        ref_q[which], ref_s[which] = rq, rs
+    log("weights quantised; running the decode layer", fmt)
+    res = moe.moe_layer(to_dev(x), dev_q["gate"], dev_q["up"], dev_q["down"], k,
+                        logits=to_dev(lg), s_gate=dev_s["gate"], s_up=dev_s["up"],
+                        s_down=dev_s["down"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
+    tokens = np.arange(0, T, 4)
+    ex = oracle.Experts(ref_q["gate"], ref_q["up"], ref_q["down"], ref_s["gate"], ref_s["up"],
+                        ref_s["down"], quant_act=True, scale_fmt=fmt)
+    ref = oracle.moe_forward(x[tokens], ex, ids_ref[tokens], w_ref[tokens])
+    assert_close_rel_max(out_to_f64(res.out)[tokens], ref, 6e-2, "mixtral fp8 decode %s" % fmt)
