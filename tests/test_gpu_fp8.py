@@ -237,3 +237,36 @@ def test_mixtral_fp8_decode_full_sampled(fmt):
                         ref_s["down"], quant_act=True, scale_fmt=fmt)
     ref = oracle.moe_forward(x[tokens], ex, ids_ref[tokens], w_ref[tokens])
     assert_close_rel_max(out_to_f64(res.out)[tokens], ref, 6e-2, "mixtral fp8 decode %s" % fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_act_edge_groups_bit_exact(fmt):
+    # groups that stress the scale rule: all zero (with -0), amax exactly 448 * 2^e and one ulp
+    # above, fp32 subnormals (the UE8M0 byte clamps at 0), values near the fp32 maximum, a single
+    # non-zero element, alternating signs
+    rng = np.random.default_rng(17)
+    rows = []
+    z = np.zeros(128, np.float32)
+    z[::3] = -0.0
+    rows.append(z)
+    for e in (-20, 0, 7):
+        b = np.full(128, np.float32(448.0 * 2.0 ** e) / 3, np.float32)
+        b[5] = np.float32(448.0 * 2.0 ** e)
+        rows.append(b)
+        c = b.copy()
+        c[5] = np.nextafter(np.float32(448.0 * 2.0 ** e), np.float32(np.inf))
+        rows.append(c)
+    rows.append((rng.standard_normal(128) * 1e-41).astype(np.float32))   # subnormal
+    rows.append((rng.standard_normal(128) * 1e37).astype(np.float32))    # near the top
+    one = np.zeros(128, np.float32)
+    one[77] = np.float32(-3.25)
+    rows.append(one)
+    rows.append(np.where(np.arange(128) % 2 == 0, 1.0, -1.0).astype(np.float32) * 0.01)
+    rows.append(rng.standard_normal(128).astype(np.float32))
+    assert len(rows) % 2 == 0
+    x = np.stack(rows).reshape(-1, 256)
+    q, s = moe.fp8_quantize_act(to_dev(x), scale_fmt=fmt)
+    torch.cuda.synchronize()
+    qr, sr = oracle.quantize_act(x, scale_fmt=fmt)
+    np.testing.assert_array_equal(to_host(s), sr)
+    np.testing.assert_array_equal(to_host(q), qr)
