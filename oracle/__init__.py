@@ -19,7 +19,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, E2M1 = 0, 1, 2, 3
 SCALE_FMTS = {"f32": 0, "ue8m0": 1}   # block scales: fp32 values, or UE8M0 bytes (2^(b-127))
 
 
@@ -47,6 +47,12 @@ def _load():
         lib.oracle_e4m3_value.restype = ctypes.c_double
         lib.oracle_e4m3_encode.argtypes = [f32]
         lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_value.restype = ctypes.c_double
+        lib.oracle_e2m1_encode.argtypes = [f32]
+        lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+        lib.oracle_quantize_weight_mxfp4.argtypes = [vp, i32, i32, vp, vp]
+        lib.oracle_quantize_weight_mxfp4.restype = None
         lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         lib.oracle_e8m0_value.restype = ctypes.c_double
         lib.oracle_ue8m0_scale.argtypes = [f32]
@@ -120,6 +126,39 @@ def ue8m0_scale(amax: float) -> int:
 def e8m0_decode_array(b: np.ndarray) -> np.ndarray:
     table = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
     return table[np.asarray(b, dtype=np.uint8)]
+
+
+def e2m1_value(code: int) -> float:
+    return _load().oracle_e2m1_value(code)
+
+
+def e2m1_encode(v: float) -> int:
+    return _load().oracle_e2m1_encode(v)
+
+
+def e2m1_decode_packed(q: np.ndarray) -> np.ndarray:
+    """Packed FP4 [..., K/2] bytes -> float64 [..., K] (element 2j in the low nibble of byte j)."""
+    table = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+    q = np.asarray(q, dtype=np.uint8)
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), np.float64)
+    out[..., 0::2] = table[q & 0xF]
+    out[..., 1::2] = table[q >> 4]
+    return out
+
+
+def quantize_weight_mxfp4(W: np.ndarray):
+    """W [..., N, K] fp32 -> (q [..., N, K/2] packed e2m1, s [..., N, K/32] UE8M0 bytes)."""
+    W = _c(W, np.float32)
+    lead, (N, K) = W.shape[:-2], W.shape[-2:]
+    assert K % 32 == 0
+    Wf = W.reshape(-1, N, K)
+    q = np.empty((Wf.shape[0], N, K // 2), np.uint8)
+    s = np.empty((Wf.shape[0], N, K // 32), np.uint8)
+    lib = _load()
+    for e in range(Wf.shape[0]):
+        lib.oracle_quantize_weight_mxfp4(Wf[e].ctypes.data, N, K, q[e].ctypes.data,
+                                         s[e].ctypes.data)
+    return q.reshape(lead + (N, K // 2)), s.reshape(lead + (N, K // 32))
 
 
 def scale_values(s: np.ndarray, scale_fmt: str = "f32") -> np.ndarray:
@@ -215,18 +254,22 @@ class Experts:
     """
 
     def __init__(self, w_gate, w_up, w_down, s_gate=None, s_up=None, s_down=None,
-                 quant_act=False, scale_fmt="f32"):
+                 quant_act=False, scale_fmt="f32", w_fp4=False):
         self.w_gate, self.w_up, self.w_down = _c(w_gate), _c(w_up), _c(w_down)
         self.E, self.f, self.d = self.w_gate.shape
+        if w_fp4:  # packed FP4: two input channels per byte, MX scales [.., rows, cols/32]
+            self.d *= 2
+            assert self.w_down.shape == (self.E, self.d, self.f // 2) and scale_fmt == "ue8m0"
+        else:
+            assert self.w_down.shape == (self.E, self.d, self.f)
         assert self.w_up.shape == self.w_gate.shape
-        assert self.w_down.shape == (self.E, self.d, self.f)
-        self.w_dtype = _dtype_code(self.w_gate)
+        self.w_dtype = E2M1 if w_fp4 else _dtype_code(self.w_gate)
         self.scale_fmt = scale_fmt
         sdt = np.uint8 if scale_fmt == "ue8m0" else np.float32
         self.s_gate = None if s_gate is None else _c(s_gate, sdt)
         self.s_up = None if s_up is None else _c(s_up, sdt)
         self.s_down = None if s_down is None else _c(s_down, sdt)
-        if self.w_dtype == E4M3:
+        if self.w_dtype in (E4M3, E2M1):
             assert self.s_gate is not None and self.s_up is not None and self.s_down is not None
         self.quant_act = bool(quant_act)
 

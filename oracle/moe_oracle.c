@@ -35,14 +35,20 @@
  *     scale is a power of two stored as one float8_e8m0fnu byte b (value 2^(b-127)). The pages give
  *     no rule for choosing it; here the scale of a group is the smallest power of two 2^e with
  *     448 * 2^e >= amax (so no code saturates; e = 0 for an all-zero group), for weight blocks and
- *     for the dynamic activation groups alike, and codes are E4M3(v * 2^-e), an exact scaling.
+ *     for the dynamic activation groups alike, and codes are E4M3(v * 2^-e), an exact scaling;
+ *   - FP4 expert weights (p1 backends notes and p2 "UE8M0 scale format": FP4 experts packed two per
+ *     int8 with UE8M0 weight scales; no block size is given): OCP E2M1 (1 sign, 2 exponent bits,
+ *     bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), element 2j in the low nibble of byte j,
+ *     one UE8M0 scale per 32 consecutive input channels of a row (the MX block), chosen as the
+ *     smallest power of two 2^e with 6 * 2^e >= amax, codes E2M1(v * 2^-e) to nearest, ties to
+ *     the even code; activations keep the fp8 rule with UE8M0 scales.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_E4M3 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_E4M3 = 2, ORACLE_E2M1 = 3 };
 
 /* ---------------------------------------------------------------------------------------------
  * Number formats
@@ -99,10 +105,47 @@ uint8_t oracle_e4m3_encode(float v) {
   return sign | (uint8_t)code; /* values that round to zero keep their sign (-0 is 0x80) */
 }
 
+/* OCP E2M1 (FP4): code bits s e e m; exponent field 0 encodes 0 and 0.5 (m * 0.5), otherwise
+ * 2^(e-1) * (1 + m/2): 1, 1.5, 2, 3, 4, 6. */
+double oracle_e2m1_value(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* Nearest E2M1 code to v (ties to the even code), |v| beyond 6 saturating to 6. */
+uint8_t oracle_e2m1_encode(float v) {
+  double a = fabs((double)v);
+  uint8_t sign = signbit(v) ? 0x8 : 0x0;
+  if (a >= 6.0) return sign | 0x7;
+  int lo = 0, hi = 7; /* invariant: value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (oracle_e2m1_value((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  double dlo = a - oracle_e2m1_value((uint8_t)lo);
+  double dhi = oracle_e2m1_value((uint8_t)hi) - a;
+  int code;
+  if (dlo < dhi)
+    code = lo;
+  else if (dhi < dlo)
+    code = hi;
+  else
+    code = (lo % 2 == 0) ? lo : hi; /* tie: even mantissa */
+  return sign | (uint8_t)code;
+}
+
 static double load_value(const void* p, int dtype, size_t i) {
   switch (dtype) {
     case ORACLE_F32: return (double)((const float*)p)[i];
     case ORACLE_BF16: return oracle_bf16_value(((const uint16_t*)p)[i]);
+    case ORACLE_E2M1: {
+      uint8_t byte = ((const uint8_t*)p)[i / 2];
+      return oracle_e2m1_value((i & 1) ? (byte >> 4) : (byte & 0xF));
+    }
     default: return oracle_e4m3_value(((const uint8_t*)p)[i]);
   }
 }
@@ -296,6 +339,37 @@ void oracle_quantize_weight_ue8m0(const float* W, int N, int K, int block, uint8
   }
 }
 
+/* FP4 (MXFP4) weights: W [N, K] fp32 -> q [N, K/2] bytes (element 2j in the low nibble of byte j),
+ * s [N, K/32] UE8M0 bytes: per row and block of 32, b = the byte of the smallest power of two 2^e
+ * with 6 * 2^e >= amax (127 for an all-zero block), codes E2M1(v * 2^-e). K % 32 == 0. */
+void oracle_quantize_weight_mxfp4(const float* W, int N, int K, uint8_t* q, uint8_t* s) {
+  int KB = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    for (int kb = 0; kb < KB; ++kb) {
+      const float* v = W + (size_t)n * K + (size_t)kb * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i)
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+      int b = 127;
+      if (amax > 0.0f) {
+        int e = (int)ceil(log2((double)amax / 6.0));
+        while (ldexp(6.0, e) < (double)amax) ++e;
+        while (ldexp(6.0, e - 1) >= (double)amax) --e;
+        b = e + 127;
+        if (b < 0) b = 0;
+        if (b > 254) b = 254;
+      }
+      float inv = ldexpf(1.0f, 127 - b);
+      for (int i = 0; i < 32; i += 2) {
+        uint8_t lo = oracle_e2m1_encode(v[i] * inv), hi = oracle_e2m1_encode(v[i + 1] * inv);
+        q[(size_t)n * (K / 2) + (size_t)kb * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+      }
+      s[(size_t)n * KB + kb] = (uint8_t)b;
+    }
+  }
+}
+
 /* ---------------------------------------------------------------------------------------------
  * Experts (gated MLP with SwiGLU) and the weighted combine (p1 intro; p4 section 5)
  * ------------------------------------------------------------------------------------------- */
@@ -321,6 +395,8 @@ static double weight_value(const void* w, const void* s, int scale_fmt, int dtyp
   if (dtype == ORACLE_E4M3) {
     int CB = C / 128;
     v *= scale_value(s, scale_fmt, ((size_t)e * (R / 128) + r / 128) * CB + c / 128);
+  } else if (dtype == ORACLE_E2M1) { /* MX scales: one byte per row per 32 columns */
+    v *= oracle_e8m0_value(((const uint8_t*)s)[((size_t)e * R + r) * (C / 32) + c / 32]);
   }
   return v;
 }
