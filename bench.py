@@ -80,7 +80,9 @@ class Layer:
         Wg, Wu, Wd = W
         self.keep = [x, Wg, Wu, Wd, logits, Wr, scales]
         act = moe.MOE_F32 if spec.dtype == "f32" else moe.MOE_BF16
-        wdt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3}[spec.dtype]
+        wdt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3,
+               "fp4": moe.MOE_FP4_E2M1}[spec.dtype]
+        lowp = spec.dtype in ("fp8", "fp4")   # e4m3 activations with block scales
         ydt = moe.MOE_F32 if spec.dtype == "f32" else moe.MOE_BF16
         tdt = torch.float32 if ydt == moe.MOE_F32 else torch.bfloat16
         self.logits = logits if logits is not None else torch.empty((T, E), dtype=torch.float32,
@@ -93,7 +95,7 @@ class Layer:
         self.pp = torch.empty(P, dtype=torch.int32, device=dev)
         pw = self.lib.moe_permute_workspace_size(T, k, E)
         self.pws = torch.empty(max(pw, 1), dtype=torch.uint8, device=dev)
-        xact = moe.MOE_FP8_E4M3 if spec.dtype == "fp8" else act
+        xact = moe.MOE_FP8_E4M3 if lowp else act
         ew = self.lib.moe_experts_workspace_size(T, d, f, E, k, xact, wdt)
         self.ews = torch.empty(ew, dtype=torch.uint8, device=dev)
         self.y = torch.empty((T, k, d), dtype=tdt, device=dev)
@@ -106,7 +108,7 @@ class Layer:
         x_in, xs = x, None
         ue = scale_fmt == "ue8m0"
         self._quant_fn = self.lib.fp8_quantize_act_ue8m0 if ue else self.lib.fp8_quantize_act
-        if spec.dtype == "fp8":
+        if lowp:
             self.xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
             self.xs = torch.empty((T, d // 128), dtype=torch.uint8 if ue else torch.float32,
                                   device=dev)
@@ -262,16 +264,21 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
     return r
 
 
-def measure_decode_fp8(moe, synth, W, Wr, steps, warmup, scale_fmt):
+def measure_decode_fp8(moe, synth, W, Wr, steps, warmup, scale_fmt, fp4=False):
     """The Mixtral-shaped decode layer with its bf16 weights quantised to e4m3 (128x128 blocks,
-    fp32 or UE8M0 scales) on the device: the weight-streaming fp8 kernels."""
+    fp32 or UE8M0 scales), or with fp4=True to E2M1 with MX scales (one e8m0 byte per row per 32
+    channels), on the device: the weight-streaming kernels."""
     import torch
-    dspec = synth.MIXTRAL_DECODE.with_(dtype="fp8")
-    name = "mixtral_decode_fp8_T%d_d%d_f%d_E%d_k%d%s" % (
-        dspec.T, dspec.d, dspec.f, dspec.E, dspec.k, "_ue8m0" if scale_fmt == "ue8m0" else "")
+    dspec = synth.MIXTRAL_DECODE.with_(dtype="fp4" if fp4 else "fp8")
+    name = "mixtral_decode_%s_T%d_d%d_f%d_E%d_k%d%s" % (
+        "fp4" if fp4 else "fp8", dspec.T, dspec.d, dspec.f, dspec.E, dspec.k,
+        "_mx" if fp4 else ("_ue8m0" if scale_fmt == "ue8m0" else ""))
     Q, S = [], []
     for w in W:
-        q, s_ = moe.fp8_quantize_weight(w, scale_fmt=scale_fmt)
+        if fp4:
+            q, s_ = moe.fp4_quantize_weight_mx(w)
+        else:
+            q, s_ = moe.fp8_quantize_weight(w, scale_fmt=scale_fmt)
         Q.append(q)
         S.append(s_)
     xd = torch.from_numpy(synth.gen_x(synth.MIXTRAL_DECODE).view("int16")).cuda().view(torch.bfloat16)
@@ -280,13 +287,15 @@ def measure_decode_fp8(moe, synth, W, Wr, steps, warmup, scale_fmt):
     g1, g2 = layer.kernel_ms(steps)
     touched = int((layer.counts.cpu().numpy() > 0).sum())
     ms = el / steps * 1e3
-    wb = touched * 3 * dspec.d * dspec.f
+    per_w = 0.5 + 1 / 32 if fp4 else 1.0   # streamed bytes per weight (E2M1 codes + MX scales)
+    wb = touched * 3 * dspec.d * dspec.f * per_w
     r = {"workload": name, "ms_per_step": round(ms, 4),
          "tokens_per_s": round(dspec.T / (ms * 1e-3), 1),
          "gate_up_ms": round(g1, 4), "down_ms": round(g2, 4),
-         "gate_up_weight_GBps": round(touched * 2 * dspec.d * dspec.f / (g1 * 1e-3) / 1e9, 1),
+         "gate_up_weight_GBps": round(touched * 2 * dspec.d * dspec.f * per_w / (g1 * 1e-3) / 1e9,
+                                      1),
          "weight_GBps_layer": round(wb / (ms * 1e-3) / 1e9, 1), "experts_touched": touched}
-    log("%s: %.3f ms/step, %.0f tokens/s; gate/up %.3f ms (%.0f GB/s of e4m3 weights), down "
+    log("%s: %.3f ms/step, %.0f tokens/s; gate/up %.3f ms (%.0f GB/s of weights), down "
         "%.3f ms (incl. h quantisation)" % (name, ms, r["tokens_per_s"], g1,
                                             r["gate_up_weight_GBps"], g2))
     del layer, Q, S
@@ -436,6 +445,8 @@ def main():
         for fmt in ("f32", "ue8m0"):
             rep.append(measure_decode_fp8(moe, synth, (Wg, Wu, Wd), Wr, max(args.decode_steps, 5),
                                           5, fmt))
+        rep.append(measure_decode_fp8(moe, synth, (Wg, Wu, Wd), Wr, max(args.decode_steps, 5), 5,
+                                      "ue8m0", fp4=True))
         del Wg, Wu, Wd
         torch.cuda.empty_cache()
         for spec_o, fmt in ((synth.SKEWED_128E, "f32"), (synth.DSV3_FP8, "f32"),

@@ -53,7 +53,9 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,       /* IEEE binary32 */
   MOE_BF16 = 1,      /* bfloat16 */
-  MOE_FP8_E4M3 = 2   /* OCP E4M3FN: bias 7, max 448, no infinities */
+  MOE_FP8_E4M3 = 2,  /* OCP E4M3FN: bias 7, max 448, no infinities */
+  MOE_FP4_E2M1 = 3   /* OCP E2M1 (0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte: element 2j in the
+                        low nibble of byte j; expert weights only, with MX scales (below) */
 } moe_dtype;
 
 /* Format of fp8 block scales (Transformers "Fine-grained FP8" page, section "UE8M0 scale
@@ -172,6 +174,22 @@ moe_status fp8_quantize_weight_ue8m0(const void* w, moe_dtype w_dtype, int batch
                                      int block, uint8_t* q, uint8_t* scales, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * fp4_quantize_weight_mx - expert weights to FP4 E2M1 with MX block scales (Transformers
+ * "Experts backends" page, notes on FP8 and FP4 quantised experts packed as int8 with UE8M0 or
+ * float32 scales; "Fine-grained FP8" page, section "UE8M0 scale format": FP4 experts with UE8M0
+ * weight scales).
+ *
+ *  w       [batch, N, K] of w_dtype (MOE_F32 or MOE_BF16).
+ *  q       [batch, N, K/2] packed E2M1 out; scales [batch, N, K/32] e8m0 bytes out: one per row
+ *          per 32 consecutive input channels.
+ *  Per block: b is the byte of the smallest power of two 2^e with 6 * 2^e >= amax (127 for an
+ *  all-zero block, clamped to 0..254), codes E2M1(v * 2^-e) to nearest, ties to the even code.
+ *  K % 32 == 0 (MOE_ERR_UNSUPPORTED otherwise); bad pointers or sizes: MOE_ERR_INVALID_ARGUMENT.
+ * ------------------------------------------------------------------------------------------ */
+moe_status fp4_quantize_weight_mx(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                                  uint8_t* q, uint8_t* scales, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_experts_forward - both grouped projections of every selected expert.
  * (Transformers "Experts backends" page: introduction and backends table rows grouped_mm,
  * deepgemm_megamoe, sonicmoe; the decode-time switch to a small-batch kernel; AWS fused-MoE news
@@ -195,6 +213,12 @@ moe_status fp8_quantize_weight_ue8m0(const void* w, moe_dtype w_dtype, int batch
  *        applies them as its per-row / per-column block scales (no promotion step) and h is
  *        re-quantised with UE8M0 scales. scale_fmt other than MOE_SCALE_F32 on a non-fp8 path,
  *        or an unknown value, is MOE_ERR_INVALID_ARGUMENT.
+ *    FP8_E4M3 / FP4_E2M1 / BF16 or F32, scale_fmt = MOE_SCALE_UE8M0 (MOE_SCALE_F32 is
+ *        MOE_ERR_UNSUPPORTED)
+ *        weights packed E2M1 [E, f, d/2] and [E, d, f/2] (from fp4_quantize_weight_mx) with MX
+ *        scales s_gate / s_up [E, f, d/32] and s_down [E, d, f/32]; x and h e4m3 with UE8M0
+ *        per-128 scales. Weight-streaming kernels only: P <= 256, otherwise
+ *        MOE_ERR_UNSUPPORTED. d % 128 == f % 128 == 0.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int T, d, f, E, k;

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, \
     MOE_ERR_DEVICE = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1 = range(4)
 MOE_Y_PERMUTED, MOE_Y_SLOTS, MOE_Y_ACC_F32 = range(3)
 
 _LAYOUTS = {"permuted": MOE_Y_PERMUTED, "slots": MOE_Y_SLOTS, "acc_f32": MOE_Y_ACC_F32}
@@ -30,7 +30,7 @@ _LAYOUTS = {"permuted": MOE_Y_PERMUTED, "slots": MOE_Y_SLOTS, "acc_f32": MOE_Y_A
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_route", "moe_permute", "moe_permute_workspace_size",
     "fp8_quantize_act", "fp8_quantize_weight", "fp8_quantize_act_ue8m0",
-    "fp8_quantize_weight_ue8m0", "moe_experts_forward",
+    "fp8_quantize_weight_ue8m0", "fp4_quantize_weight_mx", "moe_experts_forward",
     "moe_experts_workspace_size", "moe_combine", "moe_event_create", "moe_event_destroy",
     "moe_event_record", "moe_event_elapsed_ms",
 )
@@ -85,6 +85,7 @@ def load_library(path: str = LIB_PATH):
         "fp8_quantize_weight": ([vp, i32, i32, i32, i32, i32, vp, vp, vp], st),
         "fp8_quantize_act_ue8m0": ([vp, i32, i32, i32, i32, vp, vp, vp, vp], st),
         "fp8_quantize_weight_ue8m0": ([vp, i32, i32, i32, i32, i32, vp, vp, vp], st),
+        "fp4_quantize_weight_mx": ([vp, i32, i32, i32, i32, vp, vp, vp], st),
         "moe_experts_forward": ([ctypes.POINTER(moe_experts_args), vp], st),
         "moe_experts_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "moe_combine": ([vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp], st),
@@ -240,6 +241,22 @@ def fp8_quantize_weight(w: torch.Tensor, block: int = 128, scale_fmt: str = "f32
     return q, s
 
 
+def fp4_quantize_weight_mx(w: torch.Tensor):
+    """E2M1 quantisation of [batch, N, K] (or [N, K]) weights with one e8m0 scale per row per 32
+    input channels. Returns (q uint8 [..., N, K/2] packed, element 2j in the low nibble of byte
+    j; scales uint8 [..., N, K/32])."""
+    lib = load_library()
+    _contig(w)
+    shape = w.shape
+    batch = 1 if w.dim() == 2 else int(torch.tensor(shape[:-2]).prod())
+    N, K = shape[-2], shape[-1]
+    q = torch.empty(tuple(shape[:-1]) + (max(K // 2, 1),), dtype=torch.uint8, device=w.device)
+    s = torch.empty(tuple(shape[:-1]) + (max(K // 32, 1),), dtype=torch.uint8, device=w.device)
+    _check(lib.fp4_quantize_weight_mx(_ptr(w), _dtype_code(w), batch, N, K, _ptr(q), _ptr(s),
+                                      _stream()))
+    return q, s
+
+
 def experts_workspace_bytes(T, d, f, E, k, act_dtype: int, w_dtype: int) -> int:
     return load_library().moe_experts_workspace_size(T, d, f, E, k, act_dtype, w_dtype)
 
@@ -247,10 +264,11 @@ def experts_workspace_bytes(T, d, f, E, k, act_dtype: int, w_dtype: int) -> int:
 def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k: int,
                         y_layout: str = "slots", y_dtype=None, x_scales=None, s_gate=None,
                         s_up=None, s_down=None, y=None, workspace=None, events=None,
-                        scale_fmt: str = "f32"):
+                        scale_fmt: str = "f32", w_fp4: bool = False):
     """Both grouped projections. Returns y in ``y_layout`` ("permuted" [P,d], "slots" [T,k,d],
     "acc_f32" [T,d] fp32). ``events``: optional 4 event handles (see moe_event_create).
-    ``scale_fmt``: fp8 block scales as fp32 values ("f32") or e8m0 bytes ("ue8m0")."""
+    ``scale_fmt``: fp8 block scales as fp32 values ("f32") or e8m0 bytes ("ue8m0").
+    ``w_fp4``: the uint8 weights are packed E2M1 (from fp4_quantize_weight_mx) with MX scales."""
     lib = load_library()
     for t in (x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, x_scales, s_gate, s_up,
               s_down):
@@ -259,6 +277,10 @@ def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k
     E, f, _ = w_gate.shape
     act = _dtype_code(x)
     wdt = _dtype_code(w_gate)
+    if w_fp4:
+        if w_gate.dtype != torch.uint8 or 2 * w_gate.shape[2] != d:
+            raise ValueError("E2M1 weights are uint8 [E, f, d/2]")
+        wdt = MOE_FP4_E2M1
     layout = _LAYOUTS[y_layout]
     if y_dtype is None:
         y_dtype = torch.float32 if act == MOE_F32 else torch.bfloat16
@@ -335,11 +357,13 @@ class LayerResult:
 
 
 def moe_layer(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, y_layout="slots",
-              s_gate=None, s_up=None, s_down=None, out_dtype=None, events=None) -> LayerResult:
+              s_gate=None, s_up=None, s_down=None, out_dtype=None, events=None,
+              w_fp4: bool = False) -> LayerResult:
     """route -> permute -> (fp8: quantise x) -> experts -> combine, all on the device.
 
     For fp8 weights (uint8 e4m3 codes with block scales s_*), x is given in bf16/fp32 and quantised
-    per token per 128 channels here; uint8 scales select the UE8M0 scale format.
+    per token per 128 channels here; uint8 scales select the UE8M0 scale format. ``w_fp4``:
+    packed E2M1 weights with MX scales (e4m3 activations, UE8M0 scales).
     """
     E = w_gate.shape[0]
     T, d = x.shape
@@ -356,7 +380,7 @@ def moe_layer(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, y_lay
                             y_layout=y_layout, x_scales=xs, s_gate=s_gate, s_up=s_up,
                             s_down=s_down, events=events,
                             y_dtype=torch.float32 if out_dtype == torch.float32 else None,
-                            scale_fmt=fmt)
+                            scale_fmt=fmt, w_fp4=w_fp4)
     out = moe_combine(y, y_layout, T, k, d, pair_pos=perm.pair_pos, topk_w=w,
                       out_dtype=out_dtype)
     return LayerResult(out, ids, w, lg, perm)

@@ -41,9 +41,12 @@ inline bool uses_decode(moe_dtype act, moe_dtype w, long long P, int d, int f) {
          f % 128 == 0;
 }
 
-// fp8 layers with few pairs take the weight-streaming fp8 kernels.
+// 8-bit activation codes with e4m3 or E2M1 weights (block scales, fp8 quantisation of x and h)
+inline bool is_low_precision(moe_dtype w) { return w == MOE_FP8_E4M3 || w == MOE_FP4_E2M1; }
+
+// fp8 layers with few pairs take the weight-streaming fp8 kernels (the only E2M1 kernels).
 inline bool uses_fp8_decode(moe_dtype act, moe_dtype w, long long P) {
-  return act == MOE_FP8_E4M3 && w == MOE_FP8_E4M3 && P <= kDecodeMaxPairs;
+  return act == MOE_FP8_E4M3 && is_low_precision(w) && P <= kDecodeMaxPairs;
 }
 
 // bf16 tiled GEMMs cut their tail tiles; they need partial-tile slots and counters.
@@ -64,13 +67,14 @@ ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, m
   L.cum_b = off;
   off = align_up(off + (E + 1) * sizeof(int32_t));
   L.h = off;
-  const size_t h_elem = (w == MOE_FP8_E4M3) ? 1 : (act == MOE_F32 ? 4 : 2);
+  const size_t h_elem = is_low_precision(w) ? 1 : (act == MOE_F32 ? 4 : 2);
   off = align_up(off + P * f * h_elem);
   L.h_scales = off;
-  if (w == MOE_FP8_E4M3) off = align_up(off + P * (f / kFp8Group) * sizeof(float));
+  if (is_low_precision(w)) off = align_up(off + P * (f / kFp8Group) * sizeof(float));
   // fp8 with UE8M0 scales: x_scales expanded from e8m0 bytes to fp32 values
   L.x_scales = off;
-  if (w == MOE_FP8_E4M3) off = align_up(off + static_cast<size_t>(T) * (d / kFp8Group) * sizeof(float));
+  if (is_low_precision(w))
+    off = align_up(off + static_cast<size_t>(T) * (d / kFp8Group) * sizeof(float));
   // fp8 decode: fp32 h before its quantisation, and its e8m0 scale bytes
   L.h32 = L.h_scale_bytes = 0;
   if (uses_fp8_decode(act, w, static_cast<long long>(P))) {
@@ -235,6 +239,17 @@ moe_status fp8_quantize_weight_ue8m0(const void* w, moe_dtype w_dtype, int batch
   return dev(launch_quantize_weight(w, w_dtype, batch, N, K, q, scales, true, stream));
 }
 
+moe_status fp4_quantize_weight_mx(const void* w, moe_dtype w_dtype, int batch, int N, int K,
+                                  uint8_t* q, uint8_t* scales, hipStream_t stream) {
+  if (!w || !q || !scales || batch < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!is_float_type(w_dtype)) return MOE_ERR_INVALID_ARGUMENT;
+  if (K % 32) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(q, 16)) return MOE_ERR_UNSUPPORTED;
+  const size_t nblocks = static_cast<size_t>(batch) * N * (K / 32);
+  if (nblocks > (static_cast<size_t>(INT_MAX) << 6)) return MOE_ERR_UNSUPPORTED;
+  return dev(launch_quantize_weight_mx4(w, w_dtype, nblocks, q, scales, stream));
+}
+
 size_t moe_experts_workspace_size(int T, int d, int f, int E, int k, moe_dtype act_dtype,
                                   moe_dtype w_dtype) {
   if (check_topology(T, E, k) != MOE_OK || d < 1 || f < 1) return 0;
@@ -255,7 +270,8 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   const moe_dtype act = a->act_dtype, w = a->w_dtype;
   const bool f32 = act == MOE_F32 && w == MOE_F32;
   const bool bf16 = act == MOE_BF16 && w == MOE_BF16;
-  const bool fp8 = act == MOE_FP8_E4M3 && w == MOE_FP8_E4M3;
+  const bool w4 = act == MOE_FP8_E4M3 && w == MOE_FP4_E2M1;
+  const bool fp8 = (act == MOE_FP8_E4M3 && w == MOE_FP8_E4M3) || w4;
   if (!f32 && !bf16 && !fp8) return MOE_ERR_UNSUPPORTED;
   if (f32 && a->y_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (bf16 && (a->d % 64 || a->f % 64)) return MOE_ERR_UNSUPPORTED;
@@ -269,6 +285,8 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
     if (!a->x_scales || !a->s_gate || !a->s_up || !a->s_down) return MOE_ERR_INVALID_ARGUMENT;
   }
   const long long P = static_cast<long long>(a->T) * a->k;
+  // E2M1 weights: MX scales are e8m0 bytes, and only the weight-streaming kernels take them
+  if (w4 && (!ue8m0 || P > kDecodeMaxPairs)) return MOE_ERR_UNSUPPORTED;
   // 32-bit element offsets inside the kernels
   if (static_cast<long long>(a->T) * a->d > INT_MAX / 2 || P * a->f > INT_MAX / 2 ||
       P * a->d > INT_MAX / 2 || static_cast<long long>(a->f) * a->d > INT_MAX / 4)
@@ -295,6 +313,7 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   X.s_up = a->s_up;
   X.s_down = a->s_down;
   X.scale_ue8m0 = ue8m0 ? 1 : 0;
+  X.w_fp4 = w4 ? 1 : 0;
   X.offsets = a->offsets;
   X.tile_cum_a = reinterpret_cast<int32_t*>(ws + L.cum_a);
   X.tile_cum_b = reinterpret_cast<int32_t*>(ws + L.cum_b);

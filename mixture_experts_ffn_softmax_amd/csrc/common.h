@@ -46,6 +46,27 @@ __device__ __forceinline__ int ue8m0_byte(float amax) {
   return min(254, max(0, e + 127));
 }
 
+// OCP E2M1 (FP4) code of v (|v| rounded to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to
+// the even code, beyond 6 saturating): each threshold adds one code step; at a midpoint the
+// comparison is strict when the lower code is even and inclusive when it is odd.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const float a = fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c | (signbit(v) ? 8u : 0u);
+}
+
+// MX scale byte for E2M1 blocks: the smallest e with 6 * 2^e >= amax (0 -> byte 127), clamped to
+// 0..254. With amax = fr * 2^ex, fr in [0.5, 1), and 6 = 0.75 * 2^3: e = ex - 3, plus one when
+// fr > 0.75.
+__device__ __forceinline__ int mx4_byte(float amax) {
+  if (!(amax > 0.0f)) return 127;
+  const int ex = __builtin_amdgcn_frexp_expf(amax);
+  const float fr = __builtin_amdgcn_frexp_mantf(amax);
+  const int e = ex - 3 + (fr > 0.75f ? 1 : 0);
+  return min(254, max(0, e + 127));
+}
+
 // OCP E4M3FN encode: round to nearest even, saturate to +-448 (0x7E / 0xFE); zero keeps its sign.
 // Normal range: round the fp32 mantissa from 23 to 3 bits with the add-half-minus-one-plus-lsb
 // trick, then rebias the exponent (fp32 bias 127 -> e4m3 bias 7). Below 2^-6 the e4m3 grid is the

@@ -16,6 +16,18 @@
 // passes of 64 tokens; its 4 waves take the 128-wide K blocks in turn and reduce through LDS. The
 // gate/up kernel writes h in fp32, since one 128-channel group of h spans four workgroups; the
 // caller quantises it per (pair, 128 channels) before the down kernel.
+//
+// FP4 experts (Transformers "Experts backends" page, notes on FP4 quantised experts; "Fine-grained
+// FP8" page, "UE8M0 scale format"): weights E2M1, two per byte, with one e8m0 scale per row per 32
+// input channels, against the same e4m3 activations. The instruction takes its A operand as FP4
+// (format code 4: 32 values in the low four registers of each lane) and a scale per lane. Within
+// one 128-wide K block, lane group g (lanes 16g..16g+15) holds K = 32g..32g+31 of an FP4 operand,
+// but of an 8-bit operand K = 16g..16g+15 in its first 16 bytes and 64+16g..64+16g+15 in its last
+// 16 (measured on gfx950); a lane's scale covers K = 32g..32g+31 in both. So each lane passes its
+// own weight block's byte, loaded next to the weights, and the e4m3 activations are fetched as the
+// two 16-byte pieces that line up with the FP4 weights. (Two 8-bit operands share the one layout,
+// and their scales are uniform over the 128-wide block, so the fp8 kernels read K contiguously.)
+// Half the streamed bytes of the fp8 weights.
 #include "common.h"
 #include "launch.h"
 
@@ -34,9 +46,10 @@ struct Fp8DecodeArgs {
   int a_gather;
   const int32_t* sorted_pair;
   int k;
-  const uint8_t* w0;          // W_gate or W_down [E, N, K] e4m3
+  const uint8_t* w0;          // W_gate or W_down [E, N, K] e4m3, or [E, N, K/2] packed E2M1
   const uint8_t* w1;          // W_up
-  const void* s0;             // block scales of w0 [E, N/128, K/128]: fp32, or e8m0 bytes
+  const void* s0;             // block scales of w0 [E, N/128, K/128]: fp32, or e8m0 bytes;
+                              // E2M1: e8m0 bytes [E, N, K/32]
   const void* s1;
   int K, N;
   const int32_t* offsets;
@@ -55,7 +68,25 @@ __device__ __forceinline__ i32x8_t ld32g(const uint8_t* p) {
   return r;
 }
 
-template <int MODE, bool kUE>
+__device__ __forceinline__ i32x8_t ld16x2g(const uint8_t* p, const uint8_t* q) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(q);
+  i32x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+__device__ __forceinline__ i32x8_t ld16g(const uint8_t* p) {
+  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+  i32x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+// kW4: E2M1 weights with per-32 MX scales (implies kUE).
+template <int MODE, bool kUE, bool kW4>
 __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
   const int nrb = (p.N + kRows - 1) / kRows;
@@ -72,7 +103,8 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  const int rowb = kW4 ? p.K / 2 : p.K;   // bytes per weight row
+  const size_t wstride = static_cast<size_t>(p.N) * rowb;
   const int KB = p.K / 128, NB = p.N / 128;
 
   // A rows (4 groups of 16 weight rows); a group lies inside one 128-row scale block.
@@ -92,13 +124,21 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
       base = p.w0 + e * wstride;
       sbase = p.s0;
     }
-    const int nb = min(n, p.N - 1) / 128;
-    const size_t sidx = (static_cast<size_t>(e) * NB + nb) * KB;
-    ascale[rg] = kUE ? static_cast<const void*>(static_cast<const uint8_t*>(sbase) + sidx)
-                     : static_cast<const void*>(static_cast<const float*>(sbase) + sidx);
-    arow[rg] = base + static_cast<size_t>(min(n + r16, p.N - 1)) * p.K + g * 32;
+    const int row = min(n + r16, p.N - 1);
+    if constexpr (kW4) {
+      // this lane's row, its 32-wide block g of the first 128-wide K block
+      ascale[rg] = static_cast<const uint8_t*>(sbase) +
+                   (static_cast<size_t>(e) * p.N + row) * (p.K / 32) + g;
+      arow[rg] = base + static_cast<size_t>(row) * rowb + g * 16;
+    } else {
+      const int nb = min(n, p.N - 1) / 128;
+      const size_t sidx = (static_cast<size_t>(e) * NB + nb) * KB;
+      ascale[rg] = kUE ? static_cast<const void*>(static_cast<const uint8_t*>(sbase) + sidx)
+                       : static_cast<const void*>(static_cast<const float*>(sbase) + sidx);
+      arow[rg] = base + static_cast<size_t>(row) * rowb + g * 32;
+    }
   }
-  if constexpr (kUE) {
+  if constexpr (kUE && !kW4) {
     for (int i = tid; i < 4 * KB; i += 256)
       wsb[i / KB][i % KB] = static_cast<const uint8_t*>(ascale[i / KB])[i % KB];
     __syncthreads();
@@ -113,7 +153,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
       const int ti = min(tc0 + tg * 16 + r16, M - 1);
       const int pos = row0 + ti;
       const int src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
-      brow[tg] = p.a + static_cast<size_t>(src) * p.K + g * 32;
+      brow[tg] = p.a + static_cast<size_t>(src) * p.K + (kW4 ? g * 16 : g * 32);
       bscale[tg] = p.a_s + static_cast<size_t>(src) * KB;
     }
     f32x4_t acc[4][4];
@@ -126,12 +166,20 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
       const int kb = c * 128;
       i32x8_t av[4], bv[4];
       float bs[4];
+      int ewl[4];   // E2M1: each lane's own block scale byte
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) av[rg] = ld32g(arow[rg] + kb);
+      for (int rg = 0; rg < 4; ++rg) {
+        if constexpr (kW4) {
+          av[rg] = ld16g(arow[rg] + kb / 2);
+          ewl[rg] = static_cast<const uint8_t*>(ascale[rg])[c * 4];
+        } else {
+          av[rg] = ld32g(arow[rg] + kb);
+        }
+      }
 #pragma unroll
       for (int tg = 0; tg < 4; ++tg)
         if (tg < ntg) {
-          bv[tg] = ld32g(brow[tg] + kb);
+          bv[tg] = kW4 ? ld16x2g(brow[tg] + kb, brow[tg] + kb + 64) : ld32g(brow[tg] + kb);
           bs[tg] = bscale[tg][c];
         }
 #pragma unroll
@@ -144,9 +192,9 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
           const int ex = (__float_as_uint(bs[tg]) >> 23) & 0xFF;
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const int ew = wsb[rg][c];
+            const int ew = kW4 ? ewl[rg] : wsb[rg][c];
             acc[rg][tg] += __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                av[rg], bv[tg], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, ew, 0, ex);
+                av[rg], bv[tg], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, kW4 ? 4 : 0, 0, 0, ew, 0, ex);
           }
         } else {
 #pragma unroll
@@ -226,11 +274,12 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
 }
 
 template <int MODE>
-hipError_t launch_one(const Fp8DecodeArgs& a, int E, bool ue, hipStream_t stream) {
+hipError_t launch_one(const Fp8DecodeArgs& a, int E, bool ue, bool w4, hipStream_t stream) {
   constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
   const dim3 grid(static_cast<unsigned>(E * ((a.N + kRows - 1) / kRows))), block(256);
-  if (ue) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((decode_fp8_kernel<MODE, false>), grid, block, 0, stream, a);
+  if (w4) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, true>), grid, block, 0, stream, a);
+  else if (ue) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, false>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((decode_fp8_kernel<MODE, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -253,8 +302,10 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   g.offsets = L.offsets;
   g.h32 = L.h32;
   const bool ue = L.scale_ue8m0 != 0;
+  const bool w4 = L.w_fp4 != 0;
+  if (w4 && !ue) return hipErrorNotSupported;   // MX scales are e8m0 bytes
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipError_t e = launch_one<kGateUp>(g, L.E, ue, stream);
+  hipError_t e = launch_one<kGateUp>(g, L.E, ue, w4, stream);
   if (e != hipSuccess) return e;
   // h -> e4m3 codes with per-(pair, 128-channel) scales, as fp32 values for the down kernel
   uint8_t* hq = static_cast<uint8_t*>(L.h);
@@ -285,7 +336,7 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  e = launch_one<kDown>(dn, L.E, ue, stream);
+  e = launch_one<kDown>(dn, L.E, ue, w4, stream);
   if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return e;
 }

@@ -27,6 +27,9 @@ hipError_t launch_quantize_act(const void* x, moe_dtype x_dtype, int M, int K,
                                hipStream_t stream);
 hipError_t launch_quantize_weight(const void* w, moe_dtype w_dtype, int batch, int N, int K,
                                   uint8_t* q, void* scales, bool ue8m0, hipStream_t stream);
+// FP4 E2M1 weights with MX scales: nblocks 32-element blocks (rows * K / 32)
+hipError_t launch_quantize_weight_mx4(const void* w, moe_dtype w_dtype, size_t nblocks,
+                                      uint8_t* q, uint8_t* scales, hipStream_t stream);
 // e8m0 bytes -> fp32 values 2^(b - 127)
 hipError_t launch_e8m0_expand(const uint8_t* b, size_t n, float* out, hipStream_t stream);
 
@@ -57,6 +60,7 @@ struct ExpertsLaunch {
   const void* s_up;
   const void* s_down;
   int scale_ue8m0;            // fp8: UE8M0 scales, applied by the block-scaled MFMA
+  int w_fp4;                  // weights packed E2M1 with MX scales [E, rows, cols/32]
   const int32_t* offsets;
   const int32_t* tile_cum_a;  // row tiles of the gate/up GEMM
   const int32_t* tile_cum_b;  // row tiles of the down GEMM

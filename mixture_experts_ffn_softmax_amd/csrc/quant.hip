@@ -133,6 +133,37 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const WT* __restri
   }
 }
 
+// FP4 with MX scales: one thread per 32-element block of a row (packed 16 bytes + a scale byte).
+template <typename WT>
+__global__ __launch_bounds__(256) void quantize_weight_mx4_kernel(const WT* __restrict__ w,
+                                                                  size_t nblocks,
+                                                                  uint8_t* __restrict__ q,
+                                                                  uint8_t* __restrict__ scales) {
+  const size_t blk = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (blk >= nblocks) return;
+  const WT* src = w + blk * 32;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if constexpr (sizeof(WT) == 2) v[i] = bf16_bits_to_f32(src[i]);
+    else v[i] = src[i];
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const int b = mx4_byte(amax);
+  const float inv = ldexpf(1.0f, 127 - b);
+  u32x4_t o;
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) word |= e2m1_encode(v[wd * 8 + j] * inv) << (4 * j);
+    o[wd] = word;
+  }
+  *reinterpret_cast<u32x4_t*>(q + blk * 16) = o;
+  scales[blk] = static_cast<uint8_t>(b);
+}
+
 // e8m0 bytes -> their fp32 values 2^(b - 127) (exact).
 __global__ __launch_bounds__(256) void e8m0_expand_kernel(const uint8_t* __restrict__ b, size_t n,
                                                           float* __restrict__ out) {
@@ -182,6 +213,18 @@ hipError_t launch_quantize_weight(const void* w, moe_dtype w_dtype, int batch, i
   else
     hipLaunchKernelGGL((quantize_weight_kernel<float, false>), grid, block, 0, stream,
                        static_cast<const float*>(w), N, K, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight_mx4(const void* w, moe_dtype w_dtype, size_t nblocks,
+                                      uint8_t* q, uint8_t* scales, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>((nblocks + 255) / 256)), block(256);
+  if (w_dtype == MOE_BF16)
+    hipLaunchKernelGGL(quantize_weight_mx4_kernel<uint16_t>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(w), nblocks, q, scales);
+  else
+    hipLaunchKernelGGL(quantize_weight_mx4_kernel<float>, grid, block, 0, stream,
+                       static_cast<const float*>(w), nblocks, q, scales);
   return hipGetLastError();
 }
 

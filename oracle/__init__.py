@@ -148,6 +148,8 @@ def e2m1_decode_packed(q: np.ndarray) -> np.ndarray:
 
 def quantize_weight_mxfp4(W: np.ndarray):
     """W [..., N, K] fp32 -> (q [..., N, K/2] packed e2m1, s [..., N, K/32] UE8M0 bytes)."""
+    if not np.issubdtype(np.asarray(W).dtype, np.floating):
+        raise TypeError("quantize_weight_mxfp4 takes float values (decode bf16 bits first)")
     W = _c(W, np.float32)
     lead, (N, K) = W.shape[:-2], W.shape[-2:]
     assert K % 32 == 0

@@ -117,6 +117,14 @@ def test_quantize_validation(lib):
                                          None) == UNS
     assert lib.fp8_quantize_weight_ue8m0(FAKE, moe.MOE_F32, 0, 128, 256, 128, FAKE, FAKE,
                                          None) == INV
+    # FP4 with MX scales: K % 32, float input, 16-byte aligned codes
+    assert lib.fp4_quantize_weight_mx(FAKE, moe.MOE_F32, 2, 128, 200, FAKE, FAKE, None) == UNS
+    assert lib.fp4_quantize_weight_mx(FAKE, moe.MOE_F32, 0, 128, 256, FAKE, FAKE, None) == INV
+    assert lib.fp4_quantize_weight_mx(FAKE, moe.MOE_FP8_E4M3, 2, 128, 256, FAKE, FAKE,
+                                      None) == INV
+    assert lib.fp4_quantize_weight_mx(FAKE, moe.MOE_BF16, 2, 128, 256, ctypes.c_void_p(0x1008), FAKE,
+                                      None) == UNS
+    assert lib.fp4_quantize_weight_mx(FAKE, moe.MOE_BF16, 2, 128, 256, FAKE, None, None) == INV
 
 
 def _args(**kw):
@@ -150,6 +158,15 @@ def test_experts_validation(lib):
     assert _fwd(lib, **fp8) == INV                             # fp8 needs the scales
     assert _fwd(lib, scale_fmt=moe.MOE_SCALE_UE8M0) == INV     # UE8M0 scales only on fp8
     assert _fwd(lib, scale_fmt=7, **fp8) == INV                # unknown scale format
+    fp4 = dict(act_dtype=moe.MOE_FP8_E4M3, w_dtype=moe.MOE_FP4_E2M1, x_scales=0x1000,
+               s_gate=0x1000, s_up=0x1000, s_down=0x1000)
+    assert _fwd(lib, **fp4) == UNS                             # E2M1 needs UE8M0 scales
+    assert _fwd(lib, T=129, scale_fmt=moe.MOE_SCALE_UE8M0, **fp4) == UNS   # 258 pairs > 256
+    assert _fwd(lib, act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_FP4_E2M1) == UNS
+    assert (lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_FP8_E4M3,
+                                           moe.MOE_FP4_E2M1) ==
+            lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_FP8_E4M3,
+                                           moe.MOE_FP8_E4M3))
     need = lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_BF16, moe.MOE_BF16)
     assert need >= 32 * 2 * 512 * 2
     assert _fwd(lib, workspace_bytes=need - 1) == moe.MOE_ERR_WORKSPACE_TOO_SMALL

@@ -1,0 +1,177 @@
+"""GPU parity of FP4 (E2M1) experts with MX block scales against the oracle.
+
+Transformers "Experts backends" page (notes on FP4 quantised experts with UE8M0 scales) and
+"Fine-grained FP8" page ("UE8M0 scale format"). Weights: fp32 or bf16 masters quantised to packed
+E2M1 with one e8m0 byte per row per 32 input channels on the GPU (fp4_quantize_weight_mx) and,
+independently, by the oracle; codes and scales must agree bit-exactly, and the oracle then uses its
+own quantised weights. Activations: e4m3 with UE8M0 per-128 scales, x in the layer and h between
+the projections, the same rule on both sides. Output bound: max|err| <= 6e-2 * max|ref|, the bound
+of the fp8 layers: the weights are exact on both sides, so only the activation rule's decisions
+and the summation order differ.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_softmax_amd as moe
+import oracle
+import synth
+from gpu_util import assert_close_rel_max, log, out_to_f64, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _edge_rows(K):
+    """Rows whose 32-blocks stress the MX scale rule and the E2M1 rounding."""
+    rng = np.random.default_rng(23)
+    rows = []
+    z = np.zeros(K, np.float32)
+    z[::5] = -0.0
+    rows.append(z)                                                   # zero blocks, with -0
+    for e in (-30, 0, 9):
+        b = (rng.uniform(-1, 1, K) * 6.0 * 2.0 ** e).astype(np.float32)
+        b[3::32] = np.float32(6.0 * 2.0 ** e)                        # amax exactly 6 * 2^e
+        rows.append(b)
+        c = b.copy()
+        c[3::32] = np.nextafter(np.float32(6.0 * 2.0 ** e), np.float32(np.inf))
+        rows.append(c)                                               # one ulp above
+    grid = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], np.float32)
+    t = np.resize(np.concatenate([grid, -grid]), K).astype(np.float32)
+    t[::32] = 6.0
+    rows.append(t)                                                   # E2M1 midpoints, ties
+    rows.append((rng.standard_normal(K) * 1e-41).astype(np.float32))  # fp32 subnormals
+    rows.append((rng.standard_normal(K) * 1e37).astype(np.float32))   # near the fp32 top
+    one = np.zeros(K, np.float32)
+    one[37] = -3.0
+    rows.append(one)                                                 # a single non-zero
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("wdt", ("f32", "bf16"))
+def test_fp4_quantize_weight_bit_exact(wdt):
+    K = 256
+    edge = _edge_rows(K)
+    rnd = synth.normal_f32(7001, (2, 48, K), 1 / 16)
+    W = np.concatenate([rnd, np.stack([edge, edge[::-1]])], axis=1)   # [2, 48 + 12, K]
+    if wdt == "bf16":
+        bits = torch.from_numpy(W).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        dev_in, ref_in = to_dev(bits), synth.bf16_bits_to_f32(bits)
+    else:
+        dev_in, ref_in = to_dev(W), W
+    q, s = moe.fp4_quantize_weight_mx(dev_in)
+    qr, sr = oracle.quantize_weight_mxfp4(ref_in)
+    assert tuple(q.shape) == qr.shape and tuple(s.shape) == sr.shape
+    np.testing.assert_array_equal(to_host(s), sr)
+    np.testing.assert_array_equal(to_host(q), qr)
+
+
+def _quantised(spec):
+    """GPU-quantised weights (checked bit-exactly against the oracle's) and the oracle's."""
+    dev, ref = [], []
+    for which in ("gate", "up", "down"):
+        m = synth.gen_expert_weight(spec, which)
+        if m.dtype == np.uint16:
+            m = synth.bf16_bits_to_f32(m)
+        q, s = moe.fp4_quantize_weight_mx(to_dev(m))
+        qr, sr = oracle.quantize_weight_mxfp4(m)
+        np.testing.assert_array_equal(to_host(q), qr)
+        np.testing.assert_array_equal(to_host(s), sr)
+        dev.append((q, s))
+        ref.append((qr, sr))
+    return dev, ref
+
+
+DECODE = [
+    synth.DSV3_FP8.with_(name="fp4dec_T32_d512_f384_E8_k2", T=32, d=512, f=384, E=8, k=2),
+    # about 100 tokens per expert: several 64-token passes
+    synth.DSV3_FP8.with_(name="fp4dec_T200_d256_f256_E2_k1", T=200, d=256, f=256, E=2, k=1),
+    # P = 256, the largest batch the streaming kernels take; f not a multiple of 256
+    synth.DSV3_FP8.with_(name="fp4dec_T64_d384_f640_E16_k4", T=64, d=384, f=640, E=16, k=4),
+    synth.DSV3_FP8.with_(name="fp4dec_T3_d128_f128_E4_k1", T=3, d=128, f=128, E=4, k=1),
+]
+
+
+@pytest.mark.parametrize("spec", DECODE, ids=lambda s: s.name)
+def test_fp4_decode_layers(spec):
+    log(spec.name)
+    x = synth.gen_x(spec)
+    logits = synth.gen_logits(spec)
+    wq, wq_ref = _quantised(spec)
+    ids_ref, w_ref = oracle.route(logits, spec.k)
+    ex = oracle.Experts(*(q for q, _ in wq_ref), *(s for _, s in wq_ref), quant_act=True,
+                        scale_fmt="ue8m0", w_fp4=True)
+    ref = oracle.moe_forward(x, ex, ids_ref, w_ref)
+    (qg, sg), (qu, su), (qd, sd) = wq
+    for layout in ("slots", "permuted", "acc_f32"):
+        res = moe.moe_layer(to_dev(x), qg, qu, qd, spec.k, logits=to_dev(logits), s_gate=sg,
+                            s_up=su, s_down=sd, y_layout=layout, w_fp4=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
+        got = out_to_f64(res.out)
+        assert np.all(np.isfinite(got))
+        assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, layout))
+
+
+def test_fp4_rejects_unsupported():
+    # E2M1 weights take UE8M0 scales only, and only the weight-streaming kernels (P <= 256)
+    spec = DECODE[0]
+    wq, _ = _quantised(spec)
+    (qg, sg), (qu, su), (qd, sd) = wq
+    x = synth.gen_x(spec)
+    xq, xs = moe.fp8_quantize_act(to_dev(x), scale_fmt="ue8m0")
+    ids, w, _ = moe.moe_route(spec.k, logits=to_dev(synth.gen_logits(spec)))
+    perm = moe.moe_permute(ids, spec.E)
+    with pytest.raises(ValueError, match="UNSUPPORTED"):
+        moe.moe_experts_forward(xq, qg, qu, qd, perm.offsets, perm.sorted_pair, w, spec.k,
+                                x_scales=xs.float(), s_gate=sg, s_up=su, s_down=sd,
+                                scale_fmt="f32", w_fp4=True)
+    big = spec.with_(T=129, k=2)                         # 258 pairs
+    xb = torch.zeros((big.T, big.d), dtype=torch.uint8, device="cuda")
+    xbs = torch.full((big.T, big.d // 128), 127, dtype=torch.uint8, device="cuda")
+    ids_b = torch.zeros((big.T, 2), dtype=torch.int32, device="cuda")
+    ids_b[:, 1] = 1
+    perm_b = moe.moe_permute(ids_b, big.E)
+    wb = torch.full((big.T, 2), 0.5, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="UNSUPPORTED"):
+        moe.moe_experts_forward(xb, qg, qu, qd, perm_b.offsets, perm_b.sorted_pair, wb, 2,
+                                x_scales=xbs, s_gate=sg, s_up=su, s_down=sd, scale_fmt="ue8m0",
+                                w_fp4=True)
+    torch.cuda.synchronize()
+
+
+def test_mixtral_fp4_decode_full_sampled():
+    # the Mixtral-shaped decode layer (T=32, d=4096, f=14336, E=8, k=2) with its bf16 weights
+    # quantised to E2M1 on the GPU (codes and scales checked bit-exactly against the oracle's);
+    # the oracle runs on 8 sampled tokens
+    spec = synth.MIXTRAL_DECODE
+    T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
+    x = synth.gen_x(spec)
+    lg = oracle.router_logits(x, synth.gen_router_weight(spec))
+    ids_ref, w_ref = oracle.route(lg, k)
+    dev_q, dev_s, ref_q, ref_s = {}, {}, {}, {}
+    for which in ("gate", "up", "down"):
+        rows, cols = (f, d) if which != "down" else (d, f)
+        qt = torch.empty((E, rows, cols // 2), dtype=torch.uint8, device="cuda")
+        st = torch.empty((E, rows, cols // 32), dtype=torch.uint8, device="cuda")
+        rq = np.empty((E, rows, cols // 2), np.uint8)
+        rs = np.empty((E, rows, cols // 32), np.uint8)
+        for e in range(E):
+            bits = synth.gen_expert_weight(spec, which, experts=[e])
+            q, s = moe.fp4_quantize_weight_mx(to_dev(bits))
+            oq, os_ = oracle.quantize_weight_mxfp4(synth.bf16_bits_to_f32(bits))
+            np.testing.assert_array_equal(to_host(q), oq)
+            np.testing.assert_array_equal(to_host(s), os_)
+            qt[e], st[e], rq[e], rs[e] = q[0], s[0], oq[0], os_[0]
+        dev_q[which], dev_s[which] = qt, st
+        ref_q[which], ref_s[which] = rq, rs
+    log("weights quantised; running the fp4 decode layer")
+    res = moe.moe_layer(to_dev(x), dev_q["gate"], dev_q["up"], dev_q["down"], k,
+                        logits=to_dev(lg), s_gate=dev_s["gate"], s_up=dev_s["up"],
+                        s_down=dev_s["down"], w_fp4=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
+    tokens = np.arange(0, T, 4)
+    ex = oracle.Experts(ref_q["gate"], ref_q["up"], ref_q["down"], ref_s["gate"], ref_s["up"],
+                        ref_s["down"], quant_act=True, scale_fmt="ue8m0", w_fp4=True)
+    ref = oracle.moe_forward(x[tokens], ex, ids_ref[tokens], w_ref[tokens])
+    assert_close_rel_max(out_to_f64(res.out)[tokens], ref, 6e-2, "mixtral fp4 decode")
