@@ -218,7 +218,8 @@ moe_status fp4_quantize_weight_mx(const void* w, moe_dtype w_dtype, int batch, i
  *        weights packed E2M1 [E, f, d/2] and [E, d, f/2] (from fp4_quantize_weight_mx) with MX
  *        scales s_gate / s_up [E, f, d/32] and s_down [E, d, f/32]; x and h e4m3 with UE8M0
  *        per-128 scales. Weight-streaming kernels only: P <= 256, otherwise
- *        MOE_ERR_UNSUPPORTED. d % 128 == f % 128 == 0.
+ *        MOE_ERR_UNSUPPORTED. d % 128 == f % 128 == 0; the three MX scale arrays 4-byte aligned
+ *        (MOE_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int T, d, f, E, k;

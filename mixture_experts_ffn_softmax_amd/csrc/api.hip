@@ -287,6 +287,8 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   const long long P = static_cast<long long>(a->T) * a->k;
   // E2M1 weights: MX scales are e8m0 bytes, and only the weight-streaming kernels take them
   if (w4 && (!ue8m0 || P > kDecodeMaxPairs)) return MOE_ERR_UNSUPPORTED;
+  if (w4 && (!aligned(a->s_gate, 4) || !aligned(a->s_up, 4) || !aligned(a->s_down, 4)))
+    return MOE_ERR_UNSUPPORTED;   // MX scale rows are read as dwords
   // 32-bit element offsets inside the kernels
   if (static_cast<long long>(a->T) * a->d > INT_MAX / 2 || P * a->f > INT_MAX / 2 ||
       P * a->d > INT_MAX / 2 || static_cast<long long>(a->f) * a->d > INT_MAX / 4)

@@ -24,10 +24,9 @@
 // one 128-wide K block, lane group g (lanes 16g..16g+15) holds K = 32g..32g+31 of an FP4 operand,
 // but of an 8-bit operand K = 16g..16g+15 in its first 16 bytes and 64+16g..64+16g+15 in its last
 // 16 (measured on gfx950); a lane's scale covers K = 32g..32g+31 in both. So each lane passes its
-// own weight block's byte, loaded next to the weights, and the e4m3 activations are fetched as the
-// two 16-byte pieces that line up with the FP4 weights. (Two 8-bit operands share the one layout,
-// and their scales are uniform over the 128-wide block, so the fp8 kernels read K contiguously.)
-// Half the streamed bytes of the fp8 weights.
+// own weight block's byte, and the e4m3 activations are fetched as the two 16-byte pieces that
+// line up with the FP4 weights. The e4m3 weights are fetched the same way: then the four lanes of a
+// row read one contiguous 64-byte piece per load. Half the streamed bytes of the fp8 weights.
 #include "common.h"
 #include "launch.h"
 
@@ -36,7 +35,6 @@ namespace {
 
 constexpr int kFdGateRows = 32;   // gate rows (and as many up rows) per gate/up workgroup
 constexpr int kFdDownRows = 64;   // W_down rows per down workgroup
-constexpr int kFdTokens = 64;     // tokens per pass (4 groups of 16)
 constexpr int kGateUp = 0;
 constexpr int kDown = 1;
 
@@ -59,15 +57,6 @@ struct Fp8DecodeArgs {
   const float* topk_w;
 };
 
-__device__ __forceinline__ i32x8_t ld32g(const uint8_t* p) {
-  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
-  const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + 16);
-  i32x8_t r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-  return r;
-}
-
 __device__ __forceinline__ i32x8_t ld16x2g(const uint8_t* p, const uint8_t* q) {
   const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
   const u32x4_t b = *reinterpret_cast<const u32x4_t*>(q);
@@ -85,10 +74,12 @@ __device__ __forceinline__ i32x8_t ld16g(const uint8_t* p) {
   return r;
 }
 
-// kW4: E2M1 weights with per-32 MX scales (implies kUE).
-template <int MODE, bool kUE, bool kW4>
+// kW4: E2M1 weights with per-32 MX scales (implies kUE). kTG: groups of 16 tokens per pass over
+// the weights (fewer groups hold fewer registers and less LDS, so more waves stream at once).
+template <int MODE, bool kUE, bool kW4, int kTG>
 __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
+  constexpr int kTokens = 16 * kTG;
   const int nrb = (p.N + kRows - 1) / kRows;
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
@@ -96,10 +87,12 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   const int M = p.offsets[e + 1] - row0;
   if (M <= 0) return;
 
-  __shared__ f32x4_t red[4][4][4][64];  // [wave][row group][token group][lane], 64 KB
-  // UE8M0: the row groups' scale bytes for every K block, loaded once (byte loads in the K loop
-  // would be vector loads, and waiting for one waits for the weight stream issued before it)
-  __shared__ uint8_t wsb[4][256];
+  __shared__ f32x4_t red[4][4][kTG][64];  // [wave][row group][token group][lane], 16 KB each
+  // Weight scales for every K block, staged once: 128x128 blocks, one per row group (fp32 bits
+  // or the e8m0 byte), or for E2M1 the MX bytes of all 64 rows (dynamic, below). Loads of them
+  // in the K loop would cost the texture-address unit about as much as the weight stream.
+  __shared__ uint32_t wss[4][256];
+  extern __shared__ uint32_t wsx[];   // E2M1: [64 rows][KB | 1 dwords]: byte 4c+g = block (c, g)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
@@ -109,7 +102,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
 
   // A rows (4 groups of 16 weight rows); a group lies inside one 128-row scale block.
   const uint8_t* arow[4];
-  const void* ascale[4];   // this expert's scale row of the group's 128-row block
+  const void* ascale[4];   // 128x128 scales: this expert's scale row of the group's row block
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg) {
     int n;
@@ -126,64 +119,78 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
     }
     const int row = min(n + r16, p.N - 1);
     if constexpr (kW4) {
-      // this lane's row, its 32-wide block g of the first 128-wide K block
-      ascale[rg] = static_cast<const uint8_t*>(sbase) +
-                   (static_cast<size_t>(e) * p.N + row) * (p.K / 32) + g;
+      ascale[rg] = nullptr;   // MX scales: staged per row below
       arow[rg] = base + static_cast<size_t>(row) * rowb + g * 16;
     } else {
       const int nb = min(n, p.N - 1) / 128;
       const size_t sidx = (static_cast<size_t>(e) * NB + nb) * KB;
       ascale[rg] = kUE ? static_cast<const void*>(static_cast<const uint8_t*>(sbase) + sidx)
                        : static_cast<const void*>(static_cast<const float*>(sbase) + sidx);
-      arow[rg] = base + static_cast<size_t>(row) * rowb + g * 32;
+      arow[rg] = base + static_cast<size_t>(row) * rowb + g * 16;
     }
   }
-  if constexpr (kUE && !kW4) {
-    for (int i = tid; i < 4 * KB; i += 256)
-      wsb[i / KB][i % KB] = static_cast<const uint8_t*>(ascale[i / KB])[i % KB];
-    __syncthreads();
+  const int S = KB | 1;   // odd dword stride: the 16 rows a load touches sit in distinct banks
+  if constexpr (kW4) {
+    for (int i = tid; i < 64 * KB; i += 256) {
+      const int lr = i / KB, j = i - lr * KB;   // LDS row rg * 16 + r, dword j of the row
+      const int rg = lr >> 4;
+      const int n = MODE == kGateUp ? rb * kRows + (rg & 1) * 16 + (lr & 15) : rb * kRows + lr;
+      const void* sb = (MODE == kGateUp && rg >= 2) ? p.s1 : p.s0;
+      const uint8_t* src = static_cast<const uint8_t*>(sb) +
+                           (static_cast<size_t>(e) * p.N + min(n, p.N - 1)) * (p.K / 32);
+      wsx[lr * S + j] = reinterpret_cast<const uint32_t*>(src)[j];
+    }
+  } else {
+    for (int i = tid; i < 4 * KB; i += 256) {
+      const int rg = i / KB, c = i - rg * KB;
+      wss[rg][c] = kUE ? static_cast<uint32_t>(static_cast<const uint8_t*>(ascale[rg])[c])
+                       : __float_as_uint(static_cast<const float*>(ascale[rg])[c]);
+    }
   }
+  __syncthreads();
+  // E2M1: this lane's scale bytes, row rg * 16 + r16, block g of K block c at + 4c
+  const uint8_t* wsl = reinterpret_cast<const uint8_t*>(wsx) + r16 * S * 4 + g;
 
-  for (int tc0 = 0; tc0 < M; tc0 += kFdTokens) {
-    const int ntg = min(4, (M - tc0 + 15) / 16);
-    const uint8_t* brow[4];
-    const float* bscale[4];
+  for (int tc0 = 0; tc0 < M; tc0 += kTokens) {
+    const int ntg = min(kTG, (M - tc0 + 15) / 16);
+    const uint8_t* brow[kTG];
+    const float* bscale[kTG];
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
+    for (int tg = 0; tg < kTG; ++tg) {
       const int ti = min(tc0 + tg * 16 + r16, M - 1);
       const int pos = row0 + ti;
       const int src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
-      brow[tg] = p.a + static_cast<size_t>(src) * p.K + (kW4 ? g * 16 : g * 32);
+      brow[tg] = p.a + static_cast<size_t>(src) * p.K + g * 16;
       bscale[tg] = p.a_s + static_cast<size_t>(src) * KB;
     }
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][kTG];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int tg = 0; tg < kTG; ++tg) acc[rg][tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int c = wave; c < KB; c += 4) {
       const int kb = c * 128;
-      i32x8_t av[4], bv[4];
-      float bs[4];
+      i32x8_t av[4], bv[kTG];
+      float bs[kTG];
       int ewl[4];   // E2M1: each lane's own block scale byte
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         if constexpr (kW4) {
           av[rg] = ld16g(arow[rg] + kb / 2);
-          ewl[rg] = static_cast<const uint8_t*>(ascale[rg])[c * 4];
+          ewl[rg] = wsl[rg * 16 * S * 4 + c * 4];
         } else {
-          av[rg] = ld32g(arow[rg] + kb);
+          av[rg] = ld16x2g(arow[rg] + kb, arow[rg] + kb + 64);
         }
       }
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg)
+      for (int tg = 0; tg < kTG; ++tg)
         if (tg < ntg) {
-          bv[tg] = kW4 ? ld16x2g(brow[tg] + kb, brow[tg] + kb + 64) : ld32g(brow[tg] + kb);
+          bv[tg] = ld16x2g(brow[tg] + kb, brow[tg] + kb + 64);
           bs[tg] = bscale[tg][c];
         }
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
+      for (int tg = 0; tg < kTG; ++tg) {
         if (tg >= ntg) continue;
         if constexpr (kUE) {
           // the token's e8m0 byte: exponent field of its power-of-two fp32 scale. Each block's
@@ -192,14 +199,14 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
           const int ex = (__float_as_uint(bs[tg]) >> 23) & 0xFF;
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const int ew = kW4 ? ewl[rg] : wsb[rg][c];
+            const int ew = kW4 ? ewl[rg] : static_cast<int>(wss[rg][c]);
             acc[rg][tg] += __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 av[rg], bv[tg], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, kW4 ? 4 : 0, 0, 0, ew, 0, ex);
           }
         } else {
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
-            const float sc = static_cast<const float*>(ascale[rg])[c] * bs[tg];
+            const float sc = __uint_as_float(wss[rg][c]) * bs[tg];
             const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 av[rg], bv[tg], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
@@ -212,14 +219,14 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg)
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) red[wave][rg][tg][lane] = acc[rg][tg];
+      for (int tg = 0; tg < kTG; ++tg) red[wave][rg][tg][lane] = acc[rg][tg];
     __syncthreads();
 
     // Wave w finishes token group w. Output layout of a 16x16 block: lane l holds token l % 16
     // and weight rows 4 * (l / 16) + i, i = 0..3.
     const int tg = wave;
     const int ti = tc0 + tg * 16 + r16;
-    if (tg < ntg && ti < M) {
+    if (tg < ntg && ti < M) {   // ntg <= kTG: red is indexed in bounds
       f32x4_t s[4];
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg)
@@ -273,13 +280,33 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   }
 }
 
+template <int MODE, int kTG>
+void launch_tg(const Fp8DecodeArgs& a, dim3 grid, bool ue, bool w4, hipStream_t stream) {
+  // E2M1: the 64 rows' MX scale bytes, rows padded to an odd number of dwords
+  const unsigned mx_lds = static_cast<unsigned>(64 * ((a.K / 128) | 1) * 4);
+  if (w4) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, true, kTG>), grid, dim3(256), mx_lds,
+                             stream, a);
+  else if (ue) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, false, kTG>), grid, dim3(256), 0,
+                                  stream, a);
+  else hipLaunchKernelGGL((decode_fp8_kernel<MODE, false, false, kTG>), grid, dim3(256), 0,
+                          stream, a);
+}
+
+// Token groups per pass from the mean pairs per expert: a pass holds a typical expert's tokens
+// with room for the spread; an expert with more makes further passes over its weights.
+inline int token_groups(int P, int E) {
+  const int mean = (P + E - 1) / E;
+  return mean <= 8 ? 1 : (mean <= 24 ? 2 : 4);
+}
+
 template <int MODE>
-hipError_t launch_one(const Fp8DecodeArgs& a, int E, bool ue, bool w4, hipStream_t stream) {
+hipError_t launch_one(const Fp8DecodeArgs& a, int E, int P, bool ue, bool w4, hipStream_t stream) {
   constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
-  const dim3 grid(static_cast<unsigned>(E * ((a.N + kRows - 1) / kRows))), block(256);
-  if (w4) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, true>), grid, block, 0, stream, a);
-  else if (ue) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, false>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((decode_fp8_kernel<MODE, false, false>), grid, block, 0, stream, a);
+  const dim3 grid(static_cast<unsigned>(E * ((a.N + kRows - 1) / kRows)));
+  const int tg = token_groups(P, E);
+  if (tg == 1) launch_tg<MODE, 1>(a, grid, ue, w4, stream);
+  else if (tg == 2) launch_tg<MODE, 2>(a, grid, ue, w4, stream);
+  else launch_tg<MODE, 4>(a, grid, ue, w4, stream);
   return hipGetLastError();
 }
 
@@ -304,8 +331,8 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   const bool ue = L.scale_ue8m0 != 0;
   const bool w4 = L.w_fp4 != 0;
   if (w4 && !ue) return hipErrorNotSupported;   // MX scales are e8m0 bytes
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipError_t e = launch_one<kGateUp>(g, L.E, ue, w4, stream);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
+  hipError_t e = launch_one<kGateUp>(g, L.E, P, ue, w4, stream);
   if (e != hipSuccess) return e;
   // h -> e4m3 codes with per-(pair, 128-channel) scales, as fp32 values for the down kernel
   uint8_t* hq = static_cast<uint8_t*>(L.h);
@@ -318,7 +345,7 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
     e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, L.h_scales, false, stream);
   }
   if (e != hipSuccess) return e;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
 
   Fp8DecodeArgs dn{};
   dn.a = hq;
@@ -335,9 +362,9 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   dn.y_layout = L.y_layout;
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  e = launch_one<kDown>(dn, L.E, ue, w4, stream);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
+  e = launch_one<kDown>(dn, L.E, P, ue, w4, stream);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return e;
 }
 
