@@ -276,7 +276,7 @@ def measure_decode_fp8(moe, synth, W, Wr, steps, warmup, scale_fmt, fp4=False):
     Q, S = [], []
     for w in W:
         if fp4:
-            q, s_ = moe.fp4_quantize_weight_mx(w)
+            q, s_ = moe.fp4_quantize_weight_mx(w, tiled=True)
         else:
             q, s_ = moe.fp8_quantize_weight(w, scale_fmt=scale_fmt)
         Q.append(q)

@@ -190,6 +190,21 @@ moe_status fp4_quantize_weight_mx(const void* w, moe_dtype w_dtype, int batch, i
                                   uint8_t* q, uint8_t* scales, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * fp4_tile_weight - packed E2M1 weights from row order to the matrix-fragment order that
+ * moe_experts_forward streams (a byte permutation; the layout of the block-scaled matrix
+ * instruction with an FP4 operand, as measured on gfx950).
+ *
+ *  q        [batch, N, K/2] packed E2M1 rows (as fp4_quantize_weight_mx writes them).
+ *  q_tiled  out, same size, must not overlap q: for each b, each 16-row group n16 = n / 16 and
+ *           each 128-wide K block c, 1024 bytes at ((b * N/16 + n16) * K/128 + c) * 1024; in it,
+ *           16 bytes per lane l = r + 16 g (r, g < 16, 4): row 16 n16 + r, K = 128 c + 32 g ..
+ *           128 c + 32 g + 31, packed as in q.
+ *  N % 16 == 0, K % 128 == 0, both pointers 16-byte aligned (MOE_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------------------------ */
+moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q_tiled,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * moe_experts_forward - both grouped projections of every selected expert.
  * (Transformers "Experts backends" page: introduction and backends table rows grouped_mm,
  * deepgemm_megamoe, sonicmoe; the decode-time switch to a small-batch kernel; AWS fused-MoE news
@@ -215,9 +230,10 @@ moe_status fp4_quantize_weight_mx(const void* w, moe_dtype w_dtype, int batch, i
  *        or an unknown value, is MOE_ERR_INVALID_ARGUMENT.
  *    FP8_E4M3 / FP4_E2M1 / BF16 or F32, scale_fmt = MOE_SCALE_UE8M0 (MOE_SCALE_F32 is
  *        MOE_ERR_UNSUPPORTED)
- *        weights packed E2M1 [E, f, d/2] and [E, d, f/2] (from fp4_quantize_weight_mx) with MX
- *        scales s_gate / s_up [E, f, d/32] and s_down [E, d, f/32]; x and h e4m3 with UE8M0
- *        per-128 scales. Weight-streaming kernels only: P <= 256, otherwise
+ *        weights packed E2M1 [E, f, d/2] and [E, d, f/2] in matrix-fragment order (from
+ *        fp4_quantize_weight_mx, then fp4_tile_weight) with MX scales (row order, as the
+ *        quantiser writes them) s_gate / s_up [E, f, d/32] and s_down [E, d, f/32]; x and h
+ *        e4m3 with UE8M0 per-128 scales. Weight-streaming kernels only: P <= 256, otherwise
  *        MOE_ERR_UNSUPPORTED. d % 128 == f % 128 == 0; the three MX scale arrays 4-byte aligned
  *        (MOE_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------------------------ */

@@ -30,7 +30,8 @@ _LAYOUTS = {"permuted": MOE_Y_PERMUTED, "slots": MOE_Y_SLOTS, "acc_f32": MOE_Y_A
 EXPORTED_SYMBOLS = (
     "moe_status_string", "moe_route", "moe_permute", "moe_permute_workspace_size",
     "fp8_quantize_act", "fp8_quantize_weight", "fp8_quantize_act_ue8m0",
-    "fp8_quantize_weight_ue8m0", "fp4_quantize_weight_mx", "moe_experts_forward",
+    "fp8_quantize_weight_ue8m0", "fp4_quantize_weight_mx", "fp4_tile_weight",
+    "moe_experts_forward",
     "moe_experts_workspace_size", "moe_combine", "moe_event_create", "moe_event_destroy",
     "moe_event_record", "moe_event_elapsed_ms",
 )
@@ -86,6 +87,7 @@ def load_library(path: str = LIB_PATH):
         "fp8_quantize_act_ue8m0": ([vp, i32, i32, i32, i32, vp, vp, vp, vp], st),
         "fp8_quantize_weight_ue8m0": ([vp, i32, i32, i32, i32, i32, vp, vp, vp], st),
         "fp4_quantize_weight_mx": ([vp, i32, i32, i32, i32, vp, vp, vp], st),
+        "fp4_tile_weight": ([vp, i32, i32, i32, vp, vp], st),
         "moe_experts_forward": ([ctypes.POINTER(moe_experts_args), vp], st),
         "moe_experts_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "moe_combine": ([vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp], st),
@@ -241,10 +243,11 @@ def fp8_quantize_weight(w: torch.Tensor, block: int = 128, scale_fmt: str = "f32
     return q, s
 
 
-def fp4_quantize_weight_mx(w: torch.Tensor):
+def fp4_quantize_weight_mx(w: torch.Tensor, tiled: bool = False):
     """E2M1 quantisation of [batch, N, K] (or [N, K]) weights with one e8m0 scale per row per 32
     input channels. Returns (q uint8 [..., N, K/2] packed, element 2j in the low nibble of byte
-    j; scales uint8 [..., N, K/32])."""
+    j; scales uint8 [..., N, K/32]). ``tiled``: q in the matrix-fragment order that
+    moe_experts_forward takes (see fp4_tile_weight)."""
     lib = load_library()
     _contig(w)
     shape = w.shape
@@ -254,7 +257,22 @@ def fp4_quantize_weight_mx(w: torch.Tensor):
     s = torch.empty(tuple(shape[:-1]) + (max(K // 32, 1),), dtype=torch.uint8, device=w.device)
     _check(lib.fp4_quantize_weight_mx(_ptr(w), _dtype_code(w), batch, N, K, _ptr(q), _ptr(s),
                                       _stream()))
+    if tiled:
+        q = fp4_tile_weight(q)
     return q, s
+
+
+def fp4_tile_weight(q: torch.Tensor) -> torch.Tensor:
+    """Packed E2M1 rows [..., N, K/2] -> the same bytes in matrix-fragment order (a new tensor
+    of the same shape): for each 16-row group and 128-wide K block, 1 KB holding 16 bytes per
+    lane l = r + 16 g (row r of the group, K = 32 g .. 32 g + 31 of the block)."""
+    lib = load_library()
+    _contig(q)
+    N, K = q.shape[-2], 2 * q.shape[-1]
+    batch = 1 if q.dim() == 2 else int(torch.tensor(q.shape[:-2]).prod())
+    out = torch.empty_like(q)
+    _check(lib.fp4_tile_weight(_ptr(q), batch, N, K, _ptr(out), _stream()))
+    return out
 
 
 def experts_workspace_bytes(T, d, f, E, k, act_dtype: int, w_dtype: int) -> int:
@@ -268,7 +286,8 @@ def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k
     """Both grouped projections. Returns y in ``y_layout`` ("permuted" [P,d], "slots" [T,k,d],
     "acc_f32" [T,d] fp32). ``events``: optional 4 event handles (see moe_event_create).
     ``scale_fmt``: fp8 block scales as fp32 values ("f32") or e8m0 bytes ("ue8m0").
-    ``w_fp4``: the uint8 weights are packed E2M1 (from fp4_quantize_weight_mx) with MX scales."""
+    ``w_fp4``: the uint8 weights are packed E2M1 in matrix-fragment order (fp4_quantize_weight_mx
+    with tiled=True) with MX scales."""
     lib = load_library()
     for t in (x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, x_scales, s_gate, s_up,
               s_down):
@@ -363,7 +382,7 @@ def moe_layer(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, y_lay
 
     For fp8 weights (uint8 e4m3 codes with block scales s_*), x is given in bf16/fp32 and quantised
     per token per 128 channels here; uint8 scales select the UE8M0 scale format. ``w_fp4``:
-    packed E2M1 weights with MX scales (e4m3 activations, UE8M0 scales).
+    packed E2M1 weights in matrix-fragment order with MX scales (e4m3 activations, UE8M0 scales).
     """
     E = w_gate.shape[0]
     T, d = x.shape

@@ -239,6 +239,18 @@ moe_status fp8_quantize_weight_ue8m0(const void* w, moe_dtype w_dtype, int batch
   return dev(launch_quantize_weight(w, w_dtype, batch, N, K, q, scales, true, stream));
 }
 
+moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q_tiled,
+                           hipStream_t stream) {
+  if (!q || !q_tiled || batch < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (N % 16 || K % 128) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(q_tiled, 16)) return MOE_ERR_UNSUPPORTED;
+  const size_t bytes = static_cast<size_t>(batch) * N * (K / 2);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(q), b = reinterpret_cast<uintptr_t>(q_tiled);
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARGUMENT;   // no overlap
+  if (bytes / 16 > (static_cast<size_t>(INT_MAX) << 6)) return MOE_ERR_UNSUPPORTED;
+  return dev(launch_tile_weight_fp4(q, static_cast<size_t>(batch) * N, K, q_tiled, stream));
+}
+
 moe_status fp4_quantize_weight_mx(const void* w, moe_dtype w_dtype, int batch, int N, int K,
                                   uint8_t* q, uint8_t* scales, hipStream_t stream) {
   if (!w || !q || !scales || batch < 1 || N < 1 || K < 1) return MOE_ERR_INVALID_ARGUMENT;

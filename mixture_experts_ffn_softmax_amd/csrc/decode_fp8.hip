@@ -26,7 +26,9 @@
 // 16 (measured on gfx950); a lane's scale covers K = 32g..32g+31 in both. So each lane passes its
 // own weight block's byte, and the e4m3 activations are fetched as the two 16-byte pieces that
 // line up with the FP4 weights. The e4m3 weights are fetched the same way: then the four lanes of a
-// row read one contiguous 64-byte piece per load. Half the streamed bytes of the fp8 weights.
+// row read one contiguous 64-byte piece per load. The E2M1 weights come in matrix-fragment order
+// (each 16-row, 128-wide block is the 1 KB one load reads, lane by lane), which streams markedly
+// faster than 16 scattered row pieces. Half the streamed bytes of the fp8 weights.
 #include "common.h"
 #include "launch.h"
 
@@ -119,8 +121,9 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
     }
     const int row = min(n + r16, p.N - 1);
     if constexpr (kW4) {
+      // fragment order: the 16 rows' 128-wide K block c is 1 KB at (n / 16 * KB + c) * 1 KB
       ascale[rg] = nullptr;   // MX scales: staged per row below
-      arow[rg] = base + static_cast<size_t>(row) * rowb + g * 16;
+      arow[rg] = base + static_cast<size_t>(n / 16) * KB * 1024 + lane * 16;
     } else {
       const int nb = min(n, p.N - 1) / 128;
       const size_t sidx = (static_cast<size_t>(e) * NB + nb) * KB;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         if constexpr (kW4) {
-          av[rg] = ld16g(arow[rg] + kb / 2);
+          av[rg] = ld16g(arow[rg] + c * 1024);
           ewl[rg] = wsl[rg * 16 * S * 4 + c * 4];
         } else {
           av[rg] = ld16x2g(arow[rg] + kb, arow[rg] + kb + 64);

@@ -30,6 +30,9 @@ hipError_t launch_quantize_weight(const void* w, moe_dtype w_dtype, int batch, i
 // FP4 E2M1 weights with MX scales: nblocks 32-element blocks (rows * K / 32)
 hipError_t launch_quantize_weight_mx4(const void* w, moe_dtype w_dtype, size_t nblocks,
                                       uint8_t* q, uint8_t* scales, hipStream_t stream);
+// packed E2M1 [rows, K/2] (rows % 16 == 0, K % 128 == 0) -> matrix-fragment order
+hipError_t launch_tile_weight_fp4(const uint8_t* q, size_t rows, int K, uint8_t* out,
+                                  hipStream_t stream);
 // e8m0 bytes -> fp32 values 2^(b - 127)
 hipError_t launch_e8m0_expand(const uint8_t* b, size_t n, float* out, hipStream_t stream);
 

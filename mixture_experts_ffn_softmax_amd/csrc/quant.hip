@@ -164,6 +164,23 @@ __global__ __launch_bounds__(256) void quantize_weight_mx4_kernel(const WT* __re
   scales[blk] = static_cast<uint8_t>(b);
 }
 
+// Packed E2M1 rows -> matrix-fragment order: one thread moves the 16 bytes (32 values) that one
+// lane of a 16x128 fragment holds. Fragment (b, n16, c) is 1 KB at ((b * N/16 + n16) * KB + c);
+// within it lane l = r + 16 g holds row 16 n16 + r, K = 128 c + 32 g .. + 31.
+__global__ __launch_bounds__(256) void tile_weight_fp4_kernel(const uint8_t* __restrict__ q,
+                                                              size_t nchunks, int KB,
+                                                              uint8_t* __restrict__ out) {
+  const size_t t = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= nchunks) return;
+  const int l = static_cast<int>(t & 63);
+  const size_t frag = t >> 6;                  // (b * N/16 + n16) * KB + c
+  const size_t rowgrp = frag / KB;             // b * N/16 + n16
+  const int c = static_cast<int>(frag - rowgrp * KB);
+  const size_t row = rowgrp * 16 + (l & 15);   // b * N + n
+  const uint8_t* src = q + row * (static_cast<size_t>(KB) * 64) + c * 64 + (l >> 4) * 16;
+  *reinterpret_cast<u32x4_t*>(out + t * 16) = *reinterpret_cast<const u32x4_t*>(src);
+}
+
 // e8m0 bytes -> their fp32 values 2^(b - 127) (exact).
 __global__ __launch_bounds__(256) void e8m0_expand_kernel(const uint8_t* __restrict__ b, size_t n,
                                                           float* __restrict__ out) {
@@ -225,6 +242,14 @@ hipError_t launch_quantize_weight_mx4(const void* w, moe_dtype w_dtype, size_t n
   else
     hipLaunchKernelGGL(quantize_weight_mx4_kernel<float>, grid, block, 0, stream,
                        static_cast<const float*>(w), nblocks, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_weight_fp4(const uint8_t* q, size_t rows, int K, uint8_t* out,
+                                  hipStream_t stream) {
+  const size_t nchunks = rows * (K / 32);   // 16-byte chunks (32 values each)
+  hipLaunchKernelGGL(tile_weight_fp4_kernel, dim3(static_cast<unsigned>((nchunks + 255) / 256)),
+                     dim3(256), 0, stream, q, nchunks, K / 128, out);
   return hipGetLastError();
 }
 

@@ -125,6 +125,13 @@ def test_quantize_validation(lib):
     assert lib.fp4_quantize_weight_mx(FAKE, moe.MOE_BF16, 2, 128, 256, ctypes.c_void_p(0x1008), FAKE,
                                       None) == UNS
     assert lib.fp4_quantize_weight_mx(FAKE, moe.MOE_BF16, 2, 128, 256, FAKE, None, None) == INV
+    # tiling: N % 16, K % 128, 16-byte alignment, no overlap
+    OTHER = ctypes.c_void_p(0x100000)
+    assert lib.fp4_tile_weight(FAKE, 2, 24, 256, OTHER, None) == UNS
+    assert lib.fp4_tile_weight(FAKE, 2, 32, 192, OTHER, None) == UNS
+    assert lib.fp4_tile_weight(FAKE, 2, 32, 256, ctypes.c_void_p(0x100008), None) == UNS
+    assert lib.fp4_tile_weight(FAKE, 2, 32, 256, FAKE, None) == INV          # in place
+    assert lib.fp4_tile_weight(FAKE, 0, 32, 256, OTHER, None) == INV
 
 
 def _args(**kw):

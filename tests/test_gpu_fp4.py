@@ -7,7 +7,8 @@ independently, by the oracle; codes and scales must agree bit-exactly, and the o
 own quantised weights. Activations: e4m3 with UE8M0 per-128 scales, x in the layer and h between
 the projections, the same rule on both sides. Output bound: max|err| <= 6e-2 * max|ref|, the bound
 of the fp8 layers: the weights are exact on both sides, so only the activation rule's decisions
-and the summation order differ.
+and the summation order differ. The layer takes its codes in matrix-fragment order
+(fp4_tile_weight), checked bit-exactly against a reshape of the oracle's row-order codes.
 """
 import numpy as np
 import pytest
@@ -65,8 +66,33 @@ def test_fp4_quantize_weight_bit_exact(wdt):
     np.testing.assert_array_equal(to_host(q), qr)
 
 
+def _tiles_ref(q):
+    """Row-order packed codes [B, N, K/2] -> fragment order: per 16-row group and 128-wide K
+    block, lane l = r + 16 g holds row r's 16 bytes of K = 32 g .. 32 g + 31."""
+    B, N, H = q.shape
+    t = q.reshape(B, N // 16, 16, H // 64, 4, 16)          # b, n16, r, c, g, byte
+    return np.ascontiguousarray(t.transpose(0, 1, 3, 4, 2, 5)).reshape(B, N, H)
+
+
+def test_fp4_tile_weight_bit_exact():
+    rng = np.random.default_rng(31)
+    for B, N, K in ((1, 16, 128), (3, 48, 384), (2, 128, 1024)):
+        q = rng.integers(0, 256, (B, N, K // 2), dtype=np.uint8)
+        got = to_host(moe.fp4_tile_weight(to_dev(q)))
+        np.testing.assert_array_equal(got, _tiles_ref(q))
+    # the layout the kernels read: fragment (n16, c), lane l, byte j
+    q = rng.integers(0, 256, (1, 32, 128), dtype=np.uint8)
+    t = to_host(moe.fp4_tile_weight(to_dev(q))).reshape(-1)
+    for n in (0, 5, 17, 31):
+        for kk in (0, 37, 100, 255):                       # K index, byte kk // 2
+            c, g, r = kk // 128, (kk % 128) // 32, n % 16
+            off = ((n // 16) * 2 + c) * 1024 + (r + 16 * g) * 16 + (kk % 32) // 2
+            assert t[off] == q[0, n, kk // 2]
+
+
 def _quantised(spec):
-    """GPU-quantised weights (checked bit-exactly against the oracle's) and the oracle's."""
+    """GPU-quantised weights (checked bit-exactly against the oracle's), tiled for the layer,
+    and the oracle's."""
     dev, ref = [], []
     for which in ("gate", "up", "down"):
         m = synth.gen_expert_weight(spec, which)
@@ -76,7 +102,7 @@ def _quantised(spec):
         qr, sr = oracle.quantize_weight_mxfp4(m)
         np.testing.assert_array_equal(to_host(q), qr)
         np.testing.assert_array_equal(to_host(s), sr)
-        dev.append((q, s))
+        dev.append((moe.fp4_tile_weight(q), s))
         ref.append((qr, sr))
     return dev, ref
 
@@ -161,7 +187,7 @@ def test_mixtral_fp4_decode_full_sampled():
             oq, os_ = oracle.quantize_weight_mxfp4(synth.bf16_bits_to_f32(bits))
             np.testing.assert_array_equal(to_host(q), oq)
             np.testing.assert_array_equal(to_host(s), os_)
-            qt[e], st[e], rq[e], rs[e] = q[0], s[0], oq[0], os_[0]
+            qt[e], st[e], rq[e], rs[e] = moe.fp4_tile_weight(q)[0], s[0], oq[0], os_[0]
         dev_q[which], dev_s[which] = qt, st
         ref_q[which], ref_s[which] = rq, rs
     log("weights quantised; running the fp4 decode layer")
