@@ -155,16 +155,29 @@ class Layer:
         return sum(g1) / n, sum(g2) / n
 
 
-def time_steps(layer, steps, warmup):
+def time_steps(layer, steps, warmup, events=True):
+    """Wall time of ``steps`` steps after ``warmup``. events=True records the per-kernel HIP events
+    inside the timed steps; each record sits between two kernels on the stream and costs a few
+    microseconds, so short steps are timed without them (see kernel_pass)."""
     import torch
     for _ in range(warmup):
         layer.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        layer.step(ev_index=i)
+        layer.step(ev_index=i if events else None)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def kernel_pass(layer, steps):
+    """Per-kernel durations (gate/up incl. any h quantisation, down) over ``steps`` further steps
+    with HIP events."""
+    import torch
+    for i in range(steps):
+        layer.step(ev_index=i)
+    torch.cuda.synchronize()
+    return layer.kernel_ms(steps)
 
 
 def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
@@ -239,8 +252,8 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
     log("%s inputs ready in %.1fs" % (name, time.perf_counter() - t0))
     layer = Layer(moe, spec, x, tuple(W), steps, logits=logits, scales=scales,
                   scale_fmt=scale_fmt)
-    el = time_steps(layer, steps, warmup)
-    g1, g2 = layer.kernel_ms(steps)
+    el = time_steps(layer, steps, warmup, events=False)
+    g1, g2 = kernel_pass(layer, steps)
     counts = layer.counts.cpu().numpy()
     touched = int((counts > 0).sum())
     wbytes = {"f32": 4, "bf16": 2, "fp8": 1}[spec.dtype]
@@ -283,8 +296,8 @@ def measure_decode_fp8(moe, synth, W, Wr, steps, warmup, scale_fmt, fp4=False):
         S.append(s_)
     xd = torch.from_numpy(synth.gen_x(synth.MIXTRAL_DECODE).view("int16")).cuda().view(torch.bfloat16)
     layer = Layer(moe, dspec, xd, tuple(Q), steps, Wr=Wr, scales=tuple(S), scale_fmt=scale_fmt)
-    el = time_steps(layer, steps, warmup)
-    g1, g2 = layer.kernel_ms(steps)
+    el = time_steps(layer, steps, warmup, events=False)
+    g1, g2 = kernel_pass(layer, steps)
     touched = int((layer.counts.cpu().numpy() > 0).sum())
     ms = el / steps * 1e3
     per_w = 0.5 + 1 / 32 if fp4 else 1.0   # streamed bytes per weight (E2M1 codes + MX scales)
@@ -411,9 +424,9 @@ def main():
         dspec = synth.MIXTRAL_DECODE
         xd = up(synth.gen_x(dspec))
         dl = Layer(moe, dspec, xd, (Wg, Wu, Wd), args.decode_steps, Wr=Wr)
-        eld = time_steps(dl, args.decode_steps, 5)
+        eld = time_steps(dl, args.decode_steps, 5, events=False)
         dms = eld / args.decode_steps * 1e3
-        d1, d2 = dl.kernel_ms(args.decode_steps)
+        d1, d2 = kernel_pass(dl, args.decode_steps)
         dcounts = dl.counts.cpu().numpy()
         touched = int((dcounts > 0).sum())
         w_bytes_gu = touched * 2 * f * d * 2

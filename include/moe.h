@@ -283,6 +283,56 @@ moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
                        void* out, moe_dtype out_dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * moe_fused_forward - the whole layer for small batches (decode) in three launches: routing (+ x
+ * quantisation), the gate/up projection (+ h quantisation), the down projection (+ weighting and
+ * combine). The single fused MoE kernel of the AWS fused-MoE news page (routing, both expert
+ * projections and the combine in one kernel) as far as it goes without a grid-wide barrier: the
+ * launches hand over through stream order and per-group completion counters, and no permutation
+ * is materialised (each expert's workgroups find its pairs in topk_ids). Computes what
+ * moe_route + moe_permute (+ fp8_quantize_act) + moe_experts_forward (slots) + moe_combine compute,
+ * with the same arithmetic, so the outputs are bit-identical to that sequence.
+ *
+ *  T*k <= 256 pairs (MOE_ERR_UNSUPPORTED otherwise); d % 128 == f % 128 == 0; E <= 1024, k <= E.
+ *  x [T, d] (MOE_BF16, or MOE_F32 with fp8 / FP4 experts), 16-byte aligned.
+ *  logits [T, E] fp32 router logits, or NULL: computed as x . w_router^T (w_router [E, d] fp32,
+ *    16-byte aligned), and written to logits_out [T, E] when that is non-NULL.
+ *  w_dtype / scale_fmt and the weight and scale arrays: as for moe_experts_forward (MOE_BF16 with
+ *    bf16 x; MOE_FP8_E4M3 with fp32 or UE8M0 block scales; MOE_FP4_E2M1 in fragment order with MX
+ *    scales, UE8M0 only); fp8 / FP4 quantise x per token per 128 channels here.
+ *  out [T, d] (out_dtype MOE_BF16 or MOE_F32); topk_ids / topk_w [T, k] out (required).
+ *  workspace: >= moe_fused_workspace_size(...) bytes, caller-owned, any contents; calls that share
+ *    a workspace must not overlap on the device. Device errors: MOE_ERR_DEVICE.
+ * ------------------------------------------------------------------------------------------ */
+typedef struct {
+  int T, d, f, E, k;
+  moe_dtype x_dtype;
+  moe_dtype w_dtype;
+  moe_scale_fmt scale_fmt;
+  const void* x;                 /* [T, d] */
+  const float* logits;           /* [T, E] or NULL (router GEMM) */
+  const float* w_router;         /* [E, d] fp32, used when logits == NULL */
+  float* logits_out;             /* nullable [T, E] */
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
+  void* out;                     /* [T, d] */
+  moe_dtype out_dtype;
+  int32_t* topk_ids;             /* [T, k] out */
+  float* topk_w;                 /* [T, k] out */
+  void* workspace;
+  size_t workspace_bytes;
+} moe_fused_args;
+
+moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream);
+
+/* Bytes of workspace moe_fused_forward needs (0 for unsupported sizes). */
+size_t moe_fused_workspace_size(int T, int d, int f, int E, int k, moe_dtype w_dtype,
+                                moe_dtype out_dtype);
+
+/* ------------------------------------------------------------------------------------------
  * Timing helpers (thin wrappers over HIP events, for callers without their own HIP bindings).
  * ------------------------------------------------------------------------------------------ */
 moe_status moe_event_create(void** event);

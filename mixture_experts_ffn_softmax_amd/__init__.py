@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "fp8_quantize_act", "fp8_quantize_weight", "fp8_quantize_act_ue8m0",
     "fp8_quantize_weight_ue8m0", "fp4_quantize_weight_mx", "fp4_tile_weight",
     "moe_experts_forward",
-    "moe_experts_workspace_size", "moe_combine", "moe_event_create", "moe_event_destroy",
+    "moe_experts_workspace_size", "moe_combine", "moe_fused_forward", "moe_fused_workspace_size",
+    "moe_event_create", "moe_event_destroy",
     "moe_event_record", "moe_event_elapsed_ms",
 )
 
@@ -55,6 +56,21 @@ class moe_experts_args(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("events", ctypes.c_void_p),
         ("scale_fmt", ctypes.c_int),
+    ]
+
+
+class moe_fused_args(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int), ("d", ctypes.c_int), ("f", ctypes.c_int), ("E", ctypes.c_int),
+        ("k", ctypes.c_int),
+        ("x_dtype", ctypes.c_int), ("w_dtype", ctypes.c_int), ("scale_fmt", ctypes.c_int),
+        ("x", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
+        ("logits_out", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int),
+        ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -91,6 +107,8 @@ def load_library(path: str = LIB_PATH):
         "moe_experts_forward": ([ctypes.POINTER(moe_experts_args), vp], st),
         "moe_experts_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "moe_combine": ([vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp], st),
+        "moe_fused_forward": ([ctypes.POINTER(moe_fused_args), vp], st),
+        "moe_fused_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "moe_event_create": ([ctypes.POINTER(ctypes.c_void_p)], st),
         "moe_event_destroy": ([vp], st),
         "moe_event_record": ([vp, vp], st),
@@ -343,6 +361,42 @@ def moe_combine(y, layout: str, T: int, k: int, d: int, pair_pos=None, topk_w=No
 
 
 # ---- events ----------------------------------------------------------------------------------
+
+def moe_fused_forward(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, s_gate=None,
+                      s_up=None, s_down=None, w_fp4: bool = False, out_dtype=None,
+                      workspace=None, out=None, logits_out=None):
+    """The whole layer for small batches (T*k <= 256) in three launches (moe_fused_forward).
+    Weights as for moe_layer (bf16; uint8 e4m3 codes with fp32 or uint8 (UE8M0) block scales; with
+    w_fp4, E2M1 codes in fragment order with MX scales). Returns (out [T, d], topk_ids, topk_w)."""
+    lib = load_library()
+    for t in (x, w_gate, w_up, w_down, logits, w_router, s_gate, s_up, s_down):
+        _contig(t)
+    T, d = x.shape
+    E, f = w_gate.shape[0], w_gate.shape[1]
+    if w_fp4:
+        wdt = MOE_FP4_E2M1
+    elif w_gate.dtype in (torch.uint8, torch.float8_e4m3fn):
+        wdt = MOE_FP8_E4M3
+    else:
+        wdt = _dtype_code(w_gate)
+    fmt = "ue8m0" if s_gate is not None and s_gate.dtype == torch.uint8 else "f32"
+    if out_dtype is None:
+        out_dtype = torch.float32 if x.dtype == torch.float32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=x.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    nbytes = lib.moe_fused_workspace_size(T, d, f, E, k, wdt, _dtype_code(out))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    p = lambda t: t.data_ptr() if t is not None else None
+    a = moe_fused_args(T, d, f, E, k, _dtype_code(x), wdt, _SCALE_FMTS[fmt], p(x), p(logits),
+                       p(w_router), p(logits_out), p(w_gate), p(w_up), p(w_down), p(s_gate),
+                       p(s_up), p(s_down), p(out), _dtype_code(out), p(ids), p(w),
+                       p(workspace), workspace.numel())
+    _check(lib.moe_fused_forward(ctypes.byref(a), _stream()))
+    return out, ids, w
+
 
 def event_create():
     h = ctypes.c_void_p()

@@ -382,6 +382,136 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   return dev(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+struct FusedLayout {
+  size_t h_cnt, c_cnt, xq, xs, h, h32, hq, hs, slots, total;
+  size_t ncnt;   // ints from h_cnt to the end of c_cnt
+};
+
+FusedLayout fused_layout(int T, int d, int f, int E, int k, moe_dtype w, moe_dtype out) {
+  FusedLayout L{};
+  const size_t P = static_cast<size_t>(T) * k;
+  const bool lowp = is_low_precision(w);
+  size_t off = 0;
+  L.h_cnt = off;
+  off += static_cast<size_t>(E) * (f / kFp8Group) * sizeof(int);
+  L.c_cnt = off;
+  off += static_cast<size_t>(T) * (d / 64) * sizeof(int);
+  L.ncnt = off / sizeof(int);
+  off = align_up(off);
+  L.xq = L.xs = L.h32 = L.hq = 0;
+  if (lowp) {
+    L.xq = off;
+    off = align_up(off + static_cast<size_t>(T) * d);
+    L.xs = off;
+    off = align_up(off + static_cast<size_t>(T) * (d / kFp8Group) * sizeof(float));
+    L.h32 = off;
+    off = align_up(off + P * f * sizeof(float));
+    L.hq = off;
+    off = align_up(off + P * f);
+    L.hs = off;
+    off = align_up(off + P * (f / kFp8Group) * sizeof(float));
+  } else {
+    L.h = off;
+    off = align_up(off + P * f * 2);
+  }
+  L.slots = off;
+  off = align_up(off + P * d * (out == MOE_F32 ? 4 : 2));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_fused_workspace_size(int T, int d, int f, int E, int k, moe_dtype w_dtype,
+                                moe_dtype out_dtype) {
+  if (check_topology(T, E, k) != MOE_OK || d < 1 || f < 1) return 0;
+  if (static_cast<long long>(T) * k > kFusedMaxPairs || d % kFp8Group || f % kFp8Group) return 0;
+  return fused_layout(T, d, f, E, k, w_dtype, out_dtype).total;
+}
+
+moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
+  if (!a) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status st = check_topology(a->T, a->E, a->k);
+  if (st != MOE_OK) return st;
+  if (a->d < 1 || a->f < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!a->x || !a->w_gate || !a->w_up || !a->w_down || !a->out || !a->topk_ids || !a->topk_w)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!a->logits && !a->w_router) return MOE_ERR_INVALID_ARGUMENT;
+  if (a->out_dtype != MOE_BF16 && a->out_dtype != MOE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (a->x_dtype != MOE_BF16 && a->x_dtype != MOE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (a->scale_fmt != MOE_SCALE_F32 && a->scale_fmt != MOE_SCALE_UE8M0)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const moe_dtype w = a->w_dtype;
+  const bool lowp = is_low_precision(w);
+  const bool ue8m0 = a->scale_fmt == MOE_SCALE_UE8M0;
+  if (w != MOE_BF16 && !lowp) return MOE_ERR_UNSUPPORTED;
+  if (w == MOE_BF16 && (a->x_dtype != MOE_BF16 || ue8m0)) return MOE_ERR_UNSUPPORTED;
+  if (w == MOE_FP4_E2M1 && !ue8m0) return MOE_ERR_UNSUPPORTED;
+  if (lowp && (!a->s_gate || !a->s_up || !a->s_down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (w == MOE_FP4_E2M1 &&
+      (!aligned(a->s_gate, 4) || !aligned(a->s_up, 4) || !aligned(a->s_down, 4)))
+    return MOE_ERR_UNSUPPORTED;
+  const long long P = static_cast<long long>(a->T) * a->k;
+  if (P > kFusedMaxPairs) return MOE_ERR_UNSUPPORTED;
+  if (a->d % kFp8Group || a->f % kFp8Group) return MOE_ERR_UNSUPPORTED;
+  if (a->d > 32768 || a->f > 32768) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(a->x, 16) || (!a->logits && !aligned(a->w_router, 16))) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<long long>(a->f) * a->d > INT_MAX / 4) return MOE_ERR_UNSUPPORTED;
+  const FusedLayout L = fused_layout(a->T, a->d, a->f, a->E, a->k, w, a->out_dtype);
+  if (!a->workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  char* ws = static_cast<char*>(a->workspace);
+  int* cnt = reinterpret_cast<int*>(ws + L.h_cnt);
+  uint8_t* xq = lowp ? reinterpret_cast<uint8_t*>(ws + L.xq) : nullptr;
+  float* xs = lowp ? reinterpret_cast<float*>(ws + L.xs) : nullptr;
+  hipError_t e = launch_fused_route(a->x, a->x_dtype, a->logits, a->w_router, a->logits_out, a->T,
+                                    a->d, a->E, a->k, a->topk_ids, a->topk_w, xq, xs, ue8m0, cnt,
+                                    L.ncnt, stream);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+
+  ExpertsLaunch X{};
+  X.T = a->T;
+  X.d = a->d;
+  X.f = a->f;
+  X.E = a->E;
+  X.k = a->k;
+  X.a = lowp ? static_cast<const void*>(xq) : a->x;
+  X.a_gather = 1;
+  X.a_scales = xs;
+  X.w_gate = a->w_gate;
+  X.w_up = a->w_up;
+  X.w_down = a->w_down;
+  X.s_gate = a->s_gate;
+  X.s_up = a->s_up;
+  X.s_down = a->s_down;
+  X.scale_ue8m0 = ue8m0 ? 1 : 0;
+  X.w_fp4 = w == MOE_FP4_E2M1 ? 1 : 0;
+  X.topk_w = a->topk_w;
+  X.y_layout = MOE_Y_SLOTS;
+  X.y_bf16 = a->out_dtype == MOE_BF16;
+  X.y = ws + L.slots;
+  X.h = lowp ? nullptr : ws + L.h;
+  X.h32 = lowp ? reinterpret_cast<float*>(ws + L.h32) : nullptr;
+  X.hq = lowp ? reinterpret_cast<uint8_t*>(ws + L.hq) : nullptr;
+  X.h_scales = lowp ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
+  X.pair_ids = a->topk_ids;
+  X.h_cnt = reinterpret_cast<int*>(ws + L.h_cnt);
+  X.c_cnt = reinterpret_cast<int*>(ws + L.c_cnt);
+  X.out = a->out;
+  X.out_bf16 = a->out_dtype == MOE_BF16;
+  X.cpx = cus_per_xcd();
+  e = lowp ? launch_experts_fp8_decode(X, stream) : launch_experts_bf16_decode(X, stream);
+  if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
+  return dev(e);
+}
+
 moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
                        const int32_t* pair_pos, const float* topk_w, int T, int k, int d,
                        void* out, moe_dtype out_dtype, hipStream_t stream) {

@@ -289,6 +289,83 @@ __device__ __forceinline__ bool map_cut_tile(const int32_t* __restrict__ tile_cu
   return true;
 }
 
+// ---- helpers of the fused small-batch path ----------------------------------------------------
+
+// The pairs (flat index t * k + j) routed to expert e, in ascending order, found by one workgroup
+// of NT threads in ids[0 .. P): written to list[0 .. M) (LDS), M returned to every thread.
+// wsum: LDS scratch of NT / 64 ints. Ends with a barrier, so list is ready for the whole group.
+template <int NT>
+__device__ int expert_pair_list(const int32_t* __restrict__ ids, int P, int e, int32_t* list,
+                                int* wsum) {
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  int total = 0;
+  for (int base = 0; base < P; base += NT) {
+    const int i = base + static_cast<int>(threadIdx.x);
+    const bool hit = i < P && ids[i] == e;
+    const uint64_t m = __ballot(hit);
+    if (lane == 0) wsum[w] = __popcll(m);
+    __syncthreads();
+    int off = total, tot = 0;
+#pragma unroll
+    for (int v = 0; v < NT / kWave; ++v) {
+      off += v < w ? wsum[v] : 0;
+      tot += wsum[v];
+    }
+    if (hit) list[off + __popcll(m & ((1ull << lane) - 1ull))] = i;
+    total += tot;
+    __syncthreads();
+  }
+  return total;
+}
+
+// One 128-wide fp8 group held by 16 consecutive lanes, 8 values each (lane & 15 = position): the
+// group's amax over the 16 lanes, then the e4m3 codes of this lane's 8 values (lo: values 0..3,
+// hi: 4..7) by the fp32 rule (s = amax / 448, code = e4m3(v / s), s = 1 for a zero group) or the
+// UE8M0 rule (byte b, code = e4m3(v * 2^(127 - b))). Returns the scale's value (UE8M0: 2^(b - 127));
+// *byte gets b. Every lane of the 16 must call it.
+template <bool kUE>
+__device__ __forceinline__ float quant_group16(const float (&v)[8], uint32_t& lo, uint32_t& hi,
+                                               int* byte) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  lo = hi = 0;
+  if constexpr (kUE) {
+    const int b = ue8m0_byte(amax);
+    const float inv = ldexpf(1.0f, 127 - b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] * inv) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] * inv) << (8 * i);
+    *byte = b;
+    return ldexpf(1.0f, b - 127);
+  } else {
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / s) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / s) << (8 * i);
+    *byte = 0;
+    return s;
+  }
+}
+
+// Hand-off between workgroups of one launch: every thread has stored what it produced; after this
+// the group's stores are visible device-wide (each XCD has its own L2) and, in the one group that
+// brings counter *cnt to n, the other groups' stores are visible to all of its threads. Returns
+// true in that last group (uniform over the workgroup). flag: LDS int.
+__device__ __forceinline__ bool last_arrival(int* cnt, int n, int* flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = atomicAdd(cnt, 1) == n - 1;
+  __syncthreads();
+  const bool last = *flag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
 // Blocks to launch for map_work: per XCD at most chunk whole tiles plus cpx tail pieces.
 inline unsigned work_grid(long max_tiles, int cpx) {
   return static_cast<unsigned>(((max_tiles + 7) / 8 + cpx) * 8);

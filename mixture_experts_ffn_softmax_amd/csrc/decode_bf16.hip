@@ -49,6 +49,12 @@ struct DecodeArgs {
   const float* topk_w;
   int small_max;              // experts with at most this many tokens belong to the streaming
                               // kernel (0: this kernel takes every expert)
+  // fused small-batch path (see ExpertsLaunch): routing ids [P]; down: combine into out
+  const int32_t* ids;
+  int P;
+  int* c_cnt;
+  void* out;
+  int out_bf16;
 };
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
@@ -59,15 +65,26 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int MODE>
+// kFused: the fused small-batch path (pairs from the routing ids; the down kernel combines).
+template <int MODE, bool kFused>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
   constexpr int kRows = MODE == kGateUp ? kDecodeGateRows : kDecodeDownRows;
   const int nrb = (p.N + kRows - 1) / kRows;
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
-  const int row0 = p.offsets[e];
-  const int M = p.offsets[e + 1] - row0;
+  __shared__ int32_t plist[kFused ? kFusedMaxPairs : 1];   // fused: this expert's pairs
+  __shared__ int hand[kWave];                 // fused: per-token "last slot" flags, scratch
+  int row0, M;
+  if constexpr (kFused) {
+    row0 = 0;
+    M = expert_pair_list<256>(p.ids, p.P, e, plist, hand);
+  } else {
+    row0 = p.offsets[e];
+    M = p.offsets[e + 1] - row0;
+  }
   if (M <= p.small_max) return;  // empty, or the streaming kernel's expert
+  auto pos_of = [&](int i) { return kFused ? plist[i] : row0 + i; };
+  auto pair_of = [&](int i) { return kFused ? plist[i] : p.sorted_pair[row0 + i]; };
 
   __shared__ f32x4_t red[4][4][4][64];  // [wave][row group][token group][lane], 64 KB
 
@@ -98,8 +115,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       const int ti = min(tc0 + tg * 16 + r16, M - 1);
-      const int pos = row0 + ti;
-      const int src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+      const int pos = pos_of(ti);
+      const int src = p.a_gather ? pair_of(ti) / p.k : pos;
       brow[tg] = p.a + static_cast<size_t>(src) * p.K + g * 32;
     }
     f32x4_t acc[4][4];
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
       for (int rg = 0; rg < 4; ++rg)
         s[rg] = red[0][rg][tg][lane] + red[1][rg][tg][lane] + red[2][rg][tg][lane] +
                 red[3][rg][tg][lane];
-      const int pos = row0 + ti;
+      const int pos = pos_of(ti);
       if (MODE == kGateUp) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -162,7 +179,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
           }
         }
       } else {
-        const int pair = p.sorted_pair[pos];
+        const int pair = pair_of(ti);
         const float wgt = p.topk_w ? p.topk_w[pair] : 1.0f;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
@@ -193,6 +210,34 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
         }
       }
     }
+    if constexpr (kFused && MODE == kDown) {
+      // Every token of this pass has its slot's 64 channels written; the last of a token's k
+      // slots to arrive (per 64-channel panel) sums the k slots in slot order into out.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      const int npass = min(kDecodeTokens, M - tc0);
+      if (tid < npass) {
+        const int t = plist[tc0 + tid] / p.k;
+        hand[tid] = atomicAdd(p.c_cnt + static_cast<size_t>(t) * nrb + rb, 1) == p.k - 1;
+      }
+      __syncthreads();
+      for (int i = wave; i < npass; i += 4) {
+        if (!hand[i]) continue;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const int t = plist[tc0 + i] / p.k;
+        const int n = rb * kRows + lane;
+        if (n >= p.N) continue;
+        float acc = 0.0f;
+        for (int j = 0; j < p.k; ++j) {
+          const size_t idx = (static_cast<size_t>(t) * p.k + j) * p.N + n;
+          acc += p.y_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.y)[idx])
+                          : static_cast<const float*>(p.y)[idx];
+        }
+        const size_t o = static_cast<size_t>(t) * p.N + n;
+        if (p.out_bf16) static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(acc);
+        else static_cast<float*>(p.out)[o] = acc;
+      }
+    }
     __syncthreads();
   }
 }
@@ -216,7 +261,7 @@ __device__ __forceinline__ void str_dma(const char* slot, const uint32_t (&voff)
     dma16(base + i * 1024, voff[i], i >= KS / 64 ? rsrc1 : rsrc0, kb);  // rows 8..15: W_up
 }
 
-template <int KS>
+template <int KS, bool kFused>
 __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   constexpr int kStage = kStrRows * KS * 2;        // bytes per slot
   constexpr int kCpr = KS / 8;                     // 16-byte chunks per row per stage
@@ -226,8 +271,16 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   const int nrb = (p.N + kOut - 1) / kOut;
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
-  const int row0 = p.offsets[e];
-  const int M = p.offsets[e + 1] - row0;
+  __shared__ int32_t plist[kFused ? kFusedMaxPairs : 1];   // fused: this expert's pairs
+  __shared__ int wsum[1];
+  int row0, M;
+  if constexpr (kFused) {
+    row0 = 0;
+    M = expert_pair_list<64>(p.ids, p.P, e, plist, wsum);
+  } else {
+    row0 = p.offsets[e];
+    M = p.offsets[e + 1] - row0;
+  }
   if (M == 0 || M > 16) return;
 
   __shared__ __attribute__((aligned(1024))) char ring[kStrRing * kStage];
@@ -249,8 +302,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   }
   // token operand: lane (t = l % 16, g = l / 16) holds k = 32 u + 8 g .. +7 of token t
   const int t = min(r16, M - 1);
-  const int pos = row0 + t;
-  const int src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+  const int pos = kFused ? plist[t] : row0 + t;
+  const int src = p.a_gather ? (kFused ? plist[t] : p.sorted_pair[pos]) / p.k : pos;
   const uint16_t* trow = p.a + static_cast<size_t>(src) * p.K + g * 8;
 
   const int nst = p.K / KS;
@@ -306,7 +359,8 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
          (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[1], up[1]))) << 16);
   o[1] = f32_to_bf16_bits(silu_mul(acc[2], up[2])) |
          (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[3], up[3]))) << 16);
-  *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(row0 + r16) * p.N + n) = o;
+  const int hrow = kFused ? plist[r16] : row0 + r16;
+  *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(hrow) * p.N + n) = o;
 }
 
 }  // namespace
@@ -315,6 +369,8 @@ constexpr int kStrK = 256;  // K per stage of the streaming kernel
 
 
 hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream) {
+  const bool fused = L.pair_ids != nullptr;
+  const int P = L.T * L.k;
   DecodeArgs g{};
   g.a = static_cast<const uint16_t*>(L.a);
   g.a_gather = L.a_gather;
@@ -326,16 +382,26 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   g.N = L.f;
   g.offsets = L.offsets;
   g.h = static_cast<uint16_t*>(L.h);
+  g.ids = L.pair_ids;
+  g.P = P;
   const unsigned grid1 = static_cast<unsigned>(L.E) * ((L.f + kDecodeGateRows - 1) / kDecodeGateRows);
   // the streaming kernel needs whole K stages
   const bool stream_small = L.d % kStrK == 0;
   g.small_max = stream_small ? 16 : 0;
   const unsigned grid1s = static_cast<unsigned>(L.E) * ((L.f + 7) / 8);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  if (stream_small)
-    hipLaunchKernelGGL(decode_stream_kernel<kStrK>, dim3(grid1s), dim3(64), 0, stream, g);
-  hipLaunchKernelGGL(decode_bf16_kernel<kGateUp>, dim3(grid1), dim3(256), 0, stream, g);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
+  if (stream_small) {
+    if (fused)
+      hipLaunchKernelGGL((decode_stream_kernel<kStrK, true>), dim3(grid1s), dim3(64), 0, stream, g);
+    else
+      hipLaunchKernelGGL((decode_stream_kernel<kStrK, false>), dim3(grid1s), dim3(64), 0, stream,
+                         g);
+  }
+  if (fused)
+    hipLaunchKernelGGL((decode_bf16_kernel<kGateUp, true>), dim3(grid1), dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<kGateUp, false>), dim3(grid1), dim3(256), 0, stream, g);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
 
   DecodeArgs dn{};
   dn.a = static_cast<const uint16_t*>(L.h);
@@ -352,9 +418,17 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   dn.topk_w = L.topk_w;
   const unsigned grid2 = static_cast<unsigned>(L.E) * ((L.d + kDecodeDownRows - 1) / kDecodeDownRows);
   dn.small_max = 0;  // the K-split kernel takes every expert of the down GEMM
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  hipLaunchKernelGGL(decode_bf16_kernel<kDown>, dim3(grid2), dim3(256), 0, stream, dn);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
+  dn.ids = L.pair_ids;
+  dn.P = P;
+  dn.c_cnt = L.c_cnt;
+  dn.out = L.out;
+  dn.out_bf16 = L.out_bf16;
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
+  if (fused)
+    hipLaunchKernelGGL((decode_bf16_kernel<kDown, true>), dim3(grid2), dim3(256), 0, stream, dn);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<kDown, false>), dim3(grid2), dim3(256), 0, stream, dn);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return hipGetLastError();
 }
 

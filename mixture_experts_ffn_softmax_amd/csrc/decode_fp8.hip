@@ -57,6 +57,15 @@ struct Fp8DecodeArgs {
   void* y;                    // down output
   int y_layout, y_bf16;
   const float* topk_w;
+  // fused small-batch path (see ExpertsLaunch)
+  const int32_t* ids;         // routing ids [P]
+  int P;
+  uint8_t* hq;                // gate/up: h codes [P, N] and scales hs [P, N/128] (fp32 values)
+  float* hs;
+  int* h_cnt;
+  int* c_cnt;
+  void* out;                  // down: combined output [T, N]
+  int out_bf16;
 };
 
 __device__ __forceinline__ i32x8_t ld16x2g(const uint8_t* p, const uint8_t* q) {
@@ -78,16 +87,28 @@ __device__ __forceinline__ i32x8_t ld16g(const uint8_t* p) {
 
 // kW4: E2M1 weights with per-32 MX scales (implies kUE). kTG: groups of 16 tokens per pass over
 // the weights (fewer groups hold fewer registers and less LDS, so more waves stream at once).
-template <int MODE, bool kUE, bool kW4, int kTG>
+// kFused: the fused small-batch path (pairs from the routing ids, hand-offs at the end).
+template <int MODE, bool kUE, bool kW4, int kTG, bool kFused>
 __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
   constexpr int kTokens = 16 * kTG;
   const int nrb = (p.N + kRows - 1) / kRows;
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
-  const int row0 = p.offsets[e];
-  const int M = p.offsets[e + 1] - row0;
+  __shared__ int32_t plist[kFused ? kFusedMaxPairs : 1];   // fused: this expert's pairs
+  __shared__ int hand[kWave];                 // fused: per-token "last slot" flags, scratch
+  int row0, M;
+  if constexpr (kFused) {
+    row0 = 0;
+    M = expert_pair_list<256>(p.ids, p.P, e, plist, hand);
+  } else {
+    row0 = p.offsets[e];
+    M = p.offsets[e + 1] - row0;
+  }
   if (M <= 0) return;
+  // i-th token row of this expert: its h / slot row (pos) and its pair (t * k + j)
+  auto pos_of = [&](int i) { return kFused ? plist[i] : row0 + i; };
+  auto pair_of = [&](int i) { return kFused ? plist[i] : p.sorted_pair[row0 + i]; };
 
   __shared__ f32x4_t red[4][4][kTG][64];  // [wave][row group][token group][lane], 16 KB each
   // Weight scales for every K block, staged once: 128x128 blocks, one per row group (fp32 bits
@@ -161,8 +182,8 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
 #pragma unroll
     for (int tg = 0; tg < kTG; ++tg) {
       const int ti = min(tc0 + tg * 16 + r16, M - 1);
-      const int pos = row0 + ti;
-      const int src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+      const int pos = pos_of(ti);
+      const int src = p.a_gather ? pair_of(ti) / p.k : pos;
       brow[tg] = p.a + static_cast<size_t>(src) * p.K + g * 16;
       bscale[tg] = p.a_s + static_cast<size_t>(src) * KB;
     }
@@ -235,7 +256,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
       for (int rg = 0; rg < 4; ++rg)
         s[rg] = red[0][rg][tg][lane] + red[1][rg][tg][lane] + red[2][rg][tg][lane] +
                 red[3][rg][tg][lane];
-      const int pos = row0 + ti;
+      const int pos = pos_of(ti);
       if (MODE == kGateUp) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -248,7 +269,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
           }
         }
       } else {
-        const int pair = p.sorted_pair[pos];
+        const int pair = pair_of(ti);
         const float wgt = p.topk_w ? p.topk_w[pair] : 1.0f;
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
@@ -279,19 +300,65 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
         }
       }
     }
+    if constexpr (kFused && MODE == kDown) {
+      // Every token of this pass has its slot's 64 channels written; the last of a token's k
+      // slots to arrive (per 64-channel panel) sums the k slots in slot order into out.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      const int npass = min(kTokens, M - tc0);
+      if (tid < npass) {
+        const int t = plist[tc0 + tid] / p.k;
+        hand[tid] = atomicAdd(p.c_cnt + static_cast<size_t>(t) * nrb + rb, 1) == p.k - 1;
+      }
+      __syncthreads();
+      for (int i = wave; i < npass; i += 4) {
+        if (!hand[i]) continue;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const int t = plist[tc0 + i] / p.k;
+        const int n = rb * kRows + lane;
+        if (n >= p.N) continue;
+        float acc = 0.0f;
+        for (int j = 0; j < p.k; ++j) {
+          const size_t idx = (static_cast<size_t>(t) * p.k + j) * p.N + n;
+          acc += p.y_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.y)[idx])
+                          : static_cast<const float*>(p.y)[idx];
+        }
+        const size_t o = static_cast<size_t>(t) * p.N + n;
+        if (p.out_bf16) static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(acc);
+        else static_cast<float*>(p.out)[o] = acc;
+      }
+    }
     __syncthreads();
+  }
+  if constexpr (kFused && MODE == kGateUp) {
+    // The groups rb = 4j .. 4j + 3 write h channels [128 j, 128 j + 128) of this expert's pairs
+    // (fp32); the last of them to finish quantises that group of every pair.
+    if (last_arrival(p.h_cnt + static_cast<size_t>(e) * (p.N / 128) + rb / 4, 4, hand)) {
+      const int c0 = (rb / 4) * 128 + (tid & 15) * 8;
+      for (int i = tid / 16; i < M; i += 16) {   // 16 lanes per pair row
+        const size_t r = static_cast<size_t>(plist[i]);
+        const f32x4_t lo4 = *reinterpret_cast<const f32x4_t*>(p.h32 + r * p.N + c0);
+        const f32x4_t hi4 = *reinterpret_cast<const f32x4_t*>(p.h32 + r * p.N + c0 + 4);
+        const float v[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        uint32_t lo, hi;
+        int byte;
+        const float sc = quant_group16<kUE>(v, lo, hi, &byte);
+        *reinterpret_cast<uint2*>(p.hq + r * p.N + c0) = make_uint2(lo, hi);
+        if ((tid & 15) == 0) p.hs[r * (p.N / 128) + rb / 4] = sc;
+      }
+    }
   }
 }
 
-template <int MODE, int kTG>
+template <int MODE, int kTG, bool kF>
 void launch_tg(const Fp8DecodeArgs& a, dim3 grid, bool ue, bool w4, hipStream_t stream) {
   // E2M1: the 64 rows' MX scale bytes, rows padded to an odd number of dwords
   const unsigned mx_lds = static_cast<unsigned>(64 * ((a.K / 128) | 1) * 4);
-  if (w4) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, true, kTG>), grid, dim3(256), mx_lds,
-                             stream, a);
-  else if (ue) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, false, kTG>), grid, dim3(256), 0,
-                                  stream, a);
-  else hipLaunchKernelGGL((decode_fp8_kernel<MODE, false, false, kTG>), grid, dim3(256), 0,
+  if (w4) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, true, kTG, kF>), grid, dim3(256),
+                             mx_lds, stream, a);
+  else if (ue) hipLaunchKernelGGL((decode_fp8_kernel<MODE, true, false, kTG, kF>), grid,
+                                  dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((decode_fp8_kernel<MODE, false, false, kTG, kF>), grid, dim3(256), 0,
                           stream, a);
 }
 
@@ -302,15 +369,22 @@ inline int token_groups(int P, int E) {
   return mean <= 8 ? 1 : (mean <= 24 ? 2 : 4);
 }
 
-template <int MODE>
+template <int MODE, bool kF>
 hipError_t launch_one(const Fp8DecodeArgs& a, int E, int P, bool ue, bool w4, hipStream_t stream) {
   constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
   const dim3 grid(static_cast<unsigned>(E * ((a.N + kRows - 1) / kRows)));
   const int tg = token_groups(P, E);
-  if (tg == 1) launch_tg<MODE, 1>(a, grid, ue, w4, stream);
-  else if (tg == 2) launch_tg<MODE, 2>(a, grid, ue, w4, stream);
-  else launch_tg<MODE, 4>(a, grid, ue, w4, stream);
+  if (tg == 1) launch_tg<MODE, 1, kF>(a, grid, ue, w4, stream);
+  else if (tg == 2) launch_tg<MODE, 2, kF>(a, grid, ue, w4, stream);
+  else launch_tg<MODE, 4, kF>(a, grid, ue, w4, stream);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const Fp8DecodeArgs& a, int E, int P, bool ue, bool w4, bool fused,
+                       hipStream_t stream) {
+  return fused ? launch_one<MODE, true>(a, E, P, ue, w4, stream)
+               : launch_one<MODE, false>(a, E, P, ue, w4, stream);
 }
 
 }  // namespace
@@ -333,13 +407,23 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   g.h32 = L.h32;
   const bool ue = L.scale_ue8m0 != 0;
   const bool w4 = L.w_fp4 != 0;
+  const bool fused = L.pair_ids != nullptr;
   if (w4 && !ue) return hipErrorNotSupported;   // MX scales are e8m0 bytes
+  uint8_t* hq = fused ? L.hq : static_cast<uint8_t*>(L.h);
+  if (fused) {
+    g.ids = L.pair_ids;
+    g.P = P;
+    g.hq = hq;
+    g.hs = L.h_scales;
+    g.h_cnt = L.h_cnt;
+  }
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipError_t e = launch_one<kGateUp>(g, L.E, P, ue, w4, stream);
+  hipError_t e = launch_mode<kGateUp>(g, L.E, P, ue, w4, fused, stream);
   if (e != hipSuccess) return e;
-  // h -> e4m3 codes with per-(pair, 128-channel) scales, as fp32 values for the down kernel
-  uint8_t* hq = static_cast<uint8_t*>(L.h);
-  if (ue) {
+  // h -> e4m3 codes with per-(pair, 128-channel) scales, as fp32 values for the down kernel (the
+  // fused gate/up groups do this themselves)
+  if (fused) {
+  } else if (ue) {
     e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, L.h_scale_bytes, true, stream);
     if (e == hipSuccess)
       e = launch_e8m0_expand(L.h_scale_bytes, static_cast<size_t>(P) * (L.f / 128), L.h_scales,
@@ -365,8 +449,15 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   dn.y_layout = L.y_layout;
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
+  if (fused) {
+    dn.ids = L.pair_ids;
+    dn.P = P;
+    dn.c_cnt = L.c_cnt;
+    dn.out = L.out;
+    dn.out_bf16 = L.out_bf16;
+  }
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  e = launch_one<kDown>(dn, L.E, P, ue, w4, stream);
+  e = launch_mode<kDown>(dn, L.E, P, ue, w4, fused, stream);
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return e;
 }

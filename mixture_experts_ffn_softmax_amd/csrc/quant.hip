@@ -55,29 +55,15 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const XT* __restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
   }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  uint32_t lo, hi;
+  int b;
+  const float s = quant_group16<kUe8m0>(v, lo, hi, &b);
   if (!active) return;
-  uint32_t lo = 0, hi = 0;
-  if constexpr (kUe8m0) {
-    const int b = ue8m0_byte(amax);
-    const float inv = ldexpf(1.0f, 127 - b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] * inv) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] * inv) << (8 * i);
-    if ((lane & 15) == 0)
+  if ((lane & 15) == 0) {
+    if constexpr (kUe8m0)
       static_cast<uint8_t*>(scales)[static_cast<size_t>(row) * G + g] = static_cast<uint8_t>(b);
-  } else {
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_encode(v[i] / s) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_encode(v[4 + i] / s) << (8 * i);
-    if ((lane & 15) == 0) static_cast<float*>(scales)[static_cast<size_t>(row) * G + g] = s;
+    else
+      static_cast<float*>(scales)[static_cast<size_t>(row) * G + g] = s;
   }
   *reinterpret_cast<uint2*>(q + static_cast<size_t>(row) * K + col) = make_uint2(lo, hi);
 }

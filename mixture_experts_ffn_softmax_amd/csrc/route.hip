@@ -5,6 +5,7 @@
 // section 5 (router step by step) and its pseudocode.
 #include "common.h"
 #include "launch.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
@@ -80,29 +81,6 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT* __restrict
 // the wave (32 + 16 + ... + 1 exchanges) leaves the full wave sum of entry l in lane l, and the
 // four waves' sums are added through LDS in wave order.
 constexpr int kVecTokens = 8;
-constexpr int kVecExperts = 8;
-
-template <typename XT>
-__device__ __forceinline__ void load_x8(const XT* p, float (&v)[8]);
-template <>
-__device__ __forceinline__ void load_x8<float>(const float* p, float (&v)[8]) {
-  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    v[c] = a[c];
-    v[4 + c] = b[c];
-  }
-}
-template <>
-__device__ __forceinline__ void load_x8<uint16_t>(const uint16_t* p, float (&v)[8]) {
-  const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    v[2 * c] = __uint_as_float(w[c] << 16);
-    v[2 * c + 1] = __uint_as_float(w[c] & 0xFFFF0000u);
-  }
-}
 
 // One halving step: lanes with bit H set keep entries [H, 2H), the others [0, H); each adds the
 // partner's copy of the kept half, received in exchange for the half it gives away.
@@ -176,61 +154,19 @@ __global__ __launch_bounds__(256) void router_logits_vec_kernel(const XT* __rest
 }
 
 // Few tokens (a decode step): one block per token, so the router weights are read by many CUs at
-// once instead of a handful. Thread j covers x[t][i .. i+8) for i = 8 j + 2048 n against 8 experts
-// at a time; the 8 sums are reduced over each wave and then over the 4 waves in wave order.
+// once instead of a handful.
 template <typename XT>
 __global__ __launch_bounds__(256) void router_logits_tok_kernel(const XT* __restrict__ x,
                                                                 const float* __restrict__ wr,
                                                                 int d, int E,
                                                                 float* __restrict__ logits) {
   __shared__ float red[4][kVecExperts];
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
   const int t = blockIdx.x;
-  for (int e0 = 0; e0 < E; e0 += kVecExperts) {
-    float acc[kVecExperts];
-#pragma unroll
-    for (int b = 0; b < kVecExperts; ++b) acc[b] = 0.0f;
-    for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
-      float xv[8];
-      load_x8<XT>(x + static_cast<size_t>(t) * d + i, xv);
-#pragma unroll
-      for (int b = 0; b < kVecExperts; ++b) {
-        if (e0 + b < E) {
-          float wv[8];
-          load_x8<float>(wr + static_cast<size_t>(e0 + b) * d + i, wv);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[b] = fmaf(xv[c], wv[c], acc[b]);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kVecExperts; ++b) {
-      const float v = wave_sum(acc[b]);
-      if (lane == b) red[wave][b] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < kVecExperts && e0 + threadIdx.x < E) {
-      const int b = threadIdx.x;
-      logits[static_cast<size_t>(t) * E + e0 + b] = ((red[0][b] + red[1][b]) + red[2][b]) + red[3][b];
-    }
-    __syncthreads();
-  }
+  token_logits<XT>(x + static_cast<size_t>(t) * d, wr, d, E, logits + static_cast<size_t>(t) * E,
+                   red);
 }
 
-// "a is a better candidate than b": larger logit, equal logits -> lower expert index;
-// index < 0 means "no candidate".
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  if (ib < 0) return ia >= 0;
-  if (ia < 0) return false;
-  return va > vb || (va == vb && ia < ib);
-}
-
-// Top-k + renormalised softmax weights. A group of G lanes (a power of two: pow2(E) up to 16 lanes,
-// more only when k > 16 so that every pick has its own lane) handles one token; each lane holds
-// VPL logits (expert e = lane_in_group + G * v). k rounds of a lane-local scan plus a butterfly
-// argmax inside the group pick the experts in descending order; the lane whose slot index equals
-// the round keeps the winner, so lane j of the group ends with the j-th selection.
+// Top-k for T tokens: groups of G lanes, one token each (topk_select).
 template <int VPL>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits, int T,
                                                            int E, int k, int G,
@@ -242,42 +178,8 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
   const int t = (blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave) * groups_per_wave +
                 lane / G;
   const bool tok_ok = t < T;
-  float v[VPL];
-  uint64_t taken = 0;
-#pragma unroll
-  for (int q = 0; q < VPL; ++q) {
-    int e = gl + G * q;
-    v[q] = (tok_ok && e < E) ? logits[static_cast<size_t>(t) * E + e] : 0.0f;
-  }
-  float my_v = 0.0f, vmax = 0.0f;
-  int my_i = -1;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int bi = -1;
-#pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-      int e = gl + G * q;
-      bool cand = e < E && !((taken >> q) & 1ull);
-      if (cand && better(v[q], e, bv, bi)) { bv = v[q]; bi = e; }
-    }
-    for (int o = G >> 1; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (j == 0) vmax = bv;
-#pragma unroll
-    for (int q = 0; q < VPL; ++q)
-      if (gl + G * q == bi) taken |= 1ull << q;
-    if (gl == j) { my_v = bv; my_i = bi; }
-  }
-  float a = (gl < k) ? expf(my_v - vmax) : 0.0f;
-  float s = a;
-  for (int o = G >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (tok_ok && gl < k) {
-    ids[static_cast<size_t>(t) * k + gl] = my_i;
-    w[static_cast<size_t>(t) * k + gl] = a / s;
-  }
+  const size_t tt = tok_ok ? static_cast<size_t>(t) : 0;
+  topk_select<VPL>(logits + tt * E, tok_ok, E, k, G, gl, ids + tt * k, w + tt * k);
 }
 
 }  // namespace
@@ -319,10 +221,7 @@ hipError_t launch_router_logits(const void* x, moe_dtype x_dtype, const float* w
 
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                                hipStream_t stream) {
-  int G = 1;
-  while (G < E && G < 16) G <<= 1;
-  while (G < k) G <<= 1;  // k <= 32 <= kWave
-  const int vpl = (E + G - 1) / G;
+  const int G = topk_group_lanes(E, k);
   const int tokens_per_block = 4 * (kWave / G);
   dim3 grid((T + tokens_per_block - 1) / tokens_per_block), block(256);
 #define MOE_TOPK_CASE(N)                                                                      \
@@ -330,7 +229,7 @@ hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t
     hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, block, 0, stream, logits, T, E, k, G, ids, \
                        w);                                                                    \
     break;
-  switch (vpl <= 1 ? 1 : vpl <= 2 ? 2 : vpl <= 4 ? 4 : vpl <= 8 ? 8 : vpl <= 16 ? 16 : vpl <= 32 ? 32 : 64) {
+  switch (topk_vpl(E, G)) {
     MOE_TOPK_CASE(1)
     MOE_TOPK_CASE(2)
     MOE_TOPK_CASE(4)

@@ -181,6 +181,41 @@ def test_experts_validation(lib):
     assert lib.moe_experts_workspace_size(32, 256, 512, 8, 9, moe.MOE_BF16, moe.MOE_BF16) == 0
 
 
+def _fz(lib, **kw):
+    base = dict(T=32, d=256, f=512, E=8, k=2, x_dtype=moe.MOE_BF16, w_dtype=moe.MOE_BF16,
+                scale_fmt=moe.MOE_SCALE_F32, x=0x1000, logits=0x1000, w_router=None,
+                logits_out=None, w_gate=0x1000, w_up=0x1000, w_down=0x1000, s_gate=None,
+                s_up=None, s_down=None, out=0x1000, out_dtype=moe.MOE_BF16, topk_ids=0x1000,
+                topk_w=0x1000, workspace=0x1000, workspace_bytes=1 << 40)
+    base.update(kw)
+    a = moe.moe_fused_args(**base)
+    return lib.moe_fused_forward(ctypes.byref(a), None)
+
+
+def test_fused_validation(lib):
+    INV, UNS = moe.MOE_ERR_INVALID_ARGUMENT, moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fused_forward(None, None) == INV
+    assert _fz(lib, T=129) == UNS                                  # 258 pairs > 256
+    assert _fz(lib, d=192) == UNS                                  # d % 128
+    assert _fz(lib, out=None) == INV
+    assert _fz(lib, topk_ids=None) == INV
+    assert _fz(lib, logits=None) == INV                            # neither logits nor router
+    assert _fz(lib, x=0x1008) == UNS                               # x alignment
+    assert _fz(lib, w_dtype=moe.MOE_F32) == UNS
+    assert _fz(lib, x_dtype=moe.MOE_F32) == UNS                    # bf16 experts take bf16 x
+    assert _fz(lib, out_dtype=moe.MOE_FP8_E4M3) == INV
+    fp8 = dict(w_dtype=moe.MOE_FP8_E4M3, s_gate=0x1000, s_up=0x1000, s_down=0x1000)
+    assert _fz(lib, w_dtype=moe.MOE_FP8_E4M3) == INV               # fp8 needs the scales
+    assert _fz(lib, w_dtype=moe.MOE_FP4_E2M1, s_gate=0x1000, s_up=0x1000,
+               s_down=0x1000) == UNS                               # FP4 needs UE8M0
+    assert _fz(lib, scale_fmt=5, **fp8) == INV
+    assert _fz(lib, workspace=None, **fp8) == INV
+    need = lib.moe_fused_workspace_size(32, 256, 512, 8, 2, moe.MOE_FP8_E4M3, moe.MOE_BF16)
+    assert need > 64 * 512 * 4                                     # at least h in fp32
+    assert _fz(lib, workspace_bytes=need - 1, **fp8) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_fused_workspace_size(129, 256, 512, 8, 2, moe.MOE_BF16, moe.MOE_BF16) == 0
+
+
 def test_combine_validation(lib):
     INV = moe.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_combine(FAKE, moe.MOE_BF16, moe.MOE_Y_PERMUTED, None, FAKE, 4, 2, 64, FAKE,
