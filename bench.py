@@ -316,6 +316,52 @@ def measure_decode_fp8(moe, synth, W, Wr, steps, warmup, scale_fmt, fp4=False):
     return r
 
 
+def measure_fused(moe, synth, W, Wr, steps, warmup, fmt):
+    """The Mixtral-shaped decode layer through moe_fused_forward (one routing kernel with the router
+    GEMM, top-k and x quantisation; no permutation), weights bf16, e4m3 with UE8M0 scales
+    ("ue8m0") or E2M1 with MX scales ("fp4"), quantised on the device."""
+    import torch
+    spec = synth.MIXTRAL_DECODE
+    T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
+    if fmt == "bf16":
+        Q, S, wdt = list(W), [None] * 3, moe.MOE_BF16
+    elif fmt == "fp4":
+        Q, S = zip(*[moe.fp4_quantize_weight_mx(w, tiled=True) for w in W])
+        wdt = moe.MOE_FP4_E2M1
+    else:
+        Q, S = zip(*[moe.fp8_quantize_weight(w, scale_fmt="ue8m0") for w in W])
+        wdt = moe.MOE_FP8_E4M3
+    x = torch.from_numpy(synth.gen_x(spec).view("int16")).cuda().view(torch.bfloat16)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    lib = moe.load_library()
+    ws = torch.empty(lib.moe_fused_workspace_size(T, d, f, E, k, wdt, moe.MOE_BF16),
+                     dtype=torch.uint8, device="cuda")
+    p = lambda t: t.data_ptr() if t is not None else None
+    args = moe.moe_fused_args(T, d, f, E, k, moe.MOE_BF16, wdt,
+                              moe.MOE_SCALE_UE8M0 if fmt != "bf16" else moe.MOE_SCALE_F32,
+                              p(x), None, p(Wr), None, *(p(q) for q in Q), *(p(s_) for s_ in S),
+                              p(out), moe.MOE_BF16, p(ids), p(w), p(ws), ws.numel())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ref = ctypes.byref(args)
+
+    def run(n):
+        for _ in range(n):
+            moe._check(lib.moe_fused_forward(ref, stream))
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    name = "mixtral_decode_fused_%s_T%d_d%d_f%d_E%d_k%d" % (fmt, T, d, f, E, k)
+    log("%s: %.3f ms/step, %.0f tokens/s" % (name, ms, T / (ms * 1e-3)))
+    del Q, S, ws
+    torch.cuda.empty_cache()
+    return {"workload": name, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +506,9 @@ def main():
                                           5, fmt))
         rep.append(measure_decode_fp8(moe, synth, (Wg, Wu, Wd), Wr, max(args.decode_steps, 5), 5,
                                       "ue8m0", fp4=True))
+        for fmt in ("bf16", "ue8m0", "fp4"):
+            rep.append(measure_fused(moe, synth, (Wg, Wu, Wd), Wr, max(args.decode_steps, 5), 5,
+                                     fmt))
         del Wg, Wu, Wd
         torch.cuda.empty_cache()
         for spec_o, fmt in ((synth.SKEWED_128E, "f32"), (synth.DSV3_FP8, "f32"),

@@ -283,14 +283,16 @@ moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
                        void* out, moe_dtype out_dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
- * moe_fused_forward - the whole layer for small batches (decode) in three launches: routing (+ x
- * quantisation), the gate/up projection (+ h quantisation), the down projection (+ weighting and
- * combine). The single fused MoE kernel of the AWS fused-MoE news page (routing, both expert
- * projections and the combine in one kernel) as far as it goes without a grid-wide barrier: the
- * launches hand over through stream order and per-group completion counters, and no permutation
- * is materialised (each expert's workgroups find its pairs in topk_ids). Computes what
- * moe_route + moe_permute (+ fp8_quantize_act) + moe_experts_forward (slots) + moe_combine compute,
- * with the same arithmetic, so the outputs are bit-identical to that sequence.
+ * moe_fused_forward - the whole layer for small batches (decode) in one call: one routing kernel
+ * (router logits or given logits, top-k with renormalised weights, and for fp8 / FP4 experts the
+ * activation quantisation), the two expert projections (for fp8 / FP4 with the h quantiser between
+ * them) and the combine. After the single fused MoE kernel of the AWS fused-MoE news page, as far
+ * as it pays here: no permutation is materialised (each expert's workgroups find its pairs in
+ * topk_ids), and the steps that need every workgroup's results (h quantisation, combine) stay
+ * launches of their own, since a hand-off inside a launch costs each workgroup an L2 write-back
+ * and invalidation on gfx950. Computes what moe_route + moe_permute (+ fp8_quantize_act) +
+ * moe_experts_forward (slots) + moe_combine compute, with the same arithmetic, so the outputs
+ * are bit-identical to that sequence.
  *
  *  T*k <= 256 pairs (MOE_ERR_UNSUPPORTED otherwise); d % 128 == f % 128 == 0; E <= 1024, k <= E.
  *  x [T, d] (MOE_BF16, or MOE_F32 with fp8 / FP4 experts), 16-byte aligned.

@@ -365,7 +365,7 @@ def moe_combine(y, layout: str, T: int, k: int, d: int, pair_pos=None, topk_w=No
 def moe_fused_forward(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, s_gate=None,
                       s_up=None, s_down=None, w_fp4: bool = False, out_dtype=None,
                       workspace=None, out=None, logits_out=None):
-    """The whole layer for small batches (T*k <= 256) in three launches (moe_fused_forward).
+    """The whole layer for small batches (T*k <= 256) in one call (moe_fused_forward).
     Weights as for moe_layer (bf16; uint8 e4m3 codes with fp32 or uint8 (UE8M0) block scales; with
     w_fp4, E2M1 codes in fragment order with MX scales). Returns (out [T, d], topk_ids, topk_w)."""
     lib = load_library()

@@ -365,8 +365,9 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
                        dim3(256), 0, stream, static_cast<float*>(a->y), n);
     if ((e = hipGetLastError()) != hipSuccess) return MOE_ERR_DEVICE;
   }
-  if (ue8m0) {
-    // the GEMMs read activation scales as fp32 values; e8m0 bytes expand exactly
+  if (ue8m0) X.a_scale_bytes = a->x_scales;   // the small-batch kernels read the bytes
+  if (ue8m0 && !fp8_decode) {
+    // the tiled GEMMs read activation scales as fp32 values; e8m0 bytes expand exactly
     float* xs = reinterpret_cast<float*>(ws + L.x_scales);
     e = launch_e8m0_expand(static_cast<const uint8_t*>(a->x_scales),
                            static_cast<size_t>(a->T) * (a->d / kFp8Group), xs, stream);
@@ -387,30 +388,23 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
 namespace {
 
 struct FusedLayout {
-  size_t h_cnt, c_cnt, xq, xs, h, h32, hq, hs, slots, total;
-  size_t ncnt;   // ints from h_cnt to the end of c_cnt
+  size_t xq, xs, h, h32, hs, slots, total;
 };
 
-FusedLayout fused_layout(int T, int d, int f, int E, int k, moe_dtype w, moe_dtype out) {
+// Workspace of the fused path: x codes and scales (fp8 / FP4), h (bf16; or fp32 before its
+// quantisation, e4m3 codes and scales), and the slots [P, d] in the output type.
+FusedLayout fused_layout(int T, int d, int f, int k, moe_dtype w, moe_dtype out) {
   FusedLayout L{};
   const size_t P = static_cast<size_t>(T) * k;
-  const bool lowp = is_low_precision(w);
   size_t off = 0;
-  L.h_cnt = off;
-  off += static_cast<size_t>(E) * (f / kFp8Group) * sizeof(int);
-  L.c_cnt = off;
-  off += static_cast<size_t>(T) * (d / 64) * sizeof(int);
-  L.ncnt = off / sizeof(int);
-  off = align_up(off);
-  L.xq = L.xs = L.h32 = L.hq = 0;
-  if (lowp) {
+  if (is_low_precision(w)) {
     L.xq = off;
     off = align_up(off + static_cast<size_t>(T) * d);
     L.xs = off;
     off = align_up(off + static_cast<size_t>(T) * (d / kFp8Group) * sizeof(float));
     L.h32 = off;
     off = align_up(off + P * f * sizeof(float));
-    L.hq = off;
+    L.h = off;   // e4m3 codes
     off = align_up(off + P * f);
     L.hs = off;
     off = align_up(off + P * (f / kFp8Group) * sizeof(float));
@@ -432,7 +426,7 @@ size_t moe_fused_workspace_size(int T, int d, int f, int E, int k, moe_dtype w_d
                                 moe_dtype out_dtype) {
   if (check_topology(T, E, k) != MOE_OK || d < 1 || f < 1) return 0;
   if (static_cast<long long>(T) * k > kFusedMaxPairs || d % kFp8Group || f % kFp8Group) return 0;
-  return fused_layout(T, d, f, E, k, w_dtype, out_dtype).total;
+  return fused_layout(T, d, f, k, w_dtype, out_dtype).total;
 }
 
 moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
@@ -463,17 +457,16 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   if (a->d > 32768 || a->f > 32768) return MOE_ERR_UNSUPPORTED;
   if (!aligned(a->x, 16) || (!a->logits && !aligned(a->w_router, 16))) return MOE_ERR_UNSUPPORTED;
   if (static_cast<long long>(a->f) * a->d > INT_MAX / 4) return MOE_ERR_UNSUPPORTED;
-  const FusedLayout L = fused_layout(a->T, a->d, a->f, a->E, a->k, w, a->out_dtype);
+  const FusedLayout L = fused_layout(a->T, a->d, a->f, a->k, w, a->out_dtype);
   if (!a->workspace) return MOE_ERR_INVALID_ARGUMENT;
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
   char* ws = static_cast<char*>(a->workspace);
-  int* cnt = reinterpret_cast<int*>(ws + L.h_cnt);
   uint8_t* xq = lowp ? reinterpret_cast<uint8_t*>(ws + L.xq) : nullptr;
-  float* xs = lowp ? reinterpret_cast<float*>(ws + L.xs) : nullptr;
+  void* xs = lowp ? static_cast<void*>(ws + L.xs) : nullptr;
   hipError_t e = launch_fused_route(a->x, a->x_dtype, a->logits, a->w_router, a->logits_out, a->T,
-                                    a->d, a->E, a->k, a->topk_ids, a->topk_w, xq, xs, ue8m0, cnt,
-                                    L.ncnt, stream);
+                                    a->d, a->E, a->k, a->topk_ids, a->topk_w, xq, xs, ue8m0,
+                                    stream);
   if (e != hipSuccess) return MOE_ERR_DEVICE;
 
   ExpertsLaunch X{};
@@ -484,7 +477,8 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   X.k = a->k;
   X.a = lowp ? static_cast<const void*>(xq) : a->x;
   X.a_gather = 1;
-  X.a_scales = xs;
+  X.a_scales = static_cast<const float*>(xs);
+  X.a_scale_bytes = xs;
   X.w_gate = a->w_gate;
   X.w_up = a->w_up;
   X.w_down = a->w_down;
@@ -497,19 +491,17 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   X.y_layout = MOE_Y_SLOTS;
   X.y_bf16 = a->out_dtype == MOE_BF16;
   X.y = ws + L.slots;
-  X.h = lowp ? nullptr : ws + L.h;
+  X.h = ws + L.h;
   X.h32 = lowp ? reinterpret_cast<float*>(ws + L.h32) : nullptr;
-  X.hq = lowp ? reinterpret_cast<uint8_t*>(ws + L.hq) : nullptr;
   X.h_scales = lowp ? reinterpret_cast<float*>(ws + L.hs) : nullptr;
+  X.h_scale_bytes = lowp ? reinterpret_cast<uint8_t*>(ws + L.hs) : nullptr;
   X.pair_ids = a->topk_ids;
-  X.h_cnt = reinterpret_cast<int*>(ws + L.h_cnt);
-  X.c_cnt = reinterpret_cast<int*>(ws + L.c_cnt);
-  X.out = a->out;
-  X.out_bf16 = a->out_dtype == MOE_BF16;
   X.cpx = cus_per_xcd();
   e = lowp ? launch_experts_fp8_decode(X, stream) : launch_experts_bf16_decode(X, stream);
   if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
-  return dev(e);
+  if (e != hipSuccess) return MOE_ERR_DEVICE;
+  return dev(launch_combine(ws + L.slots, a->out_dtype, MOE_Y_SLOTS, nullptr, nullptr, a->T, a->k,
+                            a->d, a->out, a->out_dtype, stream));
 }
 
 moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,

@@ -292,9 +292,10 @@ __device__ __forceinline__ bool map_cut_tile(const int32_t* __restrict__ tile_cu
 // ---- helpers of the fused small-batch path ----------------------------------------------------
 
 // The pairs (flat index t * k + j) routed to expert e, in ascending order, found by one workgroup
-// of NT threads in ids[0 .. P): written to list[0 .. M) (LDS), M returned to every thread.
-// wsum: LDS scratch of NT / 64 ints. Ends with a barrier, so list is ready for the whole group.
-template <int NT>
+// of NT threads in ids[0 .. P): the first CAP of them written to list (LDS), their number M
+// returned to every thread. wsum: LDS scratch of NT / 64 ints. Ends with a barrier, so list is
+// ready for the whole group.
+template <int NT, int CAP>
 __device__ int expert_pair_list(const int32_t* __restrict__ ids, int P, int e, int32_t* list,
                                 int* wsum) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
@@ -311,7 +312,8 @@ __device__ int expert_pair_list(const int32_t* __restrict__ ids, int P, int e, i
       off += v < w ? wsum[v] : 0;
       tot += wsum[v];
     }
-    if (hit) list[off + __popcll(m & ((1ull << lane) - 1ull))] = i;
+    const int at = off + __popcll(m & ((1ull << lane) - 1ull));
+    if (hit && at < CAP) list[at] = i;
     total += tot;
     __syncthreads();
   }
@@ -350,20 +352,6 @@ __device__ __forceinline__ float quant_group16(const float (&v)[8], uint32_t& lo
     *byte = 0;
     return s;
   }
-}
-
-// Hand-off between workgroups of one launch: every thread has stored what it produced; after this
-// the group's stores are visible device-wide (each XCD has its own L2) and, in the one group that
-// brings counter *cnt to n, the other groups' stores are visible to all of its threads. Returns
-// true in that last group (uniform over the workgroup). flag: LDS int.
-__device__ __forceinline__ bool last_arrival(int* cnt, int n, int* flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = atomicAdd(cnt, 1) == n - 1;
-  __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
 }
 
 // Blocks to launch for map_work: per XCD at most chunk whole tiles plus cpx tail pieces.

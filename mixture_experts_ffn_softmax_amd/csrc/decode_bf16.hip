@@ -49,12 +49,9 @@ struct DecodeArgs {
   const float* topk_w;
   int small_max;              // experts with at most this many tokens belong to the streaming
                               // kernel (0: this kernel takes every expert)
-  // fused small-batch path (see ExpertsLaunch): routing ids [P]; down: combine into out
+  // fused small-batch path (see ExpertsLaunch): routing ids [P]
   const int32_t* ids;
   int P;
-  int* c_cnt;
-  void* out;
-  int out_bf16;
 };
 
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
@@ -65,7 +62,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// kFused: the fused small-batch path (pairs from the routing ids; the down kernel combines).
+// kFused: the fused small-batch path (pairs from the routing ids; h and slots indexed by pair).
 template <int MODE, bool kFused>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
   constexpr int kRows = MODE == kGateUp ? kDecodeGateRows : kDecodeDownRows;
@@ -73,11 +70,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
   __shared__ int32_t plist[kFused ? kFusedMaxPairs : 1];   // fused: this expert's pairs
-  __shared__ int hand[kWave];                 // fused: per-token "last slot" flags, scratch
+  __shared__ int wsum[4];
   int row0, M;
   if constexpr (kFused) {
     row0 = 0;
-    M = expert_pair_list<256>(p.ids, p.P, e, plist, hand);
+    M = expert_pair_list<256, kFusedMaxPairs>(p.ids, p.P, e, plist, wsum);
   } else {
     row0 = p.offsets[e];
     M = p.offsets[e + 1] - row0;
@@ -210,34 +207,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
         }
       }
     }
-    if constexpr (kFused && MODE == kDown) {
-      // Every token of this pass has its slot's 64 channels written; the last of a token's k
-      // slots to arrive (per 64-channel panel) sums the k slots in slot order into out.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      const int npass = min(kDecodeTokens, M - tc0);
-      if (tid < npass) {
-        const int t = plist[tc0 + tid] / p.k;
-        hand[tid] = atomicAdd(p.c_cnt + static_cast<size_t>(t) * nrb + rb, 1) == p.k - 1;
-      }
-      __syncthreads();
-      for (int i = wave; i < npass; i += 4) {
-        if (!hand[i]) continue;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const int t = plist[tc0 + i] / p.k;
-        const int n = rb * kRows + lane;
-        if (n >= p.N) continue;
-        float acc = 0.0f;
-        for (int j = 0; j < p.k; ++j) {
-          const size_t idx = (static_cast<size_t>(t) * p.k + j) * p.N + n;
-          acc += p.y_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.y)[idx])
-                          : static_cast<const float*>(p.y)[idx];
-        }
-        const size_t o = static_cast<size_t>(t) * p.N + n;
-        if (p.out_bf16) static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(acc);
-        else static_cast<float*>(p.out)[o] = acc;
-      }
-    }
     __syncthreads();
   }
 }
@@ -271,21 +240,33 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   const int nrb = (p.N + kOut - 1) / kOut;
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
-  __shared__ int32_t plist[kFused ? kFusedMaxPairs : 1];   // fused: this expert's pairs
-  __shared__ int wsum[1];
+  // Exactly 32 KB, so that five workgroups fit a CU. On the fused path the expert's first 16
+  // pairs (experts with more belong to the K-split kernel) are gathered in the first slot before
+  // any DMA lands there.
+  __shared__ __attribute__((aligned(1024))) char ring[kStrRing * kStage];
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15, g = lane >> 4;
   int row0, M;
   if constexpr (kFused) {
+    int32_t* plist = reinterpret_cast<int32_t*>(ring);
     row0 = 0;
-    M = expert_pair_list<64>(p.ids, p.P, e, plist, wsum);
+    M = expert_pair_list<64, 16>(p.ids, p.P, e, plist, plist + 16);
   } else {
     row0 = p.offsets[e];
     M = p.offsets[e + 1] - row0;
   }
   if (M == 0 || M > 16) return;
-
-  __shared__ __attribute__((aligned(1024))) char ring[kStrRing * kStage];
-  const int lane = threadIdx.x;
-  const int r16 = lane & 15, g = lane >> 4;
+  // token r16's pair (its h row on the fused path) and the row of x it reads
+  const int t = min(r16, M - 1);
+  int pos, src;
+  if constexpr (kFused) {
+    pos = reinterpret_cast<const int32_t*>(ring)[t];
+    src = p.a_gather ? pos / p.k : pos;
+    __syncthreads();   // the list is read before the ring is refilled
+  } else {
+    pos = row0 + t;
+    src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+  }
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
   const uint32_t wbytes = static_cast<uint32_t>(p.N) * p.K * 2u;
   const i32x4_t rs0 = make_rsrc(p.w0 + e * wstride, wbytes);
@@ -301,9 +282,6 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
     voff[i] = static_cast<uint32_t>(min(n, p.N - 1)) * p.K * 2u + c * 16;
   }
   // token operand: lane (t = l % 16, g = l / 16) holds k = 32 u + 8 g .. +7 of token t
-  const int t = min(r16, M - 1);
-  const int pos = kFused ? plist[t] : row0 + t;
-  const int src = p.a_gather ? (kFused ? plist[t] : p.sorted_pair[pos]) / p.k : pos;
   const uint16_t* trow = p.a + static_cast<size_t>(src) * p.K + g * 8;
 
   const int nst = p.K / KS;
@@ -359,8 +337,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
          (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[1], up[1]))) << 16);
   o[1] = f32_to_bf16_bits(silu_mul(acc[2], up[2])) |
          (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[3], up[3]))) << 16);
-  const int hrow = kFused ? plist[r16] : row0 + r16;
-  *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(hrow) * p.N + n) = o;
+  *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(pos) * p.N + n) = o;   // r16 < M: t == r16
 }
 
 }  // namespace
@@ -420,9 +397,6 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   dn.small_max = 0;  // the K-split kernel takes every expert of the down GEMM
   dn.ids = L.pair_ids;
   dn.P = P;
-  dn.c_cnt = L.c_cnt;
-  dn.out = L.out;
-  dn.out_bf16 = L.out_bf16;
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
   if (fused)
     hipLaunchKernelGGL((decode_bf16_kernel<kDown, true>), dim3(grid2), dim3(256), 0, stream, dn);

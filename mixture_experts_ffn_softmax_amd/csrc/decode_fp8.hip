@@ -42,7 +42,7 @@ constexpr int kDown = 1;
 
 struct Fp8DecodeArgs {
   const uint8_t* a;           // gate/up: x codes [T, K] (gathered); down: h codes [P, K]
-  const float* a_s;           // activation scales [rows, K/128] (fp32; powers of two for UE8M0)
+  const void* a_s;            // activation scales [rows, K/128]: fp32, or e8m0 bytes (UE8M0)
   int a_gather;
   const int32_t* sorted_pair;
   int k;
@@ -57,15 +57,9 @@ struct Fp8DecodeArgs {
   void* y;                    // down output
   int y_layout, y_bf16;
   const float* topk_w;
-  // fused small-batch path (see ExpertsLaunch)
-  const int32_t* ids;         // routing ids [P]
+  // fused small-batch path (see ExpertsLaunch): routing ids [P]
+  const int32_t* ids;
   int P;
-  uint8_t* hq;                // gate/up: h codes [P, N] and scales hs [P, N/128] (fp32 values)
-  float* hs;
-  int* h_cnt;
-  int* c_cnt;
-  void* out;                  // down: combined output [T, N]
-  int out_bf16;
 };
 
 __device__ __forceinline__ i32x8_t ld16x2g(const uint8_t* p, const uint8_t* q) {
@@ -87,7 +81,7 @@ __device__ __forceinline__ i32x8_t ld16g(const uint8_t* p) {
 
 // kW4: E2M1 weights with per-32 MX scales (implies kUE). kTG: groups of 16 tokens per pass over
 // the weights (fewer groups hold fewer registers and less LDS, so more waves stream at once).
-// kFused: the fused small-batch path (pairs from the routing ids, hand-offs at the end).
+// kFused: the fused small-batch path (pairs from the routing ids; h and slots indexed by pair).
 template <int MODE, bool kUE, bool kW4, int kTG, bool kFused>
 __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   constexpr int kRows = MODE == kGateUp ? kFdGateRows : kFdDownRows;
@@ -96,11 +90,11 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
   __shared__ int32_t plist[kFused ? kFusedMaxPairs : 1];   // fused: this expert's pairs
-  __shared__ int hand[kWave];                 // fused: per-token "last slot" flags, scratch
+  __shared__ int wsum[4];
   int row0, M;
   if constexpr (kFused) {
     row0 = 0;
-    M = expert_pair_list<256>(p.ids, p.P, e, plist, hand);
+    M = expert_pair_list<256, kFusedMaxPairs>(p.ids, p.P, e, plist, wsum);
   } else {
     row0 = p.offsets[e];
     M = p.offsets[e + 1] - row0;
@@ -178,14 +172,14 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   for (int tc0 = 0; tc0 < M; tc0 += kTokens) {
     const int ntg = min(kTG, (M - tc0 + 15) / 16);
     const uint8_t* brow[kTG];
-    const float* bscale[kTG];
+    size_t bscale[kTG];   // index of the token's first scale
 #pragma unroll
     for (int tg = 0; tg < kTG; ++tg) {
       const int ti = min(tc0 + tg * 16 + r16, M - 1);
       const int pos = pos_of(ti);
       const int src = p.a_gather ? pair_of(ti) / p.k : pos;
       brow[tg] = p.a + static_cast<size_t>(src) * p.K + g * 16;
-      bscale[tg] = p.a_s + static_cast<size_t>(src) * KB;
+      bscale[tg] = static_cast<size_t>(src) * KB;
     }
     f32x4_t acc[4][kTG];
 #pragma unroll
@@ -196,7 +190,8 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
     for (int c = wave; c < KB; c += 4) {
       const int kb = c * 128;
       i32x8_t av[4], bv[kTG];
-      float bs[kTG];
+      float bs[kTG];    // fp32 scales
+      int bx[kTG];      // UE8M0: e8m0 bytes
       int ewl[4];   // E2M1: each lane's own block scale byte
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
@@ -211,16 +206,17 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
       for (int tg = 0; tg < kTG; ++tg)
         if (tg < ntg) {
           bv[tg] = ld16x2g(brow[tg] + kb, brow[tg] + kb + 64);
-          bs[tg] = bscale[tg][c];
+          if constexpr (kUE) bx[tg] = static_cast<const uint8_t*>(p.a_s)[bscale[tg] + c];
+          else bs[tg] = static_cast<const float*>(p.a_s)[bscale[tg] + c];
         }
 #pragma unroll
       for (int tg = 0; tg < kTG; ++tg) {
         if (tg >= ntg) continue;
         if constexpr (kUE) {
-          // the token's e8m0 byte: exponent field of its power-of-two fp32 scale. Each block's
-          // product starts from zero and is added afterwards: with a token group or two the
-          // few accumulators would otherwise chain every MFMA to the previous K block's.
-          const int ex = (__float_as_uint(bs[tg]) >> 23) & 0xFF;
+          // the token's e8m0 byte goes to the instruction. Each block's product starts from
+          // zero and is added afterwards: with a token group or two the few accumulators would
+          // otherwise chain every MFMA to the previous K block's.
+          const int ex = bx[tg];
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
             const int ew = kW4 ? ewl[rg] : static_cast<int>(wss[rg][c]);
@@ -300,53 +296,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
         }
       }
     }
-    if constexpr (kFused && MODE == kDown) {
-      // Every token of this pass has its slot's 64 channels written; the last of a token's k
-      // slots to arrive (per 64-channel panel) sums the k slots in slot order into out.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      const int npass = min(kTokens, M - tc0);
-      if (tid < npass) {
-        const int t = plist[tc0 + tid] / p.k;
-        hand[tid] = atomicAdd(p.c_cnt + static_cast<size_t>(t) * nrb + rb, 1) == p.k - 1;
-      }
-      __syncthreads();
-      for (int i = wave; i < npass; i += 4) {
-        if (!hand[i]) continue;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const int t = plist[tc0 + i] / p.k;
-        const int n = rb * kRows + lane;
-        if (n >= p.N) continue;
-        float acc = 0.0f;
-        for (int j = 0; j < p.k; ++j) {
-          const size_t idx = (static_cast<size_t>(t) * p.k + j) * p.N + n;
-          acc += p.y_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.y)[idx])
-                          : static_cast<const float*>(p.y)[idx];
-        }
-        const size_t o = static_cast<size_t>(t) * p.N + n;
-        if (p.out_bf16) static_cast<uint16_t*>(p.out)[o] = f32_to_bf16_bits(acc);
-        else static_cast<float*>(p.out)[o] = acc;
-      }
-    }
     __syncthreads();
-  }
-  if constexpr (kFused && MODE == kGateUp) {
-    // The groups rb = 4j .. 4j + 3 write h channels [128 j, 128 j + 128) of this expert's pairs
-    // (fp32); the last of them to finish quantises that group of every pair.
-    if (last_arrival(p.h_cnt + static_cast<size_t>(e) * (p.N / 128) + rb / 4, 4, hand)) {
-      const int c0 = (rb / 4) * 128 + (tid & 15) * 8;
-      for (int i = tid / 16; i < M; i += 16) {   // 16 lanes per pair row
-        const size_t r = static_cast<size_t>(plist[i]);
-        const f32x4_t lo4 = *reinterpret_cast<const f32x4_t*>(p.h32 + r * p.N + c0);
-        const f32x4_t hi4 = *reinterpret_cast<const f32x4_t*>(p.h32 + r * p.N + c0 + 4);
-        const float v[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        uint32_t lo, hi;
-        int byte;
-        const float sc = quant_group16<kUE>(v, lo, hi, &byte);
-        *reinterpret_cast<uint2*>(p.hq + r * p.N + c0) = make_uint2(lo, hi);
-        if ((tid & 15) == 0) p.hs[r * (p.N / 128) + rb / 4] = sc;
-      }
-    }
   }
 }
 
@@ -391,9 +341,10 @@ hipError_t launch_mode(const Fp8DecodeArgs& a, int E, int P, bool ue, bool w4, b
 
 hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream) {
   const int P = L.T * L.k;
+  const bool ue = L.scale_ue8m0 != 0;
   Fp8DecodeArgs g{};
   g.a = static_cast<const uint8_t*>(L.a);
-  g.a_s = L.a_scales;
+  g.a_s = ue ? L.a_scale_bytes : static_cast<const void*>(L.a_scales);
   g.a_gather = L.a_gather;
   g.sorted_pair = L.sorted_pair;
   g.k = L.k;
@@ -405,38 +356,25 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   g.N = L.f;
   g.offsets = L.offsets;
   g.h32 = L.h32;
-  const bool ue = L.scale_ue8m0 != 0;
   const bool w4 = L.w_fp4 != 0;
   const bool fused = L.pair_ids != nullptr;
   if (w4 && !ue) return hipErrorNotSupported;   // MX scales are e8m0 bytes
-  uint8_t* hq = fused ? L.hq : static_cast<uint8_t*>(L.h);
-  if (fused) {
-    g.ids = L.pair_ids;
-    g.P = P;
-    g.hq = hq;
-    g.hs = L.h_scales;
-    g.h_cnt = L.h_cnt;
-  }
+  uint8_t* hq = static_cast<uint8_t*>(L.h);
+  g.ids = L.pair_ids;
+  g.P = P;
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
   hipError_t e = launch_mode<kGateUp>(g, L.E, P, ue, w4, fused, stream);
   if (e != hipSuccess) return e;
-  // h -> e4m3 codes with per-(pair, 128-channel) scales, as fp32 values for the down kernel (the
-  // fused gate/up groups do this themselves)
-  if (fused) {
-  } else if (ue) {
-    e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, L.h_scale_bytes, true, stream);
-    if (e == hipSuccess)
-      e = launch_e8m0_expand(L.h_scale_bytes, static_cast<size_t>(P) * (L.f / 128), L.h_scales,
-                             stream);
-  } else {
-    e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, L.h_scales, false, stream);
-  }
+  // h -> e4m3 codes with per-(pair, 128-channel) scales: e8m0 bytes or fp32, as the down kernel
+  // reads them (rows in h's own order: sorted, or by pair on the fused path)
+  void* hs = ue ? static_cast<void*>(L.h_scale_bytes) : static_cast<void*>(L.h_scales);
+  e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, hs, ue, stream);
   if (e != hipSuccess) return e;
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
 
   Fp8DecodeArgs dn{};
   dn.a = hq;
-  dn.a_s = L.h_scales;
+  dn.a_s = hs;
   dn.a_gather = 0;
   dn.sorted_pair = L.sorted_pair;
   dn.k = L.k;
@@ -449,13 +387,8 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   dn.y_layout = L.y_layout;
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
-  if (fused) {
-    dn.ids = L.pair_ids;
-    dn.P = P;
-    dn.c_cnt = L.c_cnt;
-    dn.out = L.out;
-    dn.out_bf16 = L.out_bf16;
-  }
+  dn.ids = L.pair_ids;
+  dn.P = P;
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
   e = launch_mode<kDown>(dn, L.E, P, ue, w4, fused, stream);
   if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);

@@ -1,13 +1,12 @@
 // Fused small-batch path, launch 1 of 3: routing for one token per workgroup.
 //
 // The single fused MoE kernel idea (AWS fused-MoE news page: one kernel for routing, both expert
-// projections and the combine) taken as far as one GPU allows without a grid-wide barrier: three
-// launches whose only hand-offs are stream order and per-group completion counters. This kernel
+// projections and the combine), taken as far as it pays on gfx950: routing, top-k and the
+// activation quantisation in one launch, no permutation (the expert kernels find each expert's
+// pairs in the routing ids themselves), then the expert projections and the combine. This kernel
 // computes a token's router logits (or reads given ones), picks its top k with renormalised
-// softmax weights (lira-now explainer, section 5), quantises its activations to e4m3 per 128
-// channels for fp8 / FP4 experts (Transformers "Fine-grained FP8" page), and clears the counters
-// the other two launches hand off through. The expert kernels then find each expert's pairs in
-// the routing ids themselves, so no permutation is materialised.
+// softmax weights (lira-now explainer, section 5) and quantises its activations to e4m3 per 128
+// channels for fp8 / FP4 experts (Transformers "Fine-grained FP8" page).
 #include "common.h"
 #include "launch.h"
 #include "route_dev.h"
@@ -24,9 +23,7 @@ struct FusedRouteArgs {
   int32_t* ids;               // [T, k]
   float* w;                   // [T, k]
   uint8_t* xq;                // fp8: e4m3 codes [T, d]
-  float* xs;                  // fp8: scales [T, d/128] as fp32 values
-  int* cnt;                   // hand-off counters to clear
-  size_t ncnt;
+  void* xs;                   // fp8: scales [T, d/128], fp32 or (UE8M0) e8m0 bytes
 };
 
 template <typename XT, int VPL, bool kQuant, bool kUE>
@@ -34,9 +31,6 @@ __global__ __launch_bounds__(256) void fused_route_kernel(FusedRouteArgs a) {
   __shared__ float lg[kMaxExperts];
   __shared__ float red[4][kVecExperts];
   const int t = blockIdx.x;
-  for (size_t i = static_cast<size_t>(t) * 256 + threadIdx.x; i < a.ncnt;
-       i += static_cast<size_t>(gridDim.x) * 256)
-    a.cnt[i] = 0;
   const XT* xr = static_cast<const XT*>(a.x) + static_cast<size_t>(t) * a.d;
   const float* row;
   if (a.logits_in) {
@@ -69,7 +63,11 @@ __global__ __launch_bounds__(256) void fused_route_kernel(FusedRouteArgs a) {
       const float s = quant_group16<kUE>(v, lo, hi, &byte);
       if (active) {
         *reinterpret_cast<uint2*>(a.xq + static_cast<size_t>(t) * a.d + col) = make_uint2(lo, hi);
-        if ((threadIdx.x & 15) == 0) a.xs[static_cast<size_t>(t) * ng + grp] = s;
+        if ((threadIdx.x & 15) == 0) {
+          const size_t si = static_cast<size_t>(t) * ng + grp;
+          if constexpr (kUE) static_cast<uint8_t*>(a.xs)[si] = static_cast<uint8_t>(byte);
+          else static_cast<float*>(a.xs)[si] = s;
+        }
       }
     }
   }
@@ -104,8 +102,8 @@ void launch_route_x(const FusedRouteArgs& a, int T, int vpl, bool quant, bool ue
 
 hipError_t launch_fused_route(const void* x, moe_dtype x_dtype, const float* logits,
                               const float* wr, float* logits_out, int T, int d, int E, int k,
-                              int32_t* ids, float* w, uint8_t* xq, float* xs, bool ue, int* cnt,
-                              size_t ncnt, hipStream_t stream) {
+                              int32_t* ids, float* w, uint8_t* xq, void* xs, bool ue,
+                              hipStream_t stream) {
   FusedRouteArgs a{};
   a.x = x;
   a.logits_in = logits;
@@ -119,8 +117,6 @@ hipError_t launch_fused_route(const void* x, moe_dtype x_dtype, const float* log
   a.w = w;
   a.xq = xq;
   a.xs = xs;
-  a.cnt = cnt;
-  a.ncnt = ncnt;
   const int vpl = topk_vpl(E, a.G);
   const bool quant = xq != nullptr;
   if (x_dtype == MOE_BF16) launch_route_x<uint16_t>(a, T, vpl, quant, ue, stream);

@@ -79,30 +79,25 @@ struct ExpertsLaunch {
   float* split_partial;       // bf16 GEMMs: [kSplitSlots][256 * 256] fp32, or null (no cutting;
                               // the two GEMMs use it one after the other)
   void** ev;                  // nullable timing events (4)
+  // fp8 small-batch kernels with UE8M0 scales read the activation scales as e8m0 bytes:
+  // a_scale_bytes [T, d/128] (or [P, d/128]) for x, h_scale_bytes for h
+  const void* a_scale_bytes;
   // Fused small-batch path (decode kernels only): pair_ids non-null. Each workgroup finds its
   // expert's pairs in the routing ids [T * k] itself (no offsets or sorted_pair); h, its scales
-  // and the slots y [P, d] are indexed by pair. The fp8 gate/up groups quantise h themselves (the
-  // last of the four producing a 128-channel group; counters h_cnt [E * f/128]) and the down
-  // groups combine (the last of a token's k slots per 64-channel panel; c_cnt [T * d/64]) into
-  // out [T, d]. Both counter arrays are zero at launch.
+  // and the slots y [P, d] are indexed by pair.
   const int32_t* pair_ids;
-  uint8_t* hq;                // fp8: h codes [P, f] (h above holds h32's codes otherwise)
-  int* h_cnt;
-  int* c_cnt;
-  void* out;
-  int out_bf16;
 };
 
 // pairs a fused small-batch launch may carry (one pair per thread of a 256-thread workgroup)
 constexpr int kFusedMaxPairs = 256;
 
 // Fused small-batch path, launch 1: per token router logits (or given logits), top-k, and with
-// xq non-null e4m3 codes xq [T, d] + scales xs [T, d/128] (fp32 values; UE8M0 rule when ue);
-// clears cnt[0 .. ncnt). x and wr 16-byte aligned, d % 128 == 0, E <= kMaxExperts.
+// xq non-null e4m3 codes xq [T, d] + scales xs [T, d/128] (fp32, or e8m0 bytes with ue).
+// x and wr 16-byte aligned, d % 128 == 0, E <= kMaxExperts.
 hipError_t launch_fused_route(const void* x, moe_dtype x_dtype, const float* logits,
                               const float* wr, float* logits_out, int T, int d, int E, int k,
-                              int32_t* ids, float* w, uint8_t* xq, float* xs, bool ue, int* cnt,
-                              size_t ncnt, hipStream_t stream);
+                              int32_t* ids, float* w, uint8_t* xq, void* xs, bool ue,
+                              hipStream_t stream);
 
 int f32_tile_rows();
 hipError_t launch_experts_f32(const ExpertsLaunch& L, hipStream_t stream);
