@@ -66,6 +66,11 @@ CASES = [
     ("fp4", synth.DSV3_FP8.with_(name="fz_fp4_T32_d512_f384_E8_k2", T=32, d=512, f=384, E=8,
                                  k=2)),
     ("fp4", synth.DSV3_FP8.with_(name="fz_fp4_T1_d256_f128_E4_k1", T=1, d=256, f=128, E=4, k=1)),
+    # many experts (several logits per lane in the top-k selection), P = 256
+    ("fp4", synth.DSV3_FP8.with_(name="fz_fp4_T64_d256_f256_E64_k4", T=64, d=256, f=256, E=64,
+                                 k=4)),
+    ("ue8m0", synth.DSV3_FP8.with_(name="fz_fp8ue_T32_d512_f256_E256_k8_router", T=32, d=512,
+                                   f=256, E=256, k=8, logits="router")),
 ]
 
 
