@@ -233,9 +233,8 @@ moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q
  *        weights packed E2M1 [E, f, d/2] and [E, d, f/2] in matrix-fragment order (from
  *        fp4_quantize_weight_mx, then fp4_tile_weight) with MX scales (row order, as the
  *        quantiser writes them) s_gate / s_up [E, f, d/32] and s_down [E, d, f/32]; x and h
- *        e4m3 with UE8M0 per-128 scales. Weight-streaming kernels only: P <= 256, otherwise
- *        MOE_ERR_UNSUPPORTED. d % 128 == f % 128 == 0; the three MX scale arrays 4-byte aligned
- *        (MOE_ERR_UNSUPPORTED otherwise).
+ *        e4m3 with UE8M0 per-128 scales. d % 128 == f % 128 == 0; the three MX scale arrays
+ *        4-byte aligned (MOE_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int T, d, f, E, k;

@@ -297,8 +297,8 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
     if (!a->x_scales || !a->s_gate || !a->s_up || !a->s_down) return MOE_ERR_INVALID_ARGUMENT;
   }
   const long long P = static_cast<long long>(a->T) * a->k;
-  // E2M1 weights: MX scales are e8m0 bytes, and only the weight-streaming kernels take them
-  if (w4 && (!ue8m0 || P > kDecodeMaxPairs)) return MOE_ERR_UNSUPPORTED;
+  // E2M1 weights: MX scales are e8m0 bytes
+  if (w4 && !ue8m0) return MOE_ERR_UNSUPPORTED;
   if (w4 && (!aligned(a->s_gate, 4) || !aligned(a->s_up, 4) || !aligned(a->s_down, 4)))
     return MOE_ERR_UNSUPPORTED;   // MX scale rows are read as dwords
   // 32-bit element offsets inside the kernels

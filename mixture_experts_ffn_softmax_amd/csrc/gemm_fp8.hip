@@ -18,6 +18,14 @@
 // rows, i.e. one full 128-channel group of h), 8 waves in a 2 x 4 grid, each 64 rows x 64
 // weight rows = 4 x 4 MFMA blocks of 16 x 16. K is staged 128 at a time (one scale block)
 // through a ring of three LDS stages filled two stages ahead by global -> LDS DMA.
+//
+// FP4 experts (kW4; Transformers "Experts backends" page, FP4 quantised experts; "Fine-grained
+// FP8" page, "UE8M0 scale format"): E2M1 weights in matrix-fragment order, so a stage's weight
+// rows are sixteen contiguous 1 KB fragments (one DMA instruction each, read back lane by lane),
+// and one e8m0 byte per weight row per 32 channels, DMA'd as a dword per row per stage. The
+// instruction takes B as FP4 (format code 4) with a scale per lane; a lane of an FP4 operand holds
+// K = 32g .. 32g + 31 of its block, an 8-bit one K = 16g .. 16g + 15 and 64 + 16g .. 64 + 16g + 15
+// (gfx950), so the e4m3 activations are read as 16-byte chunks g and 4 + g of the stage row.
 #include "common.h"
 #include "launch.h"
 
@@ -30,6 +38,8 @@ constexpr int kBKf = 128;                          // K per stage (one scale blo
 constexpr int kAf = kBMf * kBKf;                   // A bytes per stage (16 KB)
 constexpr int kBf = kBNf * kBKf;                   // B bytes per stage (32 KB)
 constexpr int kStageF = kAf + kBf + kBMf * 4;      // + activation scales of the tile rows
+constexpr int kBf4 = kBNf * kBKf / 2;              // E2M1 weight bytes per stage (16 KB)
+constexpr int kStageF4 = kAf + kBf4 + kBMf * 4 + kBNf * 4;   // + MX scale dwords of the rows
 constexpr int kRingF = 3;
 constexpr int kMaxKBlocks = 256;                 // K <= 32768
 constexpr int kGateUp = 0;
@@ -43,7 +53,8 @@ struct Fp8GemmArgs {
   int k;
   const uint8_t* b0;         // gate/up: W_gate [E, N, K]; down: W_down [E, N, K]
   const uint8_t* b1;         // gate/up: W_up
-  const void* s0;            // block scales of b0 [E, N/128, K/128]: fp32, or e8m0 bytes (UE8M0)
+  const void* s0;            // block scales of b0 [E, N/128, K/128]: fp32, or e8m0 bytes (UE8M0);
+                             // E2M1 weights: MX bytes [E, N, K/32]
   const void* s1;            // block scales of b1
   int K, N;
   const int32_t* offsets;
@@ -65,6 +76,8 @@ __device__ __forceinline__ int swzf(int row, int chunk) {
 struct DmaF {
   i32x4_t ra, rs, rb0, rb1;
   uint32_t aoff[4], boff[8], soff;
+  i32x4_t rbs0, rbs1;        // E2M1: MX scales of b0 / b1
+  uint32_t bsoff;            // E2M1: this lane's weight row's MX scale offset
 };
 
 // Stage `st` (clamped to the last real stage so every access stays in bounds) into `buf`. Only
@@ -73,6 +86,10 @@ struct DmaF {
 // waves sharing it): wave w fills A rows (4w + i) * 8 .. +7, B rows (8w + i) * 8 .. +7 (one KB
 // per instruction, lane l -> row l / 8, chunk position l % 8; B rows 0..127 from rb0, 128..255
 // from rb1) and the scales of A rows 32 w .. 32 w + 31.
+// E2M1 (kW4): wave w fills weight fragments 4w .. 4w + 3 (16 rows x 128 K each, 1 KB apart in
+// global memory by K block: fragments 0..7 from rb0, 8..15 from rb1) and the MX scale dwords of
+// weight rows 64 w .. 64 w + 63 (rows 0..127 from rbs0, 128..255 from rbs1).
+template <bool kW4>
 __device__ __forceinline__ void dmaf(const char* buf, const DmaF& d, int st, int nst, int wave,
                                      int lane) {
   if (wave >= 4) return;
@@ -81,10 +98,20 @@ __device__ __forceinline__ void dmaf(const char* buf, const DmaF& d, int st, int
   const uint32_t base = lds_offset(buf);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dma16(base + (wave * 4 + i) * 1024, d.aoff[i], d.ra, kb);
+  if constexpr (kW4) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    dma16(base + kAf + (wave * 8 + i) * 1024, d.boff[i], wave < 2 ? d.rb0 : d.rb1, kb);
-  if (lane < 32) dma4(base + kAf + kBf + wave * 128, d.soff, d.rs, static_cast<uint32_t>(sc) * 4u);
+    for (int i = 0; i < 4; ++i)
+      dma16(base + kAf + (wave * 4 + i) * 1024, d.boff[i], wave < 2 ? d.rb0 : d.rb1,
+            static_cast<uint32_t>(sc) * 1024u);
+    dma4(base + kAf + kBf4 + kBMf * 4 + wave * 256, d.bsoff, wave < 2 ? d.rbs0 : d.rbs1,
+         static_cast<uint32_t>(sc) * 4u);
+    if (lane < 32) dma4(base + kAf + kBf4 + wave * 128, d.soff, d.rs, static_cast<uint32_t>(sc) * 4u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dma16(base + kAf + (wave * 8 + i) * 1024, d.boff[i], wave < 2 ? d.rb0 : d.rb1, kb);
+    if (lane < 32) dma4(base + kAf + kBf + wave * 128, d.soff, d.rs, static_cast<uint32_t>(sc) * 4u);
+  }
 }
 
 __device__ __forceinline__ i32x8_t ld32(const char* p0, const char* p1) {
@@ -96,9 +123,13 @@ __device__ __forceinline__ i32x8_t ld32(const char* p0, const char* p1) {
   return r;
 }
 
-template <int MODE, bool kUE>
+template <int MODE, bool kUE, bool kW4>
 __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
   constexpr int MI = 4, NJ = 4;   // 16x16 blocks per wave
+  constexpr int kStg = kW4 ? kStageF4 : kStageF;   // bytes per ring stage
+  constexpr int kSA = kAf + (kW4 ? kBf4 : kBf);    // activation scales within a stage
+  constexpr int kSB = kSA + kBMf * 4;              // E2M1: MX scale dwords within a stage
+  constexpr int kDmaPerStage = kW4 ? 10 : 13;      // DMA instructions per issuing wave and stage
   const int NT = MODE == kGateUp ? p.N / 128 : (p.N + kBNf - 1) / kBNf;
   TileCoord tc;
   if (!map_tile(p.tile_cum, p.offsets, p.E, kBMf, NT, tc)) return;
@@ -107,7 +138,7 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
   tc.rows = __builtin_amdgcn_readfirstlane(tc.rows);
   tc.ntile = __builtin_amdgcn_readfirstlane(tc.ntile);
 
-  __shared__ __attribute__((aligned(1024))) char ring[kRingF * kStageF];
+  __shared__ __attribute__((aligned(1024))) char ring[kRingF * kStg];
   __shared__ int row_pair[kBMf];
   __shared__ float row_w[kBMf];
 
@@ -128,13 +159,13 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
   }
 
   const int KB = p.K / kBKf;
-  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  const uint32_t wbytes = static_cast<uint32_t>(p.N) * (kW4 ? p.K / 2 : p.K);   // one expert
+  const size_t wstride = wbytes;
   DmaF d;
   d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K);
   d.rs = make_rsrc(p.a_s, static_cast<uint32_t>(p.a_rows) * KB * 4u);
-  d.rb0 = make_rsrc(p.b0 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K);
-  d.rb1 = MODE == kGateUp ? make_rsrc(p.b1 + tc.e * wstride, static_cast<uint32_t>(p.N) * p.K)
-                          : d.rb0;
+  d.rb0 = make_rsrc(p.b0 + tc.e * wstride, wbytes);
+  d.rb1 = MODE == kGateUp ? make_rsrc(p.b1 + tc.e * wstride, wbytes) : d.rb0;
   auto src_row = [&](int r) {
     const int pos = tc.row0 + min(r, tc.rows - 1);
     return p.a_gather ? p.sorted_pair[pos] / p.k : pos;
@@ -145,13 +176,32 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     d.aoff[i] = static_cast<uint32_t>(src_row(r)) * p.K + c * 16;
   }
+  if constexpr (kW4) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (wave * 8 + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
-                                  : min(tc.ntile * kBNf + r, p.N - 1);
-    d.boff[i] = static_cast<uint32_t>(n) * p.K + c * 16;
+    for (int i = 0; i < 4; ++i) {
+      const int fi = wave * 4 + i;   // fragment = 16 tile rows
+      const int n16 = MODE == kGateUp ? tc.ntile * 8 + (fi & 7)
+                                      : min(tc.ntile * 16 + fi, p.N / 16 - 1);
+      d.boff[i] = static_cast<uint32_t>(n16) * KB * 1024u + lane * 16;
+    }
+    const size_t sstride = static_cast<size_t>(p.N) * (p.K / 32);
+    d.rbs0 = make_rsrc(static_cast<const uint8_t*>(p.s0) + tc.e * sstride,
+                       static_cast<uint32_t>(sstride));
+    d.rbs1 = MODE == kGateUp ? make_rsrc(static_cast<const uint8_t*>(p.s1) + tc.e * sstride,
+                                         static_cast<uint32_t>(sstride))
+                             : d.rbs0;
+    const int r = (wave & 3) * 64 + lane;   // weight row of the tile (waves 0..3 issue)
+    const int n = MODE == kGateUp ? tc.ntile * 128 + (r & 127) : min(tc.ntile * kBNf + r, p.N - 1);
+    d.bsoff = static_cast<uint32_t>(n) * (p.K / 32);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = (wave * 8 + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
+                                    : min(tc.ntile * kBNf + r, p.N - 1);
+      d.boff[i] = static_cast<uint32_t>(n) * p.K + c * 16;
+    }
   }
   d.soff = static_cast<uint32_t>(src_row(wave * 32 + (lane & 31))) * KB * 4u;
 
@@ -159,8 +209,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
   // main loop issues no vector memory instructions besides its DMA): gate/up -> block ntile of
   // s_gate and of s_up; down -> the two 128-column blocks of the 256-column tile.
   // fp32 scales are kept as their bit patterns, UE8M0 scales as the e8m0 byte.
-  __shared__ uint32_t wsc[2][kMaxKBlocks];
-  for (int i = tid; i < 2 * KB; i += 512) {
+  __shared__ uint32_t wsc[2][kW4 ? 1 : kMaxKBlocks];
+  for (int i = tid; i < (kW4 ? 0 : 2 * KB); i += 512) {
     const int which = i >= KB, kb = i - which * KB;
     const size_t blk = MODE == kGateUp ? static_cast<size_t>(tc.ntile)
                                        : static_cast<size_t>(min(tc.ntile * 2 + which, p.N / 128 - 1));
@@ -172,6 +222,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
   __syncthreads();
   const uint32_t* sw0 = wsc[MODE == kGateUp ? 0 : (brow0 >> 7)];
   const uint32_t* sw1 = wsc[MODE == kGateUp ? 1 : (brow0 >> 7)];
+  (void)sw0;
+  (void)sw1;
 
   f32x4_t acc[MI][NJ];
 #pragma unroll
@@ -181,38 +233,53 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(Fp8GemmArgs p) {
 
   const int nst = KB;
   char* const st0 = ring;
-  char* const st1 = ring + kStageF;
-  char* const st2 = ring + 2 * kStageF;
-  dmaf(st0, d, 0, nst, wave, lane);
-  dmaf(st1, d, 1, nst, wave, lane);
+  char* const st1 = ring + kStg;
+  char* const st2 = ring + 2 * kStg;
+  dmaf<kW4>(st0, d, 0, nst, wave, lane);
+  dmaf<kW4>(st1, d, 1, nst, wave, lane);
 
   // lane -> (row / column l % 16, 32-byte k slice l / 16) of a 16x16x128 MFMA operand
   const int lr = lane & 15, lk = lane >> 4;
 #define MOE_FP8_STAGE(CUR, NXT2, S)                                                           \
   {                                                                                           \
-    wait_vmcnt<13>(); /* this wave's DMA of stage S is done (S+1's 13 may be pending) */     \
+    /* this wave's DMA of stage S is done (S+1's may be pending) */                           \
+    wait_vmcnt<kDmaPerStage>();                                                               \
     __builtin_amdgcn_s_barrier();                                                             \
-    dmaf(NXT2, d, (S) + 2, nst, wave, lane);                                                  \
+    dmaf<kW4>(NXT2, d, (S) + 2, nst, wave, lane);                                             \
     i32x8_t fa[MI], fb[NJ];                                                                   \
     f32x4_t sa[MI];                                                                           \
-    int ea[MI];                                                                               \
+    int ea[MI], ebw[NJ];                                                                      \
     _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                          \
       const int row = arow0 + i * 16 + lr;                                                    \
-      fa[i] = ld32(CUR + swzf(row, 2 * lk), CUR + swzf(row, 2 * lk + 1));                     \
+      /* E2M1 weights: the e4m3 chunks in the 8-bit operand's K order (lk, 4 + lk) */        \
+      fa[i] = kW4 ? ld32(CUR + swzf(row, lk), CUR + swzf(row, 4 + lk))                        \
+                  : ld32(CUR + swzf(row, 2 * lk), CUR + swzf(row, 2 * lk + 1));               \
       if constexpr (kUE) {                                                                    \
         /* the e8m0 byte of the lane's row: exponent field of its power-of-two fp32 scale */  \
-        ea[i] = (*reinterpret_cast<const uint32_t*>(CUR + kAf + kBf + row * 4) >> 23) & 0xFF; \
+        ea[i] = (*reinterpret_cast<const uint32_t*>(CUR + kSA + row * 4) >> 23) & 0xFF;       \
       } else {                                                                                \
-        sa[i] = *reinterpret_cast<const f32x4_t*>(CUR + kAf + kBf +                           \
-                                                  (arow0 + i * 16 + 4 * lk) * 4);             \
+        sa[i] = *reinterpret_cast<const f32x4_t*>(CUR + kSA + (arow0 + i * 16 + 4 * lk) * 4); \
       }                                                                                       \
     }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                          \
       const int row = MODE == kGateUp ? (j < 2 ? brow0 + j * 16 : 128 + brow0 + (j - 2) * 16) \
                                       : brow0 + j * 16;                                       \
-      fb[j] = ld32(CUR + kAf + swzf(row + lr, 2 * lk), CUR + kAf + swzf(row + lr, 2 * lk + 1)); \
+      if constexpr (kW4) {                                                                    \
+        /* fragment row / 16, 16 bytes per lane; the lane's MX byte: row + lr, block lk */    \
+        const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(CUR + kAf + (row >> 4) * 1024 + lane * 16); \
+        fb[j] = i32x8_t{static_cast<int>(w4[0]), static_cast<int>(w4[1]),                     \
+                        static_cast<int>(w4[2]), static_cast<int>(w4[3]), 0, 0, 0, 0};        \
+        ebw[j] = static_cast<const uint8_t*>(static_cast<const void*>(CUR))[kSB + (row + lr) * 4 + lk]; \
+      } else {                                                                                \
+        fb[j] = ld32(CUR + kAf + swzf(row + lr, 2 * lk), CUR + kAf + swzf(row + lr, 2 * lk + 1)); \
+      }                                                                                       \
     }                                                                                         \
-    if constexpr (kUE) {                                                                      \
+    if constexpr (kW4) {                                                                      \
+      _Pragma("unroll") for (int i = 0; i < MI; ++i)                                          \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                        \
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                       \
+              fa[i], fb[j], acc[i][j], 0, 4, 0, ea[i], 0, ebw[j]);                            \
+    } else if constexpr (kUE) {                                                               \
       const int eb0 = static_cast<int>(sw0[S]), eb1 = static_cast<int>(sw1[S]);              \
       _Pragma("unroll") for (int i = 0; i < MI; ++i)                                          \
         _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                        \
@@ -383,16 +450,19 @@ hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream) {
   g.E = L.E;
   g.hq = static_cast<uint8_t*>(L.h);
   g.hs = L.h_scales;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  if (L.scale_ue8m0)
-    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true>), dim3(grid_for(P, L.E, L.f / 128)),
-                       dim3(512), 0, stream, g);
+  const bool w4 = L.w_fp4 != 0;
+  if (w4 && !L.scale_ue8m0) return hipErrorNotSupported;   // MX scales are e8m0 bytes
+  const dim3 grid1(grid_for(P, L.E, L.f / 128));
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
+  if (w4)
+    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true, true>), grid1, dim3(512), 0, stream, g);
+  else if (L.scale_ue8m0)
+    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true, false>), grid1, dim3(512), 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, false>), dim3(grid_for(P, L.E, L.f / 128)),
-                       dim3(512), 0, stream, g);
+    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, false, false>), grid1, dim3(512), 0, stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
 
   Fp8GemmArgs dn{};
   dn.a = static_cast<const uint8_t*>(L.h);
@@ -412,14 +482,15 @@ hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream) {
   dn.y_layout = L.y_layout;
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  if (L.scale_ue8m0)
-    hipLaunchKernelGGL((gemm_fp8_kernel<kDown, true>),
-                       dim3(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf)), dim3(512), 0, stream, dn);
+  const dim3 grid2(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf));
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
+  if (w4)
+    hipLaunchKernelGGL((gemm_fp8_kernel<kDown, true, true>), grid2, dim3(512), 0, stream, dn);
+  else if (L.scale_ue8m0)
+    hipLaunchKernelGGL((gemm_fp8_kernel<kDown, true, false>), grid2, dim3(512), 0, stream, dn);
   else
-    hipLaunchKernelGGL((gemm_fp8_kernel<kDown, false>),
-                       dim3(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf)), dim3(512), 0, stream, dn);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
+    hipLaunchKernelGGL((gemm_fp8_kernel<kDown, false, false>), grid2, dim3(512), 0, stream, dn);
+  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return hipGetLastError();
 }
 

@@ -168,7 +168,8 @@ def test_experts_validation(lib):
     fp4 = dict(act_dtype=moe.MOE_FP8_E4M3, w_dtype=moe.MOE_FP4_E2M1, x_scales=0x1000,
                s_gate=0x1000, s_up=0x1000, s_down=0x1000)
     assert _fwd(lib, **fp4) == UNS                             # E2M1 needs UE8M0 scales
-    assert _fwd(lib, T=129, scale_fmt=moe.MOE_SCALE_UE8M0, **fp4) == UNS   # 258 pairs > 256
+    fp4_ue = dict(fp4, scale_fmt=moe.MOE_SCALE_UE8M0)
+    assert _fwd(lib, **dict(fp4_ue, s_down=0x1002)) == UNS          # MX scales read as dwords
     assert _fwd(lib, act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_FP4_E2M1) == UNS
     assert (lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_FP8_E4M3,
                                            moe.MOE_FP4_E2M1) ==

@@ -138,8 +138,22 @@ def test_fp4_decode_layers(spec):
         assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, layout))
 
 
+# larger batches: the tiled fp8 GEMM with E2M1 weights (ragged row tiles, a partial down tile)
+PREFILL = [
+    synth.DSV3_FP8.with_(name="fp4pf_T300_d512_f256_E16_k4", T=300, d=512, f=256, E=16, k=4),
+    synth.DSV3_FP8.with_(name="fp4pf_T1000_d384_f640_E8_k2", T=1000, d=384, f=640, E=8, k=2),
+    synth.DSV3_FP8.with_(name="fp4pf_T257_d256_f128_E4_k1", T=257, d=256, f=128, E=4, k=1),
+]
+
+
+@pytest.mark.parametrize("spec", PREFILL, ids=lambda s: s.name)
+def test_fp4_prefill_layers(spec):
+    assert spec.P > 256
+    test_fp4_decode_layers(spec)
+
+
 def test_fp4_rejects_unsupported():
-    # E2M1 weights take UE8M0 scales only, and only the weight-streaming kernels (P <= 256)
+    # E2M1 weights take UE8M0 scales only
     spec = DECODE[0]
     wq, _ = _quantised(spec)
     (qg, sg), (qu, su), (qd, sd) = wq
@@ -151,17 +165,6 @@ def test_fp4_rejects_unsupported():
         moe.moe_experts_forward(xq, qg, qu, qd, perm.offsets, perm.sorted_pair, w, spec.k,
                                 x_scales=xs.float(), s_gate=sg, s_up=su, s_down=sd,
                                 scale_fmt="f32", w_fp4=True)
-    big = spec.with_(T=129, k=2)                         # 258 pairs
-    xb = torch.zeros((big.T, big.d), dtype=torch.uint8, device="cuda")
-    xbs = torch.full((big.T, big.d // 128), 127, dtype=torch.uint8, device="cuda")
-    ids_b = torch.zeros((big.T, 2), dtype=torch.int32, device="cuda")
-    ids_b[:, 1] = 1
-    perm_b = moe.moe_permute(ids_b, big.E)
-    wb = torch.full((big.T, 2), 0.5, dtype=torch.float32, device="cuda")
-    with pytest.raises(ValueError, match="UNSUPPORTED"):
-        moe.moe_experts_forward(xb, qg, qu, qd, perm_b.offsets, perm_b.sorted_pair, wb, 2,
-                                x_scales=xbs, s_gate=sg, s_up=su, s_down=sd, scale_fmt="ue8m0",
-                                w_fp4=True)
     torch.cuda.synchronize()
 
 
