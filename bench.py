@@ -214,9 +214,10 @@ def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
     }
 
 
-def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
+def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32", fp4=False):
     """Times one extra workload (given router logits) and returns its figures. fp8 layers take
-    fp32 block scales, or UE8M0 (e8m0 byte) scales with scale_fmt="ue8m0"."""
+    fp32 block scales, or UE8M0 (e8m0 byte) scales with scale_fmt="ue8m0"; fp4=True quantises
+    their weights to E2M1 with MX scales instead (UE8M0 activation scales)."""
     import numpy as np
     import torch
 
@@ -230,7 +231,25 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
     x = up(synth.gen_x(spec))
     logits = up(synth.gen_logits(spec))
     scales = None
-    if spec.dtype == "fp8":
+    if fp4:
+        spec = spec.with_(dtype="fp4")
+        scale_fmt = "ue8m0"
+        W, S = [], []
+        for which in ("gate", "up", "down"):
+            rows, cols = (spec.f, spec.d) if which != "down" else (spec.d, spec.f)
+            q = torch.empty((spec.E, rows, cols // 2), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((spec.E, rows, cols // 32), dtype=torch.uint8, device="cuda")
+            for e0 in range(0, spec.E, 16):
+                m = up(synth.gen_expert_weight(spec.with_(dtype="fp8"), which,
+                                               experts=range(e0, min(e0 + 16, spec.E))))
+                qq, ss = moe.fp4_quantize_weight_mx(m, tiled=True)
+                q[e0:e0 + 16] = qq
+                sc[e0:e0 + 16] = ss
+                del m
+            W.append(q)
+            S.append(sc)
+        scales = tuple(S)
+    elif spec.dtype == "fp8":
         W, S = [], []
         for which in ("gate", "up", "down"):
             rows, cols = (spec.f, spec.d) if which != "down" else (spec.d, spec.f)
@@ -248,7 +267,8 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
         scales = tuple(S)
     else:
         W = [up(synth.gen_expert_weight(spec, n)) for n in ("gate", "up", "down")]
-    name = spec.name + ("_ue8m0" if scale_fmt == "ue8m0" else "")
+    name = (spec.name.replace("fp8", "fp4") + "_mx") if fp4 else \
+        spec.name + ("_ue8m0" if scale_fmt == "ue8m0" else "")
     log("%s inputs ready in %.1fs" % (name, time.perf_counter() - t0))
     layer = Layer(moe, spec, x, tuple(W), steps, logits=logits, scales=scales,
                   scale_fmt=scale_fmt)
@@ -256,7 +276,7 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32"):
     g1, g2 = kernel_pass(layer, steps)
     counts = layer.counts.cpu().numpy()
     touched = int((counts > 0).sum())
-    wbytes = {"f32": 4, "bf16": 2, "fp8": 1}[spec.dtype]
+    wbytes = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5 + 1 / 32}[spec.dtype]
     w_bytes = touched * 3 * spec.d * spec.f * wbytes
     ms = el / steps * 1e3
     r = {
@@ -511,9 +531,11 @@ def main():
                                      fmt))
         del Wg, Wu, Wd
         torch.cuda.empty_cache()
-        for spec_o, fmt in ((synth.SKEWED_128E, "f32"), (synth.DSV3_FP8, "f32"),
-                            (synth.DSV3_FP8, "ue8m0"), (synth.TINY_F32, "f32")):
-            rep.append(measure_other(moe, synth, spec_o, max(args.steps, 5), args.warmup, fmt))
+        for spec_o, fmt, fp4 in ((synth.SKEWED_128E, "f32", False), (synth.DSV3_FP8, "f32", False),
+                                 (synth.DSV3_FP8, "ue8m0", False), (synth.DSV3_FP8, "ue8m0", True),
+                                 (synth.TINY_F32, "f32", False)):
+            rep.append(measure_other(moe, synth, spec_o, max(args.steps, 5), args.warmup, fmt,
+                                     fp4=fp4))
         with open(args.report, "w") as fh:
             json.dump({"prefill": {k: result[k] for k in ("value", "ms_per_step", "config",
                                                           "roofline")},
