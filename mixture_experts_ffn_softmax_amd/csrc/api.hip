@@ -144,6 +144,11 @@ moe_status moe_route(const float* logits, const void* x, moe_dtype x_dtype,
     if (!x || !w_router || !logits_out || d < 1) return MOE_ERR_INVALID_ARGUMENT;
     if (!is_float_type(x_dtype)) return MOE_ERR_UNSUPPORTED;
     if (static_cast<long long>(T) * d > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    if (T < 256 && d % 8 == 0 && aligned(x, 16) && aligned(w_router, 16))
+      // few tokens: one workgroup per token computes its logits and its top-k in one launch
+      // (the same arithmetic as the two separate kernels)
+      return dev(launch_fused_route(x, x_dtype, nullptr, w_router, logits_out, T, d, E, k,
+                                    topk_ids, topk_w, nullptr, nullptr, false, stream));
     hipError_t e = launch_router_logits(x, x_dtype, w_router, T, d, E, logits_out, stream);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
     logits = logits_out;
