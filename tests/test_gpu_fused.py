@@ -125,6 +125,21 @@ def test_fused_f32_output_and_max_pairs():
     _check_same(got, ref_seq, spec.name)
 
 
+@pytest.mark.parametrize("fmt", ("f32", "ue8m0", "fp4"))
+def test_fused_f32_activations(fmt):
+    # fp32 x with fp8 / FP4 experts: quantised inside the routing kernel; fp32 output
+    spec = synth.DSV3_FP8.with_(name="fz_xf32", T=20, d=384, f=256, E=8, k=2)
+    x = to_dev(synth.bf16_bits_to_f32(synth.gen_x(spec)) * np.float32(1.5))
+    W, S, _ = _weights(spec, fmt)
+    logits = to_dev(synth.gen_logits(spec))
+    ref_seq = _unfused(x, W, S, spec.k, logits, None, fmt, torch.float32)
+    got = moe.moe_fused_forward(x, *W, spec.k, logits=logits, s_gate=S[0], s_up=S[1],
+                                s_down=S[2], w_fp4=fmt == "fp4")
+    torch.cuda.synchronize()
+    assert got[0].dtype == torch.float32
+    _check_same(got, ref_seq, "fp32 x " + fmt)
+
+
 def test_fused_rejects_large_batches():
     spec = synth.DSV3_FP8.with_(name="fz_big", T=129, d=256, f=256, E=8, k=2)   # 258 pairs
     x = to_dev(synth.gen_x(spec))
