@@ -1,4 +1,4 @@
-// Fused small-batch path, launch 1 of 3: routing for one token per workgroup.
+// Fused small-batch path, its routing launch: one token per workgroup.
 //
 // The single fused MoE kernel idea (AWS fused-MoE news page: one kernel for routing, both expert
 // projections and the combine), taken as far as it pays on gfx950: routing, top-k and the
