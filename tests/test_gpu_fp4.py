@@ -204,3 +204,55 @@ def test_mixtral_fp4_decode_full_sampled():
                         ref_s["down"], quant_act=True, scale_fmt="ue8m0", w_fp4=True)
     ref = oracle.moe_forward(x[tokens], ex, ids_ref[tokens], w_ref[tokens])
     assert_close_rel_max(out_to_f64(res.out)[tokens], ref, 6e-2, "mixtral fp4 decode")
+
+
+def test_dsv3_fp4_full_sampled():
+    # the DeepSeek-V3-shaped layer (T=8192, d=7168, f=2048, E=256, k=8) with E2M1 experts, in the
+    # launch configuration the benchmark times (tiled GEMM); weights quantised and tiled on the GPU,
+    # the codes and scales of the experts the 12 sampled tokens use checked bit-exactly against
+    # the oracle's; the oracle runs on those tokens
+    spec = synth.DSV3_FP8
+    T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
+    log("generating", spec.name, "fp4")
+    x = synth.gen_x(spec)
+    logits = synth.gen_logits(spec)
+    ids_ref, w_ref = oracle.route(logits, k)
+    rng = np.random.default_rng(3)
+    tokens = np.sort(rng.choice(T, 12, replace=False))
+    need = sorted(set(ids_ref[tokens].reshape(-1).tolist()))
+    remap = {e: i for i, e in enumerate(need)}
+    dev_q, dev_s, ref_q, ref_s = {}, {}, {}, {}
+    for which in ("gate", "up", "down"):
+        rows, cols = (f, d) if which != "down" else (d, f)
+        qt = torch.empty((E, rows, cols // 2), dtype=torch.uint8, device="cuda")
+        st = torch.empty((E, rows, cols // 32), dtype=torch.uint8, device="cuda")
+        rq = np.empty((len(need), rows, cols // 2), np.uint8)
+        rs = np.empty((len(need), rows, cols // 32), np.uint8)
+        for e0 in range(0, E, 16):
+            chunk = list(range(e0, e0 + 16))
+            m = synth.gen_expert_weight(spec, which, experts=chunk)
+            q, s = moe.fp4_quantize_weight_mx(to_dev(m))
+            sel = [e for e in chunk if e in remap]
+            if sel:
+                oq, os_ = oracle.quantize_weight_mxfp4(m[[e - e0 for e in sel]])
+                np.testing.assert_array_equal(to_host(q[[e - e0 for e in sel]]), oq)
+                np.testing.assert_array_equal(to_host(s[[e - e0 for e in sel]]), os_)
+                for i, e in enumerate(sel):
+                    rq[remap[e]] = oq[i]
+                    rs[remap[e]] = os_[i]
+            qt[e0:e0 + 16] = moe.fp4_tile_weight(q)
+            st[e0:e0 + 16] = s
+        dev_q[which], dev_s[which] = qt, st
+        ref_q[which], ref_s[which] = rq, rs
+    log("weights quantised; running the layer")
+    res = moe.moe_layer(to_dev(x), dev_q["gate"], dev_q["up"], dev_q["down"], k,
+                        logits=to_dev(logits), s_gate=dev_s["gate"], s_up=dev_s["up"],
+                        s_down=dev_s["down"], w_fp4=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(res.topk_ids), ids_ref)
+    got = out_to_f64(res.out)[tokens]
+    ex = oracle.Experts(ref_q["gate"], ref_q["up"], ref_q["down"], ref_s["gate"], ref_s["up"],
+                        ref_s["down"], quant_act=True, scale_fmt="ue8m0", w_fp4=True)
+    ids_sub = np.vectorize(remap.get)(ids_ref[tokens]).astype(np.int32)
+    ref = oracle.moe_forward(x[tokens], ex, ids_sub, w_ref[tokens])
+    assert_close_rel_max(got, ref, 6e-2, "%s fp4" % spec.name)
