@@ -58,6 +58,11 @@ CASES = [
                                         E=8, k=2)),
     ("bf16", synth.MIXTRAL_DECODE.with_(name="fz_bf16_T100_d384_f256_E4_k2", T=100, d=384, f=256,
                                         E=4, k=2)),
+    # skewed: experts of 44-64 tokens beside experts of a few and empty ones
+    ("bf16", synth.MIXTRAL_DECODE.with_(name="fz_bf16_T64_d256_f512_E16_k2_skew", T=64, d=256,
+                                        f=512, E=16, k=2, logits="given", skew=3.0)),
+    ("bf16", synth.MIXTRAL_DECODE.with_(name="fz_bf16_T64_d256_f512_E8_k2_skew", T=64, d=256,
+                                        f=512, E=8, k=2, logits="given", skew=2.0)),
     ("f32", synth.DSV3_FP8.with_(name="fz_fp8_T32_d512_f384_E8_k2", T=32, d=512, f=384, E=8, k=2)),
     ("ue8m0", synth.DSV3_FP8.with_(name="fz_fp8ue_T32_d512_f384_E8_k2", T=32, d=512, f=384, E=8,
                                    k=2)),

@@ -137,6 +137,23 @@ def test_decode_kernel_many_tokens_per_expert():
     assert counts.max() > 64
 
 
+@pytest.mark.parametrize("E", [16, 8])
+def test_decode_skewed_partial_token_groups(E):
+    # 128 pairs, skewed: two experts hold 50-64 tokens (a pass of 64 with its last group of 16
+    # partly filled), the rest a few each (streaming gate/up kernel), the others none.
+    spec = synth.TINY_F32.with_(name="bf16_decode_skew_T64_d256_f512_E%d_k2" % E, dtype="bf16",
+                                T=64, d=256, f=512, E=E, k=2, skew=3.0)
+    inp = layer_inputs(spec)
+    ids, _ = oracle.route(inp["logits"], spec.k)
+    counts = np.bincount(ids.reshape(-1), minlength=spec.E)
+    assert counts.max() > 48 and ((counts > 0) & (counts <= 16)).any() and (counts == 0).any(), \
+        counts
+    for layout in ("slots", "acc_f32"):
+        log(spec.name, layout, counts.tolist())
+        res = _run_gpu(spec, inp, layout)
+        _check_layer(spec, inp, res, 2e-2)
+
+
 def test_decode_mixed_small_and_large_experts():
     # Skewed routing at a decode-sized batch: some experts get at most 16 tokens (streaming
     # kernel), others more (the multi-pass kernel); both run in one call, K a multiple of 256.
