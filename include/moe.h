@@ -235,6 +235,9 @@ moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q
  *        quantiser writes them) s_gate / s_up [E, f, d/32] and s_down [E, d, f/32]; x and h
  *        e4m3 with UE8M0 per-128 scales. d % 128 == f % 128 == 0; the three MX scale arrays
  *        4-byte aligned (MOE_ERR_UNSUPPORTED otherwise).
+ * Alignment on every path but F32 / F32 / F32: x, w_gate, w_up, w_down and y 16-byte aligned,
+ * fp32 scale arrays 4-byte aligned (MOE_ERR_UNSUPPORTED otherwise). Contiguous tensors from a
+ * device allocator, and their slices along the expert or token dimension, satisfy this.
  * ------------------------------------------------------------------------------------------ */
 typedef struct {
   int T, d, f, E, k;
@@ -297,7 +300,8 @@ moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
  *  x [T, d] (MOE_BF16, or MOE_F32 with fp8 / FP4 experts), 16-byte aligned.
  *  logits [T, E] fp32 router logits, or NULL: computed as x . w_router^T (w_router [E, d] fp32,
  *    16-byte aligned), and written to logits_out [T, E] when that is non-NULL.
- *  w_dtype / scale_fmt and the weight and scale arrays: as for moe_experts_forward (MOE_BF16 with
+ *  w_dtype / scale_fmt and the weight and scale arrays: as for moe_experts_forward, alignment
+ *    included (MOE_BF16 with
  *    bf16 x; MOE_FP8_E4M3 with fp32 or UE8M0 block scales; MOE_FP4_E2M1 in fragment order with MX
  *    scales, UE8M0 only); fp8 / FP4 quantise x per token per 128 channels here.
  *  out [T, d] (out_dtype MOE_BF16 or MOE_F32); topk_ids / topk_w [T, k] out (required).

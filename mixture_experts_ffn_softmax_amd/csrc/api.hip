@@ -301,6 +301,14 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
     if (a->d > 32768 || a->f > 32768) return MOE_ERR_UNSUPPORTED;
     if (!a->x_scales || !a->s_gate || !a->s_up || !a->s_down) return MOE_ERR_INVALID_ARGUMENT;
   }
+  // the matrix-core paths read x and the weights with 16-byte loads and LDS DMA, and store y
+  // with 8- and 16-byte stores; fp32 block scales are read as dwords
+  if (!f32 && (!aligned(a->x, 16) || !aligned(a->w_gate, 16) || !aligned(a->w_up, 16) ||
+               !aligned(a->w_down, 16) || !aligned(a->y, 16)))
+    return MOE_ERR_UNSUPPORTED;
+  if (fp8 && !ue8m0 && (!aligned(a->x_scales, 4) || !aligned(a->s_gate, 4) ||
+                        !aligned(a->s_up, 4) || !aligned(a->s_down, 4)))
+    return MOE_ERR_UNSUPPORTED;
   const long long P = static_cast<long long>(a->T) * a->k;
   // E2M1 weights: MX scales are e8m0 bytes
   if (w4 && !ue8m0) return MOE_ERR_UNSUPPORTED;
@@ -461,6 +469,10 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   if (a->d % kFp8Group || a->f % kFp8Group) return MOE_ERR_UNSUPPORTED;
   if (a->d > 32768 || a->f > 32768) return MOE_ERR_UNSUPPORTED;
   if (!aligned(a->x, 16) || (!a->logits && !aligned(a->w_router, 16))) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(a->w_gate, 16) || !aligned(a->w_up, 16) || !aligned(a->w_down, 16))
+    return MOE_ERR_UNSUPPORTED;
+  if (lowp && !ue8m0 && (!aligned(a->s_gate, 4) || !aligned(a->s_up, 4) || !aligned(a->s_down, 4)))
+    return MOE_ERR_UNSUPPORTED;
   if (static_cast<long long>(a->f) * a->d > INT_MAX / 4) return MOE_ERR_UNSUPPORTED;
   const FusedLayout L = fused_layout(a->T, a->d, a->f, a->k, w, a->out_dtype);
   if (!a->workspace) return MOE_ERR_INVALID_ARGUMENT;

@@ -171,6 +171,15 @@ def test_experts_validation(lib):
     fp4_ue = dict(fp4, scale_fmt=moe.MOE_SCALE_UE8M0)
     assert _fwd(lib, **dict(fp4_ue, s_down=0x1002)) == UNS          # MX scales read as dwords
     assert _fwd(lib, act_dtype=moe.MOE_BF16, w_dtype=moe.MOE_FP4_E2M1) == UNS
+    # 16-byte vector loads / LDS DMA of x and weights, vector stores of y; fp32 scales as dwords
+    for name in ("x", "w_gate", "w_up", "w_down", "y"):
+        assert _fwd(lib, **{name: 0x1008}) == UNS, name
+    fp8_s = dict(fp8, x_scales=0x1000, s_gate=0x1000, s_up=0x1000, s_down=0x1000)
+    assert _fwd(lib, **dict(fp8_s, s_up=0x1002)) == UNS
+    assert _fwd(lib, **dict(fp8_s, x=0x1008)) == UNS
+    # the fp32 path takes any alignment: a misaligned x gets as far as the workspace check
+    f32 = dict(act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32, y_dtype=moe.MOE_F32)
+    assert _fwd(lib, x=0x1004, workspace_bytes=1, **f32) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
     assert (lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_FP8_E4M3,
                                            moe.MOE_FP4_E2M1) ==
             lib.moe_experts_workspace_size(32, 256, 512, 8, 2, moe.MOE_FP8_E4M3,
@@ -202,6 +211,8 @@ def test_fused_validation(lib):
     assert _fz(lib, topk_ids=None) == INV
     assert _fz(lib, logits=None) == INV                            # neither logits nor router
     assert _fz(lib, x=0x1008) == UNS                               # x alignment
+    for name in ("w_gate", "w_up", "w_down"):
+        assert _fz(lib, **{name: 0x1008}) == UNS, name
     assert _fz(lib, w_dtype=moe.MOE_F32) == UNS
     assert _fz(lib, x_dtype=moe.MOE_F32) == UNS                    # bf16 experts take bf16 x
     assert _fz(lib, out_dtype=moe.MOE_FP8_E4M3) == INV
@@ -210,6 +221,7 @@ def test_fused_validation(lib):
     assert _fz(lib, w_dtype=moe.MOE_FP4_E2M1, s_gate=0x1000, s_up=0x1000,
                s_down=0x1000) == UNS                               # FP4 needs UE8M0
     assert _fz(lib, scale_fmt=5, **fp8) == INV
+    assert _fz(lib, **dict(fp8, s_down=0x1002)) == UNS             # fp32 scales read as dwords
     assert _fz(lib, workspace=None, **fp8) == INV
     need = lib.moe_fused_workspace_size(32, 256, 512, 8, 2, moe.MOE_FP8_E4M3, moe.MOE_BF16)
     assert need > 64 * 512 * 4                                     # at least h in fp32

@@ -114,6 +114,8 @@ DECODE = [
     # P = 256, the largest batch the streaming kernels take; f not a multiple of 256
     synth.DSV3_FP8.with_(name="fp4dec_T64_d384_f640_E16_k4", T=64, d=384, f=640, E=16, k=4),
     synth.DSV3_FP8.with_(name="fp4dec_T3_d128_f128_E4_k1", T=3, d=128, f=128, E=4, k=1),
+    # every token on every expert
+    synth.DSV3_FP8.with_(name="fp4dec_all_T16_d256_f128_E4_k4", T=16, d=256, f=128, E=4, k=4),
 ]
 
 

@@ -41,6 +41,9 @@ SMALL = [
     synth.DSV3_FP8.with_(name="fp8_T300_d512_f256_E16_k4", T=300, d=512, f=256, E=16, k=4),
     synth.DSV3_FP8.with_(name="fp8_T1000_d384_f640_E8_k2", T=1000, d=384, f=640, E=8, k=2),
     synth.DSV3_FP8.with_(name="fp8_T7_d256_f128_E4_k1", T=7, d=256, f=128, E=4, k=1),
+    # one expert (small-batch kernels) and k = E (tiled GEMMs)
+    synth.DSV3_FP8.with_(name="fp8_dense_T40_d256_f128_E1_k1", T=40, d=256, f=128, E=1, k=1),
+    synth.DSV3_FP8.with_(name="fp8_all_T100_d256_f128_E4_k4", T=100, d=256, f=128, E=4, k=4),
 ]
 
 

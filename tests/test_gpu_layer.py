@@ -77,6 +77,16 @@ SMALL_BF16 = [
                          E=4, k=1),
     synth.TINY_F32.with_(name="bf16_T5_d128_f128_E8_k2", dtype="bf16", T=5, d=128, f=128),
     synth.MIXTRAL_PREFILL.with_(name="bf16_router_T600_d512_f1024_E8_k2", T=600, d=512, f=1024),
+    # degenerate topologies: one expert (a dense gated MLP, routing weight 1) and every token on
+    # every expert (k = E), each on the tiled GEMMs (P > 256) and the small-batch kernels
+    synth.TINY_F32.with_(name="bf16_dense_T300_d256_f384_E1_k1", dtype="bf16", T=300, d=256,
+                         f=384, E=1, k=1),
+    synth.TINY_F32.with_(name="bf16_dense_T20_d256_f256_E1_k1", dtype="bf16", T=20, d=256, f=256,
+                         E=1, k=1),
+    synth.TINY_F32.with_(name="bf16_all_T100_d256_f256_E4_k4", dtype="bf16", T=100, d=256, f=256,
+                         E=4, k=4),
+    synth.TINY_F32.with_(name="bf16_all_T16_d256_f256_E4_k4", dtype="bf16", T=16, d=256, f=256,
+                         E=4, k=4),
 ]
 
 
