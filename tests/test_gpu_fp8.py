@@ -44,6 +44,7 @@ SMALL = [
     # one expert (small-batch kernels) and k = E (tiled GEMMs)
     synth.DSV3_FP8.with_(name="fp8_dense_T40_d256_f128_E1_k1", T=40, d=256, f=128, E=1, k=1),
     synth.DSV3_FP8.with_(name="fp8_all_T100_d256_f128_E4_k4", T=100, d=256, f=128, E=4, k=4),
+    synth.DSV3_FP8.with_(name="fp8_one_T1_d256_f128_E8_k2", T=1, d=256, f=128, E=8, k=2),
 ]
 
 

@@ -87,6 +87,9 @@ SMALL_BF16 = [
                          E=4, k=4),
     synth.TINY_F32.with_(name="bf16_all_T16_d256_f256_E4_k4", dtype="bf16", T=16, d=256, f=256,
                          E=4, k=4),
+    # a single token: one row per selected expert, every other expert empty
+    synth.TINY_F32.with_(name="bf16_one_T1_d256_f256_E8_k2", dtype="bf16", T=1, d=256, f=256,
+                         E=8, k=2),
 ]
 
 
