@@ -2,15 +2,18 @@
 """Benchmark of the sparse MoE experts forward pass on one MI355X.
 
 One step = one pass of the whole hot path over one batch: router logits (x . Wr^T) + softmax
-top-k (moe_route), expert grouping (moe_permute), gate/up grouped GEMM + SwiGLU and down grouped
-GEMM with the fused unpermute/weighting epilogue (moe_experts_forward), and the k-slot combine
-(moe_combine). Workload: the Mixtral-shaped prefill layer (T=4096 tokens, d=4096, f=14336, E=8,
-top-2, bf16 with fp32 accumulation), synthetic seeded inputs already resident in HBM.
+top-k (moe_route), expert grouping (moe_permute), fp8 activation quantisation (fp8 layers), gate/up
+grouped GEMM + SwiGLU and down grouped GEMM with the fused unpermute/weighting epilogue
+(moe_experts_forward), and the k-slot combine (moe_combine). Synthetic seeded inputs, already
+resident in HBM.
 
-Prints one JSON line: active TFLOP/s (6*T*k*d*f per step), tokens/s, the roofline of the dominant
-kernel (gate/up GEMM, MFMA-bound) timed with HIP events on the launch stream, the Mixtral-shaped
-decode layer (T=32, weight-streaming, HBM-bound) on the same weights, and the CPU oracle timed on a
-bounded token sample as a reference baseline.
+The JSON line's value is the Mixtral-shaped prefill layer (T=4096 tokens, d=4096, f=14336, E=8,
+top-2, bf16 with fp32 accumulation) in active TFLOP/s, with the roofline of its dominant kernel
+(the gate/up GEMM, MFMA-bound) timed with HIP events on the launch stream. The same line carries
+the Mixtral-shaped decode layer (T=32, weight streaming, HBM-bound), the skewed 128-expert bf16
+layer (T=16384, d=2048, f=768, k=8), the DeepSeek-V3-shaped fine-grained FP8 layer (T=8192,
+d=7168, f=2048, E=256, k=8) with fp32 and with UE8M0 block scales, each with its own roofline
+object, and the CPU oracle timed on a bounded token sample as a reference baseline.
 """
 from __future__ import annotations
 
@@ -100,8 +103,10 @@ class Layer:
         self.ews = torch.empty(ew, dtype=torch.uint8, device=dev)
         self.y = torch.empty((T, k, d), dtype=tdt, device=dev)
         self.out = torch.empty((T, d), dtype=tdt, device=dev)
-        self.events = [[moe.event_create() for _ in range(4)] for _ in range(n_ev_steps)]
-        self.ev_arrays = [(ctypes.c_void_p * 4)(*e) for e in self.events]
+        # per-projection timing: HIP events on the stream the library launches on (torch's
+        # current stream, which self.stream is), around a gate/up-only and a down-only call
+        self.events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                       for _ in range(n_ev_steps)]
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
         self._quant = None
@@ -124,8 +129,8 @@ class Layer:
             Wd.data_ptr(), sg.data_ptr() if sg is not None else None,
             su.data_ptr() if su is not None else None, sd.data_ptr() if sd is not None else None,
             self.offsets.data_ptr(), self.sp.data_ptr(), self.w.data_ptr(), self.y.data_ptr(),
-            self.ews.data_ptr(), self.ews.numel(), None,
-            moe.MOE_SCALE_UE8M0 if ue else moe.MOE_SCALE_F32)
+            self.ews.data_ptr(), self.ews.numel(),
+            moe.MOE_SCALE_UE8M0 if ue else moe.MOE_SCALE_F32, moe.MOE_PHASE_ALL)
         if logits is None:
             self._route = (None, p(x), act, p(Wr), T, d, E, k, p(self.logits), p(self.ids),
                            p(self.w), self.stream)
@@ -144,14 +149,26 @@ class Layer:
         chk(lib.moe_permute(*self._perm))
         if self._quant is not None:
             chk(self._quant_fn(*self._quant))
-        self.args.events = (ctypes.cast(self.ev_arrays[ev_index], ctypes.c_void_p)
-                            if ev_index is not None else None)
-        chk(lib.moe_experts_forward(ctypes.byref(self.args), self.stream))
+        if ev_index is None:
+            self.args.phase = self.moe.MOE_PHASE_ALL
+            chk(lib.moe_experts_forward(ctypes.byref(self.args), self.stream))
+        else:
+            # the same work as one MOE_PHASE_ALL call, split so that events bracket each projection
+            ev = self.events[ev_index]
+            ev[0].record()
+            self.args.phase = self.moe.MOE_PHASE_GATE_UP
+            chk(lib.moe_experts_forward(ctypes.byref(self.args), self.stream))
+            ev[1].record()
+            self.args.phase = self.moe.MOE_PHASE_DOWN
+            chk(lib.moe_experts_forward(ctypes.byref(self.args), self.stream))
+            ev[2].record()
         chk(lib.moe_combine(*self._comb))
 
     def kernel_ms(self, n):
-        g1 = [self.moe.event_elapsed_ms(e[0], e[1]) for e in self.events[:n]]
-        g2 = [self.moe.event_elapsed_ms(e[2], e[3]) for e in self.events[:n]]
+        """Mean duration (ms) of the gate/up phase (its tile-table launch included) and of the
+        down phase over the first n event-timed steps."""
+        g1 = [e[0].elapsed_time(e[1]) for e in self.events[:n]]
+        g2 = [e[1].elapsed_time(e[2]) for e in self.events[:n]]
         return sum(g1) / n, sum(g2) / n
 
 
@@ -180,12 +197,31 @@ def kernel_pass(layer, steps):
     return layer.kernel_ms(steps)
 
 
+def host_cpu():
+    """Model name, logical CPUs available to this process, and the OpenMP thread setting."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    return model, nproc, os.environ.get("OMP_NUM_THREADS")
+
+
 def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
     """The oracle, as it stands, on the first n tokens of the workload (routing included)."""
     import numpy as np
     import oracle
     ex = oracle.Experts(*W_np)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model, nproc, omp = host_cpu()
+    threads = int(omp) if omp else nproc   # the oracle's OpenMP loops use this many threads
 
     def run(n):
         xs = np.ascontiguousarray(x_np[:n])
@@ -206,7 +242,10 @@ def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
         "unit": "TFLOP/s",
         "tokens_per_s": round(toks, 2),
         "seconds": round(dt, 2),
-        "cores": cores,
+        "cores": threads,
+        "cpu_model": model,
+        "nproc": nproc,
+        "omp_num_threads": omp,
         "kind": "oracle",
         "sample": "first %d of the %d tokens of %s (%d token-expert pairs): router logits, "
                   "top-k routing, experts and combine, fp64 per-token loop" % (
@@ -214,10 +253,63 @@ def cpu_baseline(spec, x_np, Wr_np, W_np, seconds):
     }
 
 
-def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32", fp4=False):
-    """Times one extra workload (given router logits) and returns its figures. fp8 layers take
-    fp32 block scales, or UE8M0 (e8m0 byte) scales with scale_fmt="ue8m0"; fp4=True quantises
-    their weights to E2M1 with MX scales instead (UE8M0 activation scales)."""
+def expert_histogram(counts):
+    """Per-expert load summary: rows of the busiest and least busy expert, empty experts, and the
+    share of all pairs taken by the busiest expert and by the 8 busiest."""
+    import numpy as np
+    c = np.sort(np.asarray(counts, np.int64))[::-1]
+    tot = max(int(c.sum()), 1)
+    return {"max_rows": int(c[0]), "min_rows": int(c[-1]), "empty": int((c == 0).sum()),
+            "nonempty": int((c > 0).sum()), "max_share": round(float(c[0]) / tot, 4),
+            "top8_share": round(float(c[:8].sum()) / tot, 4)}
+
+
+def lowp_weights(moe, synth, spec, fmts, fp4=False):
+    """Expert weights of an fp8 workload on the device, quantised there from the generator's fp32
+    masters (16 experts at a time): {fmt: ((W_gate, W_up, W_down), (s_gate, s_up, s_down))} for
+    each fmt in fmts ("f32" / "ue8m0" block scales), or {"fp4": ...} E2M1 with MX scales."""
+    import numpy as np
+    import torch
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    out = {f: ([], []) for f in (("fp4",) if fp4 else fmts)}
+    for which in ("gate", "up", "down"):
+        rows, cols = (spec.f, spec.d) if which != "down" else (spec.d, spec.f)
+        bufs = {}
+        for f in out:
+            if f == "fp4":
+                bufs[f] = (torch.empty((spec.E, rows, cols // 2), dtype=torch.uint8, device="cuda"),
+                           torch.empty((spec.E, rows, cols // 32), dtype=torch.uint8, device="cuda"))
+            else:
+                bufs[f] = (torch.empty((spec.E, rows, cols), dtype=torch.uint8, device="cuda"),
+                           torch.empty((spec.E, rows // 128, cols // 128), device="cuda",
+                                       dtype=torch.uint8 if f == "ue8m0" else torch.float32))
+        for e0 in range(0, spec.E, 16):
+            m = up(synth.gen_expert_weight(spec.with_(dtype="fp8"), which,
+                                           experts=range(e0, min(e0 + 16, spec.E))))
+            for f, (q, sc) in bufs.items():
+                if f == "fp4":
+                    qq, ss = moe.fp4_quantize_weight_mx(m, tiled=True)
+                else:
+                    qq, ss = moe.fp8_quantize_weight(m, scale_fmt=f)
+                q[e0:e0 + 16] = qq
+                sc[e0:e0 + 16] = ss
+            del m
+        for f, (q, sc) in bufs.items():
+            out[f][0].append(q)
+            out[f][1].append(sc)
+    return {f: (tuple(w), tuple(sc)) for f, (w, sc) in out.items()}
+
+
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+
+
+def measure_other(moe, synth, spec, steps, warmup, weights=None, scale_fmt="f32", name=None):
+    """Times one workload with given router logits and returns its figures, with the roofline of
+    its gate/up GEMM (the kernel that takes the most time). ``weights``: device (W, S) of a
+    low-precision layer (lowp_weights), with scale_fmt "f32", "ue8m0" or "fp4" (E2M1, MX)."""
     import numpy as np
     import torch
 
@@ -231,44 +323,14 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32", fp4=False):
     x = up(synth.gen_x(spec))
     logits = up(synth.gen_logits(spec))
     scales = None
-    if fp4:
-        spec = spec.with_(dtype="fp4")
-        scale_fmt = "ue8m0"
-        W, S = [], []
-        for which in ("gate", "up", "down"):
-            rows, cols = (spec.f, spec.d) if which != "down" else (spec.d, spec.f)
-            q = torch.empty((spec.E, rows, cols // 2), dtype=torch.uint8, device="cuda")
-            sc = torch.empty((spec.E, rows, cols // 32), dtype=torch.uint8, device="cuda")
-            for e0 in range(0, spec.E, 16):
-                m = up(synth.gen_expert_weight(spec.with_(dtype="fp8"), which,
-                                               experts=range(e0, min(e0 + 16, spec.E))))
-                qq, ss = moe.fp4_quantize_weight_mx(m, tiled=True)
-                q[e0:e0 + 16] = qq
-                sc[e0:e0 + 16] = ss
-                del m
-            W.append(q)
-            S.append(sc)
-        scales = tuple(S)
-    elif spec.dtype == "fp8":
-        W, S = [], []
-        for which in ("gate", "up", "down"):
-            rows, cols = (spec.f, spec.d) if which != "down" else (spec.d, spec.f)
-            q = torch.empty((spec.E, rows, cols), dtype=torch.uint8, device="cuda")
-            sc = torch.empty((spec.E, rows // 128, cols // 128), device="cuda",
-                             dtype=torch.uint8 if scale_fmt == "ue8m0" else torch.float32)
-            for e0 in range(0, spec.E, 16):
-                m = up(synth.gen_expert_weight(spec, which, experts=range(e0, min(e0 + 16, spec.E))))
-                qq, ss = moe.fp8_quantize_weight(m, scale_fmt=scale_fmt)
-                q[e0:e0 + 16] = qq
-                sc[e0:e0 + 16] = ss
-                del m
-            W.append(q)
-            S.append(sc)
-        scales = tuple(S)
+    if weights is not None:
+        W, scales = weights
+        if scale_fmt == "fp4":
+            spec = spec.with_(dtype="fp4")
+            scale_fmt = "ue8m0"
     else:
         W = [up(synth.gen_expert_weight(spec, n)) for n in ("gate", "up", "down")]
-    name = (spec.name.replace("fp8", "fp4") + "_mx") if fp4 else \
-        spec.name + ("_ue8m0" if scale_fmt == "ue8m0" else "")
+    name = name or spec.name
     log("%s inputs ready in %.1fs" % (name, time.perf_counter() - t0))
     layer = Layer(moe, spec, x, tuple(W), steps, logits=logits, scales=scales,
                   scale_fmt=scale_fmt)
@@ -279,17 +341,53 @@ def measure_other(moe, synth, spec, steps, warmup, scale_fmt="f32", fp4=False):
     wbytes = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5 + 1 / 32}[spec.dtype]
     w_bytes = touched * 3 * spec.d * spec.f * wbytes
     ms = el / steps * 1e3
+    tflops = spec.active_flops() / (ms * 1e-3) / 1e12
+    g1_flops = 4.0 * spec.P * spec.d * spec.f
     r = {
         "workload": name, "ms_per_step": round(ms, 4),
-        "active_tflops": round(spec.active_flops() / (ms * 1e-3) / 1e12, 2),
+        "active_tflops": round(tflops, 2),
         "tokens_per_s": round(spec.T / (ms * 1e-3), 1),
         "gate_up_ms": round(g1, 4), "down_ms": round(g2, 4),
-        "gate_up_tflops": round(4.0 * spec.P * spec.d * spec.f / (g1 * 1e-3) / 1e12, 2),
+        "gate_up_tflops": round(g1_flops / (g1 * 1e-3) / 1e12, 2),
         "down_tflops": round(2.0 * spec.P * spec.d * spec.f / (g2 * 1e-3) / 1e12, 2),
         "weight_GBps_layer": round(w_bytes / (ms * 1e-3) / 1e9, 1),
-        "experts_touched": touched, "expert_rows_max": int(counts.max()),
-        "experts_empty": int((counts == 0).sum()),
+        "experts_touched": touched,
+        "expert_histogram": expert_histogram(counts),
     }
+    if spec.dtype in ("fp8", "fp4"):
+        # gate/up roofline: the weights of the touched experts (+ their scales), the x codes and
+        # scales, and the h codes and scales it writes, against 8 TB/s; its FLOPs against the fp8
+        # peak. The larger of the two ideal times is the bound.
+        P, d, f = spec.P, spec.d, spec.f
+        sc_w = 2 * f * d / 32 if spec.dtype == "fp4" else 2 * (f // 128) * (d // 128) * 4
+        g1_bytes = touched * (2 * f * d * wbytes + sc_w) + spec.T * d * (1 + 4 / 128) + \
+            P * f * (1 + 4 / 128)
+        t_hbm = g1_bytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = g1_flops / (FP8_PEAK_TFLOPS * 1e12)
+        hbm = {"bound": "hbm", "achieved": round(g1_bytes / (g1 * 1e-3) / 1e9, 1),
+               "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(g1_bytes / (g1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        mfma = {"bound": "mfma", "achieved": round(g1_flops / (g1 * 1e-3) / 1e12, 2),
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g1_flops / (g1 * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        roof = dict(hbm if t_hbm >= t_mfma else mfma)
+        roof["kernel"] = "gemm_fp8_kernel<gate_up> (gate/up grouped GEMM + SwiGLU + h quantisation)"
+        roof["other_roof_frac"] = (mfma if t_hbm >= t_mfma else hbm)["frac"]
+        roof["traffic"] = None
+        r["roofline"] = roof
+        r["pct_fp8_peak"] = round(100 * tflops / FP8_PEAK_TFLOPS, 2)
+        ideal = max(w_bytes / (HBM_PEAK_GBS * 1e9), spec.active_flops() / (FP8_PEAK_TFLOPS * 1e12))
+        r["pct_hbm_peak"] = round(100 * w_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+        r["layer_roofline_frac"] = round(ideal / (ms * 1e-3), 4)
+    elif spec.dtype == "bf16":
+        r["roofline"] = {"kernel": "gemm_bf16_kernel<gate_up> (gate/up grouped GEMM + SwiGLU)",
+                         "bound": "mfma", "achieved": r["gate_up_tflops"],
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(r["gate_up_tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None}
+        r["pct_bf16_peak"] = round(100 * tflops / BF16_PEAK_TFLOPS, 2)
+        r["layer_roofline_frac"] = round(
+            spec.active_flops() / (BF16_PEAK_TFLOPS * 1e12) / (ms * 1e-3), 4)
     log("%s: %.3f ms/step, %.1f TFLOP/s (gate/up %.3f ms, down %.3f ms)" % (
         name, ms, r["active_tflops"], g1, g2))
     del layer
@@ -392,9 +490,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the skewed 128-expert and DeepSeek-V3-shaped fp8 workloads")
     ap.add_argument("--report", default="",
-                    help="also time the skewed 128-expert bf16 layer, the DeepSeek-V3-shaped fp8 "
-                         "layer (fp32 and UE8M0 block scales) and the tiny fp32 layer; write their "
+                    help="also time the fp8 / FP4 and fused decode variants, the DeepSeek-V3-shaped "
+                         "layer with FP4 experts and the tiny fp32 layer; write every workload's "
                          "figures to this JSON file")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain fp32 copy kernel (out = in * 1) over this many MiB, "
@@ -519,8 +619,9 @@ def main():
         }
         del dl
 
+    rep = []
     if args.report:
-        rep = [result.get("decode")]
+        rep.append(result.get("decode"))
         for fmt in ("f32", "ue8m0"):
             rep.append(measure_decode_fp8(moe, synth, (Wg, Wu, Wd), Wr, max(args.decode_steps, 5),
                                           5, fmt))
@@ -529,13 +630,35 @@ def main():
         for fmt in ("bf16", "ue8m0", "fp4"):
             rep.append(measure_fused(moe, synth, (Wg, Wu, Wd), Wr, max(args.decode_steps, 5), 5,
                                      fmt))
-        del Wg, Wu, Wd
+    del Wg, Wu, Wd
+    torch.cuda.empty_cache()
+
+    # The skewed 128-expert layer and the DeepSeek-V3-shaped fine-grained FP8 layer (its own
+    # fp32 128x128 block scales, and the same masters with UE8M0 scales) are part of every run.
+    if not args.no_others:
+        osteps = max(args.steps, 5)
+        result["skewed"] = measure_other(moe, synth, synth.SKEWED_128E, osteps, args.warmup)
+        t0 = time.perf_counter()
+        wq = lowp_weights(moe, synth, synth.DSV3_FP8, ("f32", "ue8m0"))
+        log("%s weights quantised on the device in %.1fs" % (synth.DSV3_FP8.name,
+                                                                time.perf_counter() - t0))
+        result["dsv3_fp8"] = measure_other(moe, synth, synth.DSV3_FP8, osteps, args.warmup,
+                                           weights=wq.pop("f32"), scale_fmt="f32")
+        result["dsv3_fp8_ue8m0"] = measure_other(moe, synth, synth.DSV3_FP8, osteps, args.warmup,
+                                                 weights=wq.pop("ue8m0"), scale_fmt="ue8m0",
+                                                 name=synth.DSV3_FP8.name + "_ue8m0")
+        del wq
         torch.cuda.empty_cache()
-        for spec_o, fmt, fp4 in ((synth.SKEWED_128E, "f32", False), (synth.DSV3_FP8, "f32", False),
-                                 (synth.DSV3_FP8, "ue8m0", False), (synth.DSV3_FP8, "ue8m0", True),
-                                 (synth.TINY_F32, "f32", False)):
-            rep.append(measure_other(moe, synth, spec_o, max(args.steps, 5), args.warmup, fmt,
-                                     fp4=fp4))
+    if args.report:
+        if not args.no_others:
+            rep += [result["skewed"], result["dsv3_fp8"], result["dsv3_fp8_ue8m0"]]
+        w4 = lowp_weights(moe, synth, synth.DSV3_FP8, (), fp4=True)
+        rep.append(measure_other(moe, synth, synth.DSV3_FP8, max(args.steps, 5), args.warmup,
+                                 weights=w4.pop("fp4"), scale_fmt="fp4",
+                                 name="dsv3_fp4_T8192_d7168_f2048_E256_k8_mx"))
+        del w4
+        torch.cuda.empty_cache()
+        rep.append(measure_other(moe, synth, synth.TINY_F32, max(args.steps, 5), args.warmup))
         with open(args.report, "w") as fh:
             json.dump({"prefill": {k: result[k] for k in ("value", "ms_per_step", "config",
                                                           "roofline")},

@@ -215,6 +215,8 @@ moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q
  * hidden activation h [P, f] to the workspace (bf16; e4m3 + per-128 scales on the fp8 path).
  * The down projection runs as a second grouped GEMM whose epilogue writes y in a->y_layout.
  * Small batches (P <= 256) use weight-streaming kernels with the weight rows on the MFMA M side.
+ * a->phase selects both projections (MOE_PHASE_ALL) or one of them (see moe_experts_phase); an
+ * unknown value is MOE_ERR_INVALID_ARGUMENT.
  *
  * Supported dtype combinations (act_dtype / w_dtype / y_dtype):
  *    F32 / F32 / F32                 fp32 everywhere
@@ -239,6 +241,16 @@ moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q
  * fp32 scale arrays 4-byte aligned (MOE_ERR_UNSUPPORTED otherwise). Contiguous tensors from a
  * device allocator, and their slices along the expert or token dimension, satisfy this.
  * ------------------------------------------------------------------------------------------ */
+/* Which projections one moe_experts_forward call runs. A MOE_PHASE_GATE_UP call followed, in
+ * stream order, by a MOE_PHASE_DOWN call with the same arguments and the same workspace (whose h
+ * the first call wrote) computes exactly what one MOE_PHASE_ALL call computes; a caller can put
+ * its own work on the stream between the two (e.g. event records to time each projection). */
+typedef enum {
+  MOE_PHASE_ALL = 0,      /* gate/up + SwiGLU, then down */
+  MOE_PHASE_GATE_UP = 1,  /* gate/up + SwiGLU only: h in the workspace */
+  MOE_PHASE_DOWN = 2      /* down only, from the h of a previous MOE_PHASE_GATE_UP call */
+} moe_experts_phase;
+
 typedef struct {
   int T, d, f, E, k;
   moe_dtype act_dtype;           /* dtype of x */
@@ -259,9 +271,8 @@ typedef struct {
   void* y;                       /* output, see moe_y_layout */
   void* workspace;               /* >= moe_experts_workspace_size(...) bytes */
   size_t workspace_bytes;
-  void** events;                 /* nullable: 4 hipEvent_t recorded on `stream` before/after the
-                                    gate/up GEMM and before/after the down GEMM (for timing) */
   moe_scale_fmt scale_fmt;       /* FP8 block-scale format (MOE_SCALE_F32 elsewhere) */
+  moe_experts_phase phase;       /* which projection(s) this call runs (MOE_PHASE_ALL = both) */
 } moe_experts_args;
 
 moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream);
@@ -336,15 +347,6 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream);
 /* Bytes of workspace moe_fused_forward needs (0 for unsupported sizes). */
 size_t moe_fused_workspace_size(int T, int d, int f, int E, int k, moe_dtype w_dtype,
                                 moe_dtype out_dtype);
-
-/* ------------------------------------------------------------------------------------------
- * Timing helpers (thin wrappers over HIP events, for callers without their own HIP bindings).
- * ------------------------------------------------------------------------------------------ */
-moe_status moe_event_create(void** event);
-moe_status moe_event_destroy(void* event);
-moe_status moe_event_record(void* event, hipStream_t stream);
-/* Waits for `stop`, then writes the milliseconds between the two recorded events. */
-moe_status moe_event_elapsed_ms(void* start, void* stop, float* ms);
 
 #ifdef __cplusplus
 }

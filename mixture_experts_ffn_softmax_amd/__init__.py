@@ -33,8 +33,6 @@ EXPORTED_SYMBOLS = (
     "fp8_quantize_weight_ue8m0", "fp4_quantize_weight_mx", "fp4_tile_weight",
     "moe_experts_forward",
     "moe_experts_workspace_size", "moe_combine", "moe_fused_forward", "moe_fused_workspace_size",
-    "moe_event_create", "moe_event_destroy",
-    "moe_event_record", "moe_event_elapsed_ms",
 )
 
 
@@ -54,8 +52,7 @@ class moe_experts_args(ctypes.Structure):
         ("offsets", ctypes.c_void_p), ("sorted_pair", ctypes.c_void_p),
         ("topk_w", ctypes.c_void_p), ("y", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-        ("events", ctypes.c_void_p),
-        ("scale_fmt", ctypes.c_int),
+        ("scale_fmt", ctypes.c_int), ("phase", ctypes.c_int),
     ]
 
 
@@ -76,6 +73,8 @@ class moe_fused_args(ctypes.Structure):
 
 _SCALE_FMTS = {"f32": 0, "ue8m0": 1}   # moe_scale_fmt
 MOE_SCALE_F32, MOE_SCALE_UE8M0 = 0, 1
+MOE_PHASE_ALL, MOE_PHASE_GATE_UP, MOE_PHASE_DOWN = 0, 1, 2
+_PHASES = {"all": MOE_PHASE_ALL, "gate_up": MOE_PHASE_GATE_UP, "down": MOE_PHASE_DOWN}
 
 
 _lib = None
@@ -109,10 +108,6 @@ def load_library(path: str = LIB_PATH):
         "moe_combine": ([vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp], st),
         "moe_fused_forward": ([ctypes.POINTER(moe_fused_args), vp], st),
         "moe_fused_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
-        "moe_event_create": ([ctypes.POINTER(ctypes.c_void_p)], st),
-        "moe_event_destroy": ([vp], st),
-        "moe_event_record": ([vp, vp], st),
-        "moe_event_elapsed_ms": ([vp, vp, ctypes.POINTER(ctypes.c_float)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -299,10 +294,11 @@ def experts_workspace_bytes(T, d, f, E, k, act_dtype: int, w_dtype: int) -> int:
 
 def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k: int,
                         y_layout: str = "slots", y_dtype=None, x_scales=None, s_gate=None,
-                        s_up=None, s_down=None, y=None, workspace=None, events=None,
+                        s_up=None, s_down=None, y=None, workspace=None, phase: str = "all",
                         scale_fmt: str = "f32", w_fp4: bool = False):
     """Both grouped projections. Returns y in ``y_layout`` ("permuted" [P,d], "slots" [T,k,d],
-    "acc_f32" [T,d] fp32). ``events``: optional 4 event handles (see moe_event_create).
+    "acc_f32" [T,d] fp32). ``phase``: "all", or "gate_up" then "down" as two calls on one
+    ``workspace`` (pass the same workspace and y to both).
     ``scale_fmt``: fp8 block scales as fp32 values ("f32") or e8m0 bytes ("ue8m0").
     ``w_fp4``: the uint8 weights are packed E2M1 in matrix-fragment order (fp4_quantize_weight_mx
     with tiled=True) with MX scales."""
@@ -330,9 +326,6 @@ def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k
     nbytes = lib.moe_experts_workspace_size(T, d, f, E, k, act, wdt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    ev = None
-    if events is not None:
-        ev = (ctypes.c_void_p * 4)(*events)
     a = moe_experts_args(T, d, f, E, k, act, wdt, _dtype_code(y), layout, x.data_ptr(),
                          x_scales.data_ptr() if x_scales is not None else None,
                          w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(),
@@ -341,9 +334,8 @@ def moe_experts_forward(x, w_gate, w_up, w_down, offsets, sorted_pair, topk_w, k
                          s_down.data_ptr() if s_down is not None else None,
                          offsets.data_ptr(), sorted_pair.data_ptr(),
                          topk_w.data_ptr() if topk_w is not None else None, y.data_ptr(),
-                         workspace.data_ptr(), workspace.numel(),
-                         ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None,
-                         _SCALE_FMTS[scale_fmt])
+                         workspace.data_ptr(), workspace.numel(), _SCALE_FMTS[scale_fmt],
+                         _PHASES[phase])
     _check(lib.moe_experts_forward(ctypes.byref(a), _stream()))
     return y
 
@@ -359,8 +351,6 @@ def moe_combine(y, layout: str, T: int, k: int, d: int, pair_pos=None, topk_w=No
                            _ptr(topk_w), T, k, d, _ptr(out), _dtype_code(out), _stream()))
     return out
 
-
-# ---- events ----------------------------------------------------------------------------------
 
 def moe_fused_forward(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, s_gate=None,
                       s_up=None, s_down=None, w_fp4: bool = False, out_dtype=None,
@@ -398,26 +388,6 @@ def moe_fused_forward(x, w_gate, w_up, w_down, k: int, logits=None, w_router=Non
     return out, ids, w
 
 
-def event_create():
-    h = ctypes.c_void_p()
-    _check(load_library().moe_event_create(ctypes.byref(h)))
-    return h.value
-
-
-def event_destroy(h):
-    _check(load_library().moe_event_destroy(h))
-
-
-def event_record(h):
-    _check(load_library().moe_event_record(h, _stream()))
-
-
-def event_elapsed_ms(a, b) -> float:
-    ms = ctypes.c_float()
-    _check(load_library().moe_event_elapsed_ms(a, b, ctypes.byref(ms)))
-    return ms.value
-
-
 # ---- the whole layer ------------------------------------------------------------------------
 
 @dataclass
@@ -430,7 +400,7 @@ class LayerResult:
 
 
 def moe_layer(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, y_layout="slots",
-              s_gate=None, s_up=None, s_down=None, out_dtype=None, events=None,
+              s_gate=None, s_up=None, s_down=None, out_dtype=None,
               w_fp4: bool = False) -> LayerResult:
     """route -> permute -> (fp8: quantise x) -> experts -> combine, all on the device.
 
@@ -451,7 +421,7 @@ def moe_layer(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, y_lay
         x_in, xs = fp8_quantize_act(x, scale_fmt=fmt)
     y = moe_experts_forward(x_in, w_gate, w_up, w_down, perm.offsets, perm.sorted_pair, w, k,
                             y_layout=y_layout, x_scales=xs, s_gate=s_gate, s_up=s_up,
-                            s_down=s_down, events=events,
+                            s_down=s_down,
                             y_dtype=torch.float32 if out_dtype == torch.float32 else None,
                             scale_fmt=fmt, w_fp4=w_fp4)
     out = moe_combine(y, y_layout, T, k, d, pair_pos=perm.pair_pos, topk_w=w,

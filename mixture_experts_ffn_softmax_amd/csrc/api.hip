@@ -283,6 +283,10 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   if (a->y_layout != MOE_Y_PERMUTED && a->y_layout != MOE_Y_SLOTS && a->y_layout != MOE_Y_ACC_F32)
     return MOE_ERR_INVALID_ARGUMENT;
   if (a->y_layout != MOE_Y_PERMUTED && !a->topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (a->phase != MOE_PHASE_ALL && a->phase != MOE_PHASE_GATE_UP && a->phase != MOE_PHASE_DOWN)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const bool run_gate_up = a->phase != MOE_PHASE_DOWN;
+  const bool run_down = a->phase != MOE_PHASE_GATE_UP;
   if (!is_float_type(a->y_dtype)) return MOE_ERR_INVALID_ARGUMENT;
   const moe_dtype act = a->act_dtype, w = a->w_dtype;
   const bool f32 = act == MOE_F32 && w == MOE_F32;
@@ -356,7 +360,8 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   X.cpx = cus_per_xcd();
   const bool split = uses_split(act, w, P, a->d, a->f);
   X.split_partial = split ? reinterpret_cast<float*>(ws + L.split_partial) : nullptr;
-  X.ev = a->events;
+  X.run_gate_up = run_gate_up ? 1 : 0;
+  X.run_down = run_down ? 1 : 0;
 
   const bool decode = uses_decode(act, w, P, a->d, a->f);
   int bm_a, bm_b;
@@ -367,19 +372,21 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   else { bm_a = bf16_tile_rows_gateup(); bm_b = bf16_tile_rows_down(); }
 
   hipError_t e = hipSuccess;
-  if (!decode && !fp8_decode) {  // decode kernels map (expert, row panel) directly: no tile table
+  // the gate/up phase writes the tile tables of both GEMMs (a down-only call reads them from the
+  // workspace, as it reads h)
+  if (run_gate_up && !decode && !fp8_decode) {  // decode kernels map (expert, row panel) directly
     e = launch_tile_table(a->offsets, a->E, bm_a, bm_b, const_cast<int32_t*>(X.tile_cum_a),
                           const_cast<int32_t*>(X.tile_cum_b), stream);
     if (e != hipSuccess) return MOE_ERR_DEVICE;
   }
-  if (a->y_layout == MOE_Y_ACC_F32) {
+  if (run_down && a->y_layout == MOE_Y_ACC_F32) {
     const size_t n = static_cast<size_t>(a->T) * a->d;
     hipLaunchKernelGGL(zero_f32_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 65536))),
                        dim3(256), 0, stream, static_cast<float*>(a->y), n);
     if ((e = hipGetLastError()) != hipSuccess) return MOE_ERR_DEVICE;
   }
   if (ue8m0) X.a_scale_bytes = a->x_scales;   // the small-batch kernels read the bytes
-  if (ue8m0 && !fp8_decode) {
+  if (run_gate_up && ue8m0 && !fp8_decode) {
     // the tiled GEMMs read activation scales as fp32 values; e8m0 bytes expand exactly
     float* xs = reinterpret_cast<float*>(ws + L.x_scales);
     e = launch_e8m0_expand(static_cast<const uint8_t*>(a->x_scales),
@@ -514,6 +521,7 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   X.h_scale_bytes = lowp ? reinterpret_cast<uint8_t*>(ws + L.hs) : nullptr;
   X.pair_ids = a->topk_ids;
   X.cpx = cus_per_xcd();
+  X.run_gate_up = X.run_down = 1;
   e = lowp ? launch_experts_fp8_decode(X, stream) : launch_experts_bf16_decode(X, stream);
   if (e == hipErrorNotSupported) return MOE_ERR_UNSUPPORTED;
   if (e != hipSuccess) return MOE_ERR_DEVICE;
@@ -533,30 +541,6 @@ moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
   if (layout == MOE_Y_PERMUTED && (!pair_pos || !topk_w)) return MOE_ERR_INVALID_ARGUMENT;
   if (static_cast<long long>(T) * k * d > (1ll << 40)) return MOE_ERR_UNSUPPORTED;
   return dev(launch_combine(y, y_dtype, layout, pair_pos, topk_w, T, k, d, out, out_dtype, stream));
-}
-
-moe_status moe_event_create(void** event) {
-  if (!event) return MOE_ERR_INVALID_ARGUMENT;
-  hipEvent_t ev;
-  if (hipEventCreate(&ev) != hipSuccess) return MOE_ERR_DEVICE;
-  *event = ev;
-  return MOE_OK;
-}
-
-moe_status moe_event_destroy(void* event) {
-  if (!event) return MOE_ERR_INVALID_ARGUMENT;
-  return dev(hipEventDestroy(static_cast<hipEvent_t>(event)));
-}
-
-moe_status moe_event_record(void* event, hipStream_t stream) {
-  if (!event) return MOE_ERR_INVALID_ARGUMENT;
-  return dev(hipEventRecord(static_cast<hipEvent_t>(event), stream));
-}
-
-moe_status moe_event_elapsed_ms(void* start, void* stop, float* ms) {
-  if (!start || !stop || !ms) return MOE_ERR_INVALID_ARGUMENT;
-  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return MOE_ERR_DEVICE;
-  return dev(hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)));
 }
 
 }  // extern "C"

@@ -366,19 +366,21 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   const bool stream_small = L.d % kStrK == 0;
   g.small_max = stream_small ? 16 : 0;
   const unsigned grid1s = static_cast<unsigned>(L.E) * ((L.f + 7) / 8);
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  if (stream_small) {
+  if (L.run_gate_up && stream_small) {
     if (fused)
       hipLaunchKernelGGL((decode_stream_kernel<kStrK, true>), dim3(grid1s), dim3(64), 0, stream, g);
     else
       hipLaunchKernelGGL((decode_stream_kernel<kStrK, false>), dim3(grid1s), dim3(64), 0, stream,
                          g);
   }
-  if (fused)
-    hipLaunchKernelGGL((decode_bf16_kernel<kGateUp, true>), dim3(grid1), dim3(256), 0, stream, g);
-  else
-    hipLaunchKernelGGL((decode_bf16_kernel<kGateUp, false>), dim3(grid1), dim3(256), 0, stream, g);
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+  if (L.run_gate_up) {
+    if (fused)
+      hipLaunchKernelGGL((decode_bf16_kernel<kGateUp, true>), dim3(grid1), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((decode_bf16_kernel<kGateUp, false>), dim3(grid1), dim3(256), 0, stream,
+                         g);
+  }
+  if (!L.run_down) return hipGetLastError();
 
   DecodeArgs dn{};
   dn.a = static_cast<const uint16_t*>(L.h);
@@ -397,12 +399,10 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   dn.small_max = 0;  // the K-split kernel takes every expert of the down GEMM
   dn.ids = L.pair_ids;
   dn.P = P;
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
   if (fused)
     hipLaunchKernelGGL((decode_bf16_kernel<kDown, true>), dim3(grid2), dim3(256), 0, stream, dn);
   else
     hipLaunchKernelGGL((decode_bf16_kernel<kDown, false>), dim3(grid2), dim3(256), 0, stream, dn);
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return hipGetLastError();
 }
 

@@ -362,15 +362,16 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   uint8_t* hq = static_cast<uint8_t*>(L.h);
   g.ids = L.pair_ids;
   g.P = P;
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipError_t e = launch_mode<kGateUp>(g, L.E, P, ue, w4, fused, stream);
-  if (e != hipSuccess) return e;
   // h -> e4m3 codes with per-(pair, 128-channel) scales: e8m0 bytes or fp32, as the down kernel
   // reads them (rows in h's own order: sorted, or by pair on the fused path)
   void* hs = ue ? static_cast<void*>(L.h_scale_bytes) : static_cast<void*>(L.h_scales);
-  e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, hs, ue, stream);
-  if (e != hipSuccess) return e;
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+  if (L.run_gate_up) {
+    hipError_t e = launch_mode<kGateUp>(g, L.E, P, ue, w4, fused, stream);
+    if (e != hipSuccess) return e;
+    e = launch_quantize_act(L.h32, MOE_F32, P, L.f, nullptr, hq, hs, ue, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (!L.run_down) return hipSuccess;
 
   Fp8DecodeArgs dn{};
   dn.a = hq;
@@ -389,10 +390,7 @@ hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream)
   dn.topk_w = L.topk_w;
   dn.ids = L.pair_ids;
   dn.P = P;
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  e = launch_mode<kDown>(dn, L.E, P, ue, w4, fused, stream);
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
-  return e;
+  return launch_mode<kDown>(dn, L.E, P, ue, w4, fused, stream);
 }
 
 }  // namespace moe

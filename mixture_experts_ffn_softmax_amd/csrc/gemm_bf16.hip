@@ -621,12 +621,12 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   g.max_split =
       L.split_partial && may_cut(P, (L.f + 127) / 128, L.cpx) ? max_split_for(L.d) : 1;
   g.partial = L.split_partial;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipError_t e =
-      launch_gemm<kGateUp, MOE_BF16_WAVES>(g, work_grid(max_tiles(P, L.E, (L.f + 127) / 128), L.cpx),
-                                           stream);
-  if (e != hipSuccess) return e;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+  if (L.run_gate_up) {
+    const hipError_t e = launch_gemm<kGateUp, MOE_BF16_WAVES>(
+        g, work_grid(max_tiles(P, L.E, (L.f + 127) / 128), L.cpx), stream);
+    if (e != hipSuccess) return e;
+  }
+  if (!L.run_down) return hipSuccess;
 
   Bf16GemmArgs dn{};
   dn.a = static_cast<const uint16_t*>(L.h);
@@ -648,11 +648,8 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   dn.max_split =
       L.split_partial && may_cut(P, (L.d + kBN - 1) / kBN, L.cpx) ? max_split_for(L.f) : 1;
   dn.partial = L.split_partial;
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  e = launch_gemm<kDown, MOE_BF16_WAVES>(dn, work_grid(max_tiles(P, L.E, (L.d + kBN - 1) / kBN), L.cpx),
-                                         stream);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
-  return e;
+  return launch_gemm<kDown, MOE_BF16_WAVES>(
+      dn, work_grid(max_tiles(P, L.E, (L.d + kBN - 1) / kBN), L.cpx), stream);
 }
 
 }  // namespace moe

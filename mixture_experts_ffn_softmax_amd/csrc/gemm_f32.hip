@@ -206,17 +206,15 @@ hipError_t launch_experts_f32(const ExpertsLaunch& L, hipStream_t stream) {
   const int NT1 = (L.f + kF32BN1 - 1) / kF32BN1;
   const int NT2 = (L.d + kF32BN2 - 1) / kF32BN2;
   float* h = static_cast<float*>(L.h);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  hipLaunchKernelGGL(gateup_f32_kernel, dim3(grid_for(P, L.E, kF32BM, NT1)), dim3(256), 0, stream,
+  if (L.run_gate_up)
+    hipLaunchKernelGGL(gateup_f32_kernel, dim3(grid_for(P, L.E, kF32BM, NT1)), dim3(256), 0, stream,
                      static_cast<const float*>(L.a), L.a_gather, L.sorted_pair, L.k,
                      static_cast<const float*>(L.w_gate), static_cast<const float*>(L.w_up), L.d,
                      L.f, L.offsets, L.tile_cum_a, L.E, h);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
-  hipLaunchKernelGGL(down_f32_kernel, dim3(grid_for(P, L.E, kF32BM, NT2)), dim3(256), 0, stream, h,
+  if (L.run_down)
+    hipLaunchKernelGGL(down_f32_kernel, dim3(grid_for(P, L.E, kF32BM, NT2)), dim3(256), 0, stream, h,
                      static_cast<const float*>(L.w_down), L.d, L.f, L.offsets, L.tile_cum_b, L.E,
                      L.sorted_pair, L.topk_w, L.k, L.y_layout, static_cast<float*>(L.y));
-  if (L.ev) hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return hipGetLastError();
 }
 

@@ -453,16 +453,18 @@ hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream) {
   const bool w4 = L.w_fp4 != 0;
   if (w4 && !L.scale_ue8m0) return hipErrorNotSupported;   // MX scales are e8m0 bytes
   const dim3 grid1(grid_for(P, L.E, L.f / 128));
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[0]), stream);
-  if (w4)
-    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true, true>), grid1, dim3(512), 0, stream, g);
-  else if (L.scale_ue8m0)
-    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true, false>), grid1, dim3(512), 0, stream, g);
-  else
-    hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, false, false>), grid1, dim3(512), 0, stream, g);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[1]), stream);
+  if (L.run_gate_up) {
+    if (w4)
+      hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true, true>), grid1, dim3(512), 0, stream, g);
+    else if (L.scale_ue8m0)
+      hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, true, false>), grid1, dim3(512), 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp, false, false>), grid1, dim3(512), 0, stream,
+                         g);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!L.run_down) return hipSuccess;
 
   Fp8GemmArgs dn{};
   dn.a = static_cast<const uint8_t*>(L.h);
@@ -483,14 +485,12 @@ hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream) {
   dn.y_bf16 = L.y_bf16;
   dn.topk_w = L.topk_w;
   const dim3 grid2(grid_for(P, L.E, (L.d + kBNf - 1) / kBNf));
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[2]), stream);
   if (w4)
     hipLaunchKernelGGL((gemm_fp8_kernel<kDown, true, true>), grid2, dim3(512), 0, stream, dn);
   else if (L.scale_ue8m0)
     hipLaunchKernelGGL((gemm_fp8_kernel<kDown, true, false>), grid2, dim3(512), 0, stream, dn);
   else
     hipLaunchKernelGGL((gemm_fp8_kernel<kDown, false, false>), grid2, dim3(512), 0, stream, dn);
-  if (L.ev) (void)hipEventRecord(static_cast<hipEvent_t>(L.ev[3]), stream);
   return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ struct ExpertsLaunch {
   int cpx;                    // CUs per XCD (<= kSplitSlots / 8)
   float* split_partial;       // bf16 GEMMs: [kSplitSlots][256 * 256] fp32, or null (no cutting;
                               // the two GEMMs use it one after the other)
-  void** ev;                  // nullable timing events (4)
+  int run_gate_up, run_down;  // which projections this call enqueues (the other one is skipped)
   // fp8 small-batch kernels with UE8M0 scales read the activation scales as e8m0 bytes:
   // a_scale_bytes [T, d/128] (or [P, d/128]) for x, h_scale_bytes for h
   const void* a_scale_bytes;

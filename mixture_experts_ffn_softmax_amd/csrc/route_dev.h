@@ -117,12 +117,15 @@ __device__ __forceinline__ void topk_select(const float* row, bool tok_ok, int E
       if (gl + G * q == bi) taken |= 1ull << q;
     if (gl == j) { my_v = bv; my_i = bi; }
   }
-  float a = (gl < k) ? expf(my_v - vmax) : 0.0f;
-  float s = a;
+  // The k weights in double, rounded once to fp32: the result is the correctly rounded value of
+  // exp(l_j - l_max) / sum exp(l - l_max) except within ~1e-16 of a rounding boundary, so it does
+  // not depend on the order of the sum (k exponentials per token: negligible work).
+  const double a = (gl < k) ? exp(static_cast<double>(my_v) - static_cast<double>(vmax)) : 0.0;
+  double s = a;
   for (int o = G >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
   if (tok_ok && gl < k) {
     ids[gl] = my_i;
-    w[gl] = a / s;
+    w[gl] = static_cast<float>(a / s);
   }
 }
 

@@ -69,10 +69,14 @@ def _load():
         lib.oracle_moe_forward.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp,
                                            vp, i32, i32, vp, vp, i32, vp, vp]
         lib.oracle_combine_permuted.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+        lib.oracle_router_logits_f32.argtypes = [vp, i32, vp, i32, i32, i32, vp]
+        lib.oracle_moe_forward_f32.argtypes = [i32, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp,
+                                               vp, i32, vp, vp]
         for fn in ("oracle_quantize_act", "oracle_quantize_weight", "oracle_quantize_act_ue8m0",
                    "oracle_quantize_weight_ue8m0", "oracle_router_logits",
                    "oracle_route", "oracle_permute", "oracle_expert_pairs", "oracle_moe_forward",
-                   "oracle_combine_permuted"):
+                   "oracle_combine_permuted", "oracle_router_logits_f32",
+                   "oracle_moe_forward_f32"):
             getattr(lib, fn).restype = None
         _lib = lib
     return _lib
@@ -314,6 +318,38 @@ def moe_forward(x: np.ndarray, experts: Experts, ids: np.ndarray, w: np.ndarray,
     _load().oracle_moe_forward(T, d, experts.f, k, _dtype_code(x), x.ctypes.data,
                                *experts._wargs(), ids.ctypes.data, w.ctypes.data, n_tok, _ptr(tl),
                                out.ctypes.data)
+    return out
+
+
+def router_logits_f32(x: np.ndarray, Wr: np.ndarray) -> np.ndarray:
+    """router_logits with the sum in fp32 (ascending i) instead of fp64."""
+    x = _c(x)
+    Wr = _c(Wr, np.float32)
+    T, d = x.shape
+    E = Wr.shape[0]
+    out = np.empty((T, E), np.float32)
+    _load().oracle_router_logits_f32(x.ctypes.data, _dtype_code(x), Wr.ctypes.data, T, d, E,
+                                     out.ctypes.data)
+    return out
+
+
+def moe_forward_f32(x: np.ndarray, experts: Experts, ids: np.ndarray, w: np.ndarray,
+                    tokens=None) -> np.ndarray:
+    """moe_forward with every sum in fp32 (fp32 or bf16 inputs and weights only): the plain fp32
+    per-token loop. Returns float32 [n_tok, d]."""
+    assert experts.w_dtype in (F32, BF16) and not experts.quant_act
+    x = _c(x)
+    ids = _c(ids, np.int32)
+    w = _c(w, np.float32)
+    T, d = x.shape
+    k = ids.shape[1]
+    tl = None if tokens is None else _c(np.asarray(tokens), np.int32)
+    n_tok = T if tl is None else tl.size
+    out = np.empty((n_tok, d), np.float32)
+    _load().oracle_moe_forward_f32(T, d, experts.f, k, _dtype_code(x), x.ctypes.data,
+                                   experts.w_dtype, _ptr(experts.w_gate), _ptr(experts.w_up),
+                                   _ptr(experts.w_down), ids.ctypes.data, w.ctypes.data, n_tok,
+                                   _ptr(tl), out.ctypes.data)
     return out
 
 

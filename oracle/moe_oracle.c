@@ -517,3 +517,72 @@ void oracle_combine_permuted(const double* y, const int32_t* pair_pos, const flo
       out[(size_t)t * d + i] = acc;
     }
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * The same per-token loop with every sum in fp32 (float), for fp32 or bf16 inputs. The layer's
+ * stated oracle is a plain fp32 loop; the fp64 functions above compute the same sums with a
+ * smaller rounding error and are the reference the GPU is compared with. These two functions
+ * exist so that a test can show the two precisions agree far inside the layer tolerance.
+ * ------------------------------------------------------------------------------------------- */
+
+/* logits[t][e] = sum_i x[t][i] * Wr[e][i], summed in fp32 in ascending i (fma-free: each product
+ * is rounded to fp32, then added). */
+void oracle_router_logits_f32(const void* x, int x_dtype, const float* Wr, int T, int d, int E,
+                              float* logits) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      float acc = 0.0f;
+      for (int i = 0; i < d; ++i) {
+        volatile float prod = (float)load_value(x, x_dtype, (size_t)t * d + i) * Wr[(size_t)e * d + i];
+        acc += prod;
+      }
+      logits[(size_t)t * E + e] = acc;
+    }
+}
+
+/* out[t] = sum_{j<k} w[t][j] * expert_{ids[t][j]}(x[t]) with the expert evaluated in fp32:
+ * g, u summed in ascending i, h = g / (1 + expf(-g)) * u, y summed in ascending n, then the
+ * weighted sum over j = 0..k-1 in fp32. Weights fp32 or bf16 (dtype codes as above). */
+void oracle_moe_forward_f32(int T, int d, int f, int k, int x_dtype, const void* x, int w_dtype,
+                            const void* w_gate, const void* w_up, const void* w_down,
+                            const int32_t* ids, const float* topk_w, int n_tok,
+                            const int32_t* tok_list, float* out) {
+  if (!tok_list) n_tok = T;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int n = 0; n < n_tok; ++n) {
+    int t = tok_list ? tok_list[n] : n;
+    float* xr = (float*)malloc(sizeof(float) * (size_t)d);
+    float* h = (float*)malloc(sizeof(float) * (size_t)f);
+    float* o = out + (size_t)n * d;
+    for (int i = 0; i < d; ++i) {
+      xr[i] = (float)load_value(x, x_dtype, (size_t)t * d + i);
+      o[i] = 0.0f;
+    }
+    for (int j = 0; j < k; ++j) {
+      int e = ids[(size_t)t * k + j];
+      for (int r = 0; r < f; ++r) {
+        float g = 0.0f, u = 0.0f;
+        for (int i = 0; i < d; ++i) {
+          size_t wi = ((size_t)e * f + r) * d + i;
+          volatile float pg = xr[i] * (float)load_value(w_gate, w_dtype, wi);
+          volatile float pu = xr[i] * (float)load_value(w_up, w_dtype, wi);
+          g += pg;
+          u += pu;
+        }
+        h[r] = g / (1.0f + expf(-g)) * u;
+      }
+      float wj = topk_w[(size_t)t * k + j];
+      for (int c = 0; c < d; ++c) {
+        float acc = 0.0f;
+        for (int r = 0; r < f; ++r) {
+          volatile float p = h[r] * (float)load_value(w_down, w_dtype, ((size_t)e * d + c) * f + r);
+          acc += p;
+        }
+        o[c] += wj * acc;
+      }
+    }
+    free(xr);
+    free(h);
+  }
+}

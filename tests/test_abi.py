@@ -139,7 +139,7 @@ def _args(**kw):
                 y_dtype=moe.MOE_BF16, y_layout=moe.MOE_Y_SLOTS, x=0x1000, x_scales=None,
                 w_gate=0x1000, w_up=0x1000, w_down=0x1000, s_gate=None, s_up=None, s_down=None,
                 offsets=0x1000, sorted_pair=0x1000, topk_w=0x1000, y=0x1000, workspace=0x1000,
-                workspace_bytes=1 << 40, events=None, scale_fmt=moe.MOE_SCALE_F32)
+                workspace_bytes=1 << 40, scale_fmt=moe.MOE_SCALE_F32, phase=moe.MOE_PHASE_ALL)
     base.update(kw)
     return moe.moe_experts_args(**base)
 
@@ -241,7 +241,6 @@ def test_combine_validation(lib):
                            None) == INV
 
 
-def test_event_helpers_validate(lib):
-    assert lib.moe_event_create(None) == moe.MOE_ERR_INVALID_ARGUMENT
-    assert lib.moe_event_destroy(None) == moe.MOE_ERR_INVALID_ARGUMENT
-    assert lib.moe_event_elapsed_ms(None, None, None) == moe.MOE_ERR_INVALID_ARGUMENT
+def test_experts_phase_validation(lib):
+    assert _fwd(lib, phase=3) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert _fwd(lib, phase=-1) == moe.MOE_ERR_INVALID_ARGUMENT

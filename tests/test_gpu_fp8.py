@@ -16,7 +16,8 @@ import torch
 import mixture_experts_ffn_softmax_amd as moe
 import oracle
 import synth
-from gpu_util import assert_close_rel_max, log, out_to_f64, to_dev, to_host
+from gpu_util import (assert_close_rel_max, check_edge_rows_permuted, log, out_to_f64, to_dev,
+                      to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -143,7 +144,8 @@ def test_dsv3_fp8_full_sampled(fmt):
     ids_ref, w_ref = oracle.route(logits, k)
     rng = np.random.default_rng(2)
     tokens = np.sort(rng.choice(T, 12, replace=False))
-    need = sorted(set(ids_ref[tokens].reshape(-1).tolist()))
+    cnt = np.bincount(ids_ref.reshape(-1), minlength=E)
+    need = sorted(set(ids_ref[tokens].reshape(-1).tolist()) | {int(cnt.argmax()), int(cnt.argmin())})
     remap = {e: i for i, e in enumerate(need)}
     # quantise expert by expert on the GPU; keep the oracle's own quantisation of the experts the
     # sampled tokens use, and check those bit-exactly against the GPU's
@@ -183,6 +185,11 @@ def test_dsv3_fp8_full_sampled(fmt):
     ids_sub = np.vectorize(remap.get)(ids_ref[tokens]).astype(np.int32)
     ref = oracle.moe_forward(x[tokens], ex, ids_sub, w_ref[tokens])
     assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, fmt))
+    # the edge rows of the 128-row tiles of every expert the oracle holds, per pair
+    n = check_edge_rows_permuted(spec, x, logits, [dev_q[w] for w in ("gate", "up", "down")],
+                                 [dev_s[w] for w in ("gate", "up", "down")], ex, remap, (128,),
+                                 6e-2, "%s %s" % (spec.name, fmt), scale_fmt=fmt)
+    assert n >= 4 * len(need)
 
 
 # ---- small batches: the weight-streaming fp8 kernels (P <= 256 pairs) ------------------------

@@ -14,7 +14,7 @@ import torch
 import mixture_experts_ffn_softmax_amd as moe
 import oracle
 import synth
-from gpu_util import assert_close_rel_max, log, out_to_f64, to_dev, to_host
+from gpu_util import assert_close_rel_max, check_routing, log, out_to_f64, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -107,13 +107,18 @@ def test_fused_matches_unfused_and_oracle(fmt, spec):
                                     logits_out=lg_out)
         torch.cuda.synchronize()
         _check_same(got, ref_seq, "%s %s call %d" % (spec.name, fmt, call))
-    # against the oracle (routing on the device's logits when the router GEMM ran there)
+    # against the oracle's own routing (its own logits when the router GEMM ran on the device)
+    inp = {"x": synth.gen_x(spec)}
     if wr is not None:
-        lg_np = to_host(lg_out)
-    ids_ref, w_ref = oracle.route(lg_np, spec.k)
-    np.testing.assert_array_equal(to_host(got[1]), ids_ref)
-    ref = oracle.moe_forward(synth.gen_x(spec), ex, ids_ref, w_ref)
-    assert_close_rel_max(out_to_f64(got[0]), ref, 2e-2 if fmt == "bf16" else 6e-2,
+        inp["Wr"] = wr_np
+    else:
+        inp["logits"] = lg_np
+    ids_ref, w_ref, keep = check_routing(spec, inp, to_host(got[1]), to_host(got[2]),
+                                         to_host(lg_out) if wr is not None else None,
+                                         "%s %s" % (spec.name, fmt))
+    toks = np.flatnonzero(keep)
+    ref = oracle.moe_forward(inp["x"], ex, ids_ref, w_ref, tokens=toks)
+    assert_close_rel_max(out_to_f64(got[0])[toks], ref, 2e-2 if fmt == "bf16" else 6e-2,
                          "%s %s vs oracle" % (spec.name, fmt))
 
 
