@@ -348,6 +348,29 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream);
 size_t moe_fused_workspace_size(int T, int d, int f, int E, int k, moe_dtype w_dtype,
                                 moe_dtype out_dtype);
 
+/* ------------------------------------------------------------------------------------------
+ * moe_fused_forward_noalloc - moe_fused_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Computes exactly what moe_fused_forward computes (same kernels, bit-identical outputs), but
+ * instead of a caller's workspace it uses a fixed device array inside the library, one per GPU,
+ * of MOE_NOALLOC_SCRATCH_BYTES bytes, which the GPU holds until the process ends; a->workspace
+ * and a->workspace_bytes are ignored. The call allocates and frees nothing. The caller still
+ * passes x, the weights and the outputs.
+ *  - Limit: moe_fused_workspace_size(...) of the call must be <= MOE_NOALLOC_SCRATCH_BYTES
+ *    (e.g. the Mixtral-shaped decode layer, d = 4096, f = 14336, with bf16, e4m3 or FP4 experts at
+ *    every batch the fused path takes, T*k <= 256); larger requests return MOE_ERR_UNSUPPORTED
+ *    and enqueue nothing. Other errors as moe_fused_forward.
+ *  - The first call on a device looks up that device's array (the device current at the call,
+ *    which must be the stream's device); a failed lookup returns MOE_ERR_DEVICE.
+ *  - Every call on one GPU shares that GPU's array and leaves its contents behind; nothing in the
+ *    fused path reads the array before writing it. Calls that overlap on one GPU (different
+ *    streams or host threads without ordering between them) race on the array: order them.
+ * ------------------------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+moe_status moe_fused_forward_noalloc(const moe_fused_args* a, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

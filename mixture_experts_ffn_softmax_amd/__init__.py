@@ -33,7 +33,9 @@ EXPORTED_SYMBOLS = (
     "fp8_quantize_weight_ue8m0", "fp4_quantize_weight_mx", "fp4_tile_weight",
     "moe_experts_forward",
     "moe_experts_workspace_size", "moe_combine", "moe_fused_forward", "moe_fused_workspace_size",
+    "moe_fused_forward_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -108,6 +110,7 @@ def load_library(path: str = LIB_PATH):
         "moe_combine": ([vp, i32, i32, vp, vp, i32, i32, i32, vp, i32, vp], st),
         "moe_fused_forward": ([ctypes.POINTER(moe_fused_args), vp], st),
         "moe_fused_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
+        "moe_fused_forward_noalloc": ([ctypes.POINTER(moe_fused_args), vp], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -354,10 +357,14 @@ def moe_combine(y, layout: str, T: int, k: int, d: int, pair_pos=None, topk_w=No
 
 def moe_fused_forward(x, w_gate, w_up, w_down, k: int, logits=None, w_router=None, s_gate=None,
                       s_up=None, s_down=None, w_fp4: bool = False, out_dtype=None,
-                      workspace=None, out=None, logits_out=None):
+                      workspace=None, out=None, logits_out=None, noalloc: bool = False,
+                      topk_ids=None, topk_w=None):
     """The whole layer for small batches (T*k <= 256) in one call (moe_fused_forward).
     Weights as for moe_layer (bf16; uint8 e4m3 codes with fp32 or uint8 (UE8M0) block scales; with
-    w_fp4, E2M1 codes in fragment order with MX scales). Returns (out [T, d], topk_ids, topk_w)."""
+    w_fp4, E2M1 codes in fragment order with MX scales). Returns (out [T, d], topk_ids, topk_w).
+    ``noalloc``: call moe_fused_forward_noalloc (the library's own device scratch array instead of
+    a workspace); with ``out``, ``topk_ids`` and ``topk_w`` given, nothing is allocated here
+    either."""
     lib = load_library()
     for t in (x, w_gate, w_up, w_down, logits, w_router, s_gate, s_up, s_down):
         _contig(t)
@@ -374,17 +381,21 @@ def moe_fused_forward(x, w_gate, w_up, w_down, k: int, logits=None, w_router=Non
         out_dtype = torch.float32 if x.dtype == torch.float32 else torch.bfloat16
     if out is None:
         out = torch.empty((T, d), dtype=out_dtype, device=x.device)
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
-    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
-    nbytes = lib.moe_fused_workspace_size(T, d, f, E, k, wdt, _dtype_code(out))
-    if workspace is None:
+    ids = topk_ids if topk_ids is not None else \
+        torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = topk_w if topk_w is not None else torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _contig(ids)
+    _contig(w)
+    if not noalloc and workspace is None:
+        nbytes = lib.moe_fused_workspace_size(T, d, f, E, k, wdt, _dtype_code(out))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     p = lambda t: t.data_ptr() if t is not None else None
     a = moe_fused_args(T, d, f, E, k, _dtype_code(x), wdt, _SCALE_FMTS[fmt], p(x), p(logits),
                        p(w_router), p(logits_out), p(w_gate), p(w_up), p(w_down), p(s_gate),
                        p(s_up), p(s_down), p(out), _dtype_code(out), p(ids), p(w),
-                       p(workspace), workspace.numel())
-    _check(lib.moe_fused_forward(ctypes.byref(a), _stream()))
+                       p(workspace), workspace.numel() if workspace is not None else 0)
+    fn = lib.moe_fused_forward_noalloc if noalloc else lib.moe_fused_forward
+    _check(fn(ctypes.byref(a), _stream()))
     return out, ids, w
 
 

@@ -4,6 +4,7 @@
 #include <limits.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -449,7 +450,12 @@ size_t moe_fused_workspace_size(int T, int d, int f, int E, int k, moe_dtype w_d
   return fused_layout(T, d, f, k, w_dtype, out_dtype).total;
 }
 
-moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a fused call (everything but the workspace); on success *L is its layout.
+moe_status fused_validate(const moe_fused_args* a, FusedLayout* L) {
   if (!a) return MOE_ERR_INVALID_ARGUMENT;
   moe_status st = check_topology(a->T, a->E, a->k);
   if (st != MOE_OK) return st;
@@ -481,11 +487,16 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   if (lowp && !ue8m0 && (!aligned(a->s_gate, 4) || !aligned(a->s_up, 4) || !aligned(a->s_down, 4)))
     return MOE_ERR_UNSUPPORTED;
   if (static_cast<long long>(a->f) * a->d > INT_MAX / 4) return MOE_ERR_UNSUPPORTED;
-  const FusedLayout L = fused_layout(a->T, a->d, a->f, a->k, w, a->out_dtype);
-  if (!a->workspace) return MOE_ERR_INVALID_ARGUMENT;
-  if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  *L = fused_layout(a->T, a->d, a->f, a->k, w, a->out_dtype);
+  return MOE_OK;
+}
 
-  char* ws = static_cast<char*>(a->workspace);
+// Enqueues a validated fused call with its workspace at ws (at least L.total bytes).
+moe_status fused_launch(const moe_fused_args* a, const FusedLayout& L, char* ws,
+                        hipStream_t stream) {
+  const moe_dtype w = a->w_dtype;
+  const bool lowp = is_low_precision(w);
+  const bool ue8m0 = a->scale_fmt == MOE_SCALE_UE8M0;
   uint8_t* xq = lowp ? reinterpret_cast<uint8_t*>(ws + L.xq) : nullptr;
   void* xs = lowp ? static_cast<void*>(ws + L.xs) : nullptr;
   hipError_t e = launch_fused_route(a->x, a->x_dtype, a->logits, a->w_router, a->logits_out, a->T,
@@ -527,6 +538,66 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   if (e != hipSuccess) return MOE_ERR_DEVICE;
   return dev(launch_combine(ws + L.slots, a->out_dtype, MOE_Y_SLOTS, nullptr, nullptr, a->T, a->k,
                             a->d, a->out, a->out_dtype, stream));
+}
+
+// ---- the allocation-free variant ----------------------------------------------------------------
+//
+// Device memory of moe_fused_forward_noalloc, used in place of a caller's workspace: a fixed
+// array in the library's device code, one per GPU the library runs on, alive until the process
+// ends. Host code never passes the array's name to a kernel or copy (on the host it is only a
+// stand-in for the symbol); it uses the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::atomic<char*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// This device's scratch address (device = the current one); hipGetSymbolAddress runs once per
+// device, with that device current, under the mutex.
+hipError_t device_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = static_cast<char*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
+  FusedLayout L{};
+  const moe_status st = fused_validate(a, &L);
+  if (st != MOE_OK) return st;
+  if (!a->workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return fused_launch(a, L, static_cast<char*>(a->workspace), stream);
+}
+
+moe_status moe_fused_forward_noalloc(const moe_fused_args* a, hipStream_t stream) {
+  FusedLayout L{};
+  const moe_status st = fused_validate(a, &L);
+  if (st != MOE_OK) return st;
+  if (L.total > kScratchBytes) return MOE_ERR_UNSUPPORTED;   // beyond the fixed scratch array
+  char* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess) return MOE_ERR_DEVICE;
+  return fused_launch(a, L, ws, stream);
 }
 
 moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,

@@ -244,3 +244,29 @@ def test_combine_validation(lib):
 def test_experts_phase_validation(lib):
     assert _fwd(lib, phase=3) == moe.MOE_ERR_INVALID_ARGUMENT
     assert _fwd(lib, phase=-1) == moe.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_fused_noalloc_validation(lib):
+    # host-side checks before anything touches a device: the same argument checks as
+    # moe_fused_forward, and requests whose workspace exceeds the fixed scratch array
+    def fused(**kw):
+        base = dict(T=32, d=4096, f=14336, E=8, k=2, x_dtype=moe.MOE_BF16, w_dtype=moe.MOE_BF16,
+                    scale_fmt=moe.MOE_SCALE_F32, x=0x1000, logits=None, w_router=0x1000,
+                    logits_out=None, w_gate=0x1000, w_up=0x1000, w_down=0x1000, s_gate=None,
+                    s_up=None, s_down=None, out=0x1000, out_dtype=moe.MOE_BF16, topk_ids=0x1000,
+                    topk_w=0x1000, workspace=None, workspace_bytes=0)
+        base.update(kw)
+        return lib.moe_fused_forward_noalloc(ctypes.byref(moe.moe_fused_args(**base)), None)
+    assert lib.moe_fused_forward_noalloc(None, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert fused(k=9) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert fused(x=None) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert fused(T=129) == moe.MOE_ERR_UNSUPPORTED            # more than 256 pairs
+    # 256 pairs of a d = f = 32768 bf16 layer with fp32 output need 48 MiB of workspace: beyond
+    # the array
+    need = lib.moe_fused_workspace_size(128, 32768, 32768, 8, 2, moe.MOE_BF16, moe.MOE_F32)
+    assert need > moe.NOALLOC_SCRATCH_BYTES
+    assert fused(T=128, d=32768, f=32768, out_dtype=moe.MOE_F32) == moe.MOE_ERR_UNSUPPORTED
+    # the Mixtral-shaped decode layer fits at every batch the fused path takes, in every format
+    for wdt in (moe.MOE_BF16, moe.MOE_FP8_E4M3, moe.MOE_FP4_E2M1):
+        n = lib.moe_fused_workspace_size(128, 4096, 14336, 8, 2, wdt, moe.MOE_BF16)
+        assert 0 < n <= moe.NOALLOC_SCRATCH_BYTES, (wdt, n)
