@@ -492,6 +492,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the skewed 128-expert and DeepSeek-V3-shaped fp8 workloads")
+    ap.add_argument("--others", default="skewed,dsv3_fp8,dsv3_fp8_ue8m0",
+                    help="which of the skewed / DeepSeek-V3-shaped workloads to time (comma list "
+                         "of skewed, dsv3_fp8, dsv3_fp8_ue8m0)")
     ap.add_argument("--report", default="",
                     help="also time the fp8 / FP4 and fused decode variants, the DeepSeek-V3-shaped "
                          "layer with FP4 experts and the tiny fp32 layer; write every workload's "
@@ -635,23 +638,27 @@ def main():
 
     # The skewed 128-expert layer and the DeepSeek-V3-shaped fine-grained FP8 layer (its own
     # fp32 128x128 block scales, and the same masters with UE8M0 scales) are part of every run.
-    if not args.no_others:
-        osteps = max(args.steps, 5)
+    others = [] if args.no_others else [w for w in args.others.split(",") if w]
+    osteps = max(args.steps, 5)
+    if "skewed" in others:
         result["skewed"] = measure_other(moe, synth, synth.SKEWED_128E, osteps, args.warmup)
+    fmts = tuple(f for f, w in (("f32", "dsv3_fp8"), ("ue8m0", "dsv3_fp8_ue8m0")) if w in others)
+    if fmts:
         t0 = time.perf_counter()
-        wq = lowp_weights(moe, synth, synth.DSV3_FP8, ("f32", "ue8m0"))
+        wq = lowp_weights(moe, synth, synth.DSV3_FP8, fmts)
         log("%s weights quantised on the device in %.1fs" % (synth.DSV3_FP8.name,
                                                                 time.perf_counter() - t0))
-        result["dsv3_fp8"] = measure_other(moe, synth, synth.DSV3_FP8, osteps, args.warmup,
-                                           weights=wq.pop("f32"), scale_fmt="f32")
-        result["dsv3_fp8_ue8m0"] = measure_other(moe, synth, synth.DSV3_FP8, osteps, args.warmup,
-                                                 weights=wq.pop("ue8m0"), scale_fmt="ue8m0",
-                                                 name=synth.DSV3_FP8.name + "_ue8m0")
+        if "f32" in wq:
+            result["dsv3_fp8"] = measure_other(moe, synth, synth.DSV3_FP8, osteps, args.warmup,
+                                               weights=wq.pop("f32"), scale_fmt="f32")
+        if "ue8m0" in wq:
+            result["dsv3_fp8_ue8m0"] = measure_other(
+                moe, synth, synth.DSV3_FP8, osteps, args.warmup, weights=wq.pop("ue8m0"),
+                scale_fmt="ue8m0", name=synth.DSV3_FP8.name + "_ue8m0")
         del wq
         torch.cuda.empty_cache()
     if args.report:
-        if not args.no_others:
-            rep += [result["skewed"], result["dsv3_fp8"], result["dsv3_fp8_ue8m0"]]
+        rep += [result[w] for w in ("skewed", "dsv3_fp8", "dsv3_fp8_ue8m0") if w in result]
         w4 = lowp_weights(moe, synth, synth.DSV3_FP8, (), fp4=True)
         rep.append(measure_other(moe, synth, synth.DSV3_FP8, max(args.steps, 5), args.warmup,
                                  weights=w4.pop("fp4"), scale_fmt="fp4",

@@ -214,7 +214,8 @@ moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q
  * Gate and up projections run as one grouped GEMM whose epilogue applies SwiGLU and writes the
  * hidden activation h [P, f] to the workspace (bf16; e4m3 + per-128 scales on the fp8 path).
  * The down projection runs as a second grouped GEMM whose epilogue writes y in a->y_layout.
- * Small batches (P <= 256) use weight-streaming kernels with the weight rows on the MFMA M side.
+ * Small batches (few rows per expert, see moe_experts_small_batch) use weight-streaming kernels
+ * with the weight rows on the MFMA M side.
  * a->phase selects both projections (MOE_PHASE_ALL) or one of them (see moe_experts_phase); an
  * unknown value is MOE_ERR_INVALID_ARGUMENT.
  *
@@ -280,6 +281,16 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream);
 size_t moe_experts_workspace_size(int T, int d, int f, int E, int k, moe_dtype act_dtype,
                                   moe_dtype w_dtype);
 
+/* Which kernels moe_experts_forward runs for these sizes (the Transformers "Experts backends"
+ * page, decode-time switch: a kernel made for small batches below some size; the AWS fused-MoE
+ * news page, swap-AB for small token counts): 1 = the small-batch weight-streaming kernels (weight
+ * rows on the matrix unit's M side), 0 = the tiled grouped GEMMs, -1 = no kernel for this dtype
+ * combination or invalid sizes. The switch is on the mean number of rows per expert: small-batch
+ * while T*k <= 12 E (bf16) or T*k <= 16 E (e4m3 / E2M1 weights; bf16 also needs d % 128 == 0 and
+ * f % 128 == 0); fp32 layers always take the tiled kernels. */
+int moe_experts_small_batch(int T, int d, int f, int E, int k, moe_dtype act_dtype,
+                            moe_dtype w_dtype);
+
 /* ------------------------------------------------------------------------------------------
  * moe_combine - weighted sum of each token's k expert outputs.
  * (Transformers "Experts backends" page, introduction; lira-now explainer, section 4 (router +
@@ -304,8 +315,10 @@ moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
  * topk_ids), and the steps that need every workgroup's results (h quantisation, combine) stay
  * launches of their own, since a hand-off inside a launch costs each workgroup an L2 write-back
  * and invalidation on gfx950. Computes what moe_route + moe_permute (+ fp8_quantize_act) +
- * moe_experts_forward (slots) + moe_combine compute, with the same arithmetic, so the outputs
- * are bit-identical to that sequence.
+ * moe_experts_forward (slots) + moe_combine compute: routing ids and weights bit-identical to that
+ * sequence, and the output too wherever the sequence runs the same small-batch kernels
+ * (moe_experts_small_batch(...) == 1; beyond that batch size it runs the tiled GEMMs, whose
+ * intermediate rounding differs).
  *
  *  T*k <= 256 pairs (MOE_ERR_UNSUPPORTED otherwise); d % 128 == f % 128 == 0; E <= 1024, k <= E.
  *  x [T, d] (MOE_BF16, or MOE_F32 with fp8 / FP4 experts), 16-byte aligned.

@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = (
     "fp8_quantize_weight_ue8m0", "fp4_quantize_weight_mx", "fp4_tile_weight",
     "moe_experts_forward",
     "moe_experts_workspace_size", "moe_combine", "moe_fused_forward", "moe_fused_workspace_size",
-    "moe_fused_forward_noalloc",
+    "moe_fused_forward_noalloc", "moe_experts_small_batch",
 )
 NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -111,6 +111,7 @@ def load_library(path: str = LIB_PATH):
         "moe_fused_forward": ([ctypes.POINTER(moe_fused_args), vp], st),
         "moe_fused_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "moe_fused_forward_noalloc": ([ctypes.POINTER(moe_fused_args), vp], st),
+        "moe_experts_small_batch": ([i32, i32, i32, i32, i32, i32, i32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -289,6 +290,12 @@ def fp4_tile_weight(q: torch.Tensor) -> torch.Tensor:
     out = torch.empty_like(q)
     _check(lib.fp4_tile_weight(_ptr(q), batch, N, K, _ptr(out), _stream()))
     return out
+
+
+def experts_small_batch(T, d, f, E, k, act_dtype: int, w_dtype: int) -> int:
+    """1 if moe_experts_forward takes the small-batch kernels for these sizes, 0 for the tiled
+    grouped GEMMs, -1 if it has no kernel for them (moe_experts_small_batch)."""
+    return load_library().moe_experts_small_batch(T, d, f, E, k, act_dtype, w_dtype)
 
 
 def experts_workspace_bytes(T, d, f, E, k, act_dtype: int, w_dtype: int) -> int:

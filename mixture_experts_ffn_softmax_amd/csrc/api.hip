@@ -34,25 +34,35 @@ moe_status check_topology(int T, int E, int k) {
   return MOE_OK;
 }
 
-// Small-batch (weight streaming) kernels take over at or below this many pairs.
-constexpr int kDecodeMaxPairs = 256;
-
-inline bool uses_decode(moe_dtype act, moe_dtype w, long long P, int d, int f) {
-  return act == MOE_BF16 && w == MOE_BF16 && P <= kDecodeMaxPairs && d % 128 == 0 &&
-         f % 128 == 0;
-}
+// Small-batch (weight streaming) kernels take over while the mean number of rows per expert,
+// P / E, is small; past it the tiled grouped GEMMs are faster. Both paths timed on MI355X at the
+// Mixtral-shaped (E = 8) and DeepSeek-V3-shaped (E = 256) layers for T = 8 .. 512:
+//   bf16: small-batch faster up to 12 rows per expert (Mixtral T = 48: 0.566 vs 0.574 ms), the
+//         tiled GEMM from 16 (T = 64: 0.579 vs 0.622 ms);
+//   e4m3 / E2M1: small-batch faster up to 16 rows per expert on the Mixtral shape (fp32 scales,
+//         UE8M0 and E2M1; tiled from 32) and on the DeepSeek-V3 shape with E2M1 weights (1.28 vs
+//         1.50 ms at 16 rows); on the DeepSeek-V3 shape with e4m3 weights the tiled GEMM is up to
+//         5 % faster from 4 (UE8M0) or 16 (fp32 scales) rows, the largest loss of this rule.
+constexpr int kSmallRowsBf16 = 12;
+constexpr int kSmallRowsLowp = 16;
 
 // 8-bit activation codes with e4m3 or E2M1 weights (block scales, fp8 quantisation of x and h)
 inline bool is_low_precision(moe_dtype w) { return w == MOE_FP8_E4M3 || w == MOE_FP4_E2M1; }
 
-// fp8 layers with few pairs take the weight-streaming fp8 kernels (the only E2M1 kernels).
-inline bool uses_fp8_decode(moe_dtype act, moe_dtype w, long long P) {
-  return act == MOE_FP8_E4M3 && is_low_precision(w) && P <= kDecodeMaxPairs;
+inline bool uses_decode(moe_dtype act, moe_dtype w, long long P, int E, int d, int f) {
+  return act == MOE_BF16 && w == MOE_BF16 && P <= static_cast<long long>(kSmallRowsBf16) * E &&
+         d % 128 == 0 && f % 128 == 0;
+}
+
+// fp8 layers with few rows per expert take the weight-streaming fp8 kernels.
+inline bool uses_fp8_decode(moe_dtype act, moe_dtype w, long long P, int E) {
+  return act == MOE_FP8_E4M3 && is_low_precision(w) &&
+         P <= static_cast<long long>(kSmallRowsLowp) * E;
 }
 
 // bf16 tiled GEMMs cut their tail tiles; they need partial-tile slots and counters.
-inline bool uses_split(moe_dtype act, moe_dtype w, long long P, int d, int f) {
-  return act == MOE_BF16 && w == MOE_BF16 && !uses_decode(act, w, P, d, f);
+inline bool uses_split(moe_dtype act, moe_dtype w, long long P, int E, int d, int f) {
+  return act == MOE_BF16 && w == MOE_BF16 && !uses_decode(act, w, P, E, d, f);
 }
 
 struct ExpertsLayout {
@@ -78,14 +88,14 @@ ExpertsLayout experts_layout(int T, int d, int f, int E, int k, moe_dtype act, m
     off = align_up(off + static_cast<size_t>(T) * (d / kFp8Group) * sizeof(float));
   // fp8 decode: fp32 h before its quantisation, and its e8m0 scale bytes
   L.h32 = L.h_scale_bytes = 0;
-  if (uses_fp8_decode(act, w, static_cast<long long>(P))) {
+  if (uses_fp8_decode(act, w, static_cast<long long>(P), E)) {
     L.h32 = off;
     off = align_up(off + P * f * sizeof(float));
     L.h_scale_bytes = off;
     off = align_up(off + P * (f / kFp8Group));
   }
   L.split_partial = 0;
-  if (uses_split(act, w, static_cast<long long>(P), d, f)) {
+  if (uses_split(act, w, static_cast<long long>(P), E, d, f)) {
     L.split_partial = off;
     off = align_up(off + static_cast<size_t>(kSplitSlots) * 256 * 256 * sizeof(float));
   }
@@ -268,6 +278,20 @@ moe_status fp4_quantize_weight_mx(const void* w, moe_dtype w_dtype, int batch, i
   return dev(launch_quantize_weight_mx4(w, w_dtype, nblocks, q, scales, stream));
 }
 
+int moe_experts_small_batch(int T, int d, int f, int E, int k, moe_dtype act_dtype,
+                            moe_dtype w_dtype) {
+  if (check_topology(T, E, k) != MOE_OK || d < 1 || f < 1) return -1;
+  const long long P = static_cast<long long>(T) * k;
+  const bool bf16 = act_dtype == MOE_BF16 && w_dtype == MOE_BF16;
+  const bool fp8 = act_dtype == MOE_FP8_E4M3 && is_low_precision(w_dtype);
+  const bool f32 = act_dtype == MOE_F32 && w_dtype == MOE_F32;
+  if (!bf16 && !fp8 && !f32) return -1;
+  return (bf16 && uses_decode(act_dtype, w_dtype, P, E, d, f)) ||
+                 (fp8 && uses_fp8_decode(act_dtype, w_dtype, P, E))
+             ? 1
+             : 0;
+}
+
 size_t moe_experts_workspace_size(int T, int d, int f, int E, int k, moe_dtype act_dtype,
                                   moe_dtype w_dtype) {
   if (check_topology(T, E, k) != MOE_OK || d < 1 || f < 1) return 0;
@@ -355,16 +379,16 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   X.y = a->y;
   X.h = ws + L.h;
   X.h_scales = reinterpret_cast<float*>(ws + L.h_scales);
-  const bool fp8_decode = fp8 && uses_fp8_decode(act, w, P);
+  const bool fp8_decode = fp8 && uses_fp8_decode(act, w, P, a->E);
   X.h32 = fp8_decode ? reinterpret_cast<float*>(ws + L.h32) : nullptr;
   X.h_scale_bytes = fp8_decode ? reinterpret_cast<uint8_t*>(ws + L.h_scale_bytes) : nullptr;
   X.cpx = cus_per_xcd();
-  const bool split = uses_split(act, w, P, a->d, a->f);
+  const bool split = uses_split(act, w, P, a->E, a->d, a->f);
   X.split_partial = split ? reinterpret_cast<float*>(ws + L.split_partial) : nullptr;
   X.run_gate_up = run_gate_up ? 1 : 0;
   X.run_down = run_down ? 1 : 0;
 
-  const bool decode = uses_decode(act, w, P, a->d, a->f);
+  const bool decode = uses_decode(act, w, P, a->E, a->d, a->f);
   int bm_a, bm_b;
   if (f32) { bm_a = bm_b = f32_tile_rows(); }
   else if (fp8_decode) { bm_a = bm_b = 0; }  // no tile table

@@ -152,14 +152,19 @@ __device__ __forceinline__ void spread_frag_reads() {
 // DMA of stage `st` of one operand into one buffer. The first DW waves issue all of it: wave
 // w < DW fills rows (IPW w + i) * 8 .. +7 (i < IPW = 32 / DW); waves w >= DW issue none. A rows
 // at or past the tile's valid rows are skipped (their waves skip the MFMAs); B rows 0..127 come
-// from rb0, rows 128..255 from rb1. Stages past `last` re-read stage `last` (never used), so
-// every access stays in bounds.
+// from rb0, rows 128..255 from rb1. Stages past `last` (the prefetches the loop issues beyond the
+// piece's end) get an offset past the buffer's range: the loads return zeros without touching
+// memory, their buffers are never read, and every stage still issues the same instructions, so
+// the loop's vmcnt waits stay uniform. (Buffer byte offsets stay below 2^31, so offset + 2^31
+// does not wrap.)
+constexpr uint32_t kPastEnd = 0x80000000u;
+
 template <int DW>
 __device__ __forceinline__ void dma_a(const char* buf, const Dma<32 / DW>& d, int st, int last,
                                       int wave, int rows) {
   constexpr int IPW = 32 / DW;
   if (wave >= DW) return;
-  const uint32_t kb = static_cast<uint32_t>(min(st, last)) * kBK * 2u;
+  const uint32_t kb = st <= last ? static_cast<uint32_t>(st) * kBK * 2u : kPastEnd;
   const uint32_t base = lds_offset(buf);
 #pragma unroll
   for (int i = 0; i < IPW; ++i)
@@ -171,7 +176,7 @@ __device__ __forceinline__ void dma_b(const char* buf, const Dma<32 / DW>& d, in
                                       int wave) {
   constexpr int IPW = 32 / DW;
   if (wave >= DW) return;
-  const uint32_t kb = static_cast<uint32_t>(min(st, last)) * kBK * 2u;
+  const uint32_t kb = st <= last ? static_cast<uint32_t>(st) * kBK * 2u : kPastEnd;
   const uint32_t base = lds_offset(buf);
 #pragma unroll
   for (int i = 0; i < IPW; ++i)
@@ -388,8 +393,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   const int arow0 = wm * (kBM / WM);
   const int bcol0 = MODE == kGateUp ? wn * (128 / WN) : wn * (kBN / WN);
 
+  // this piece's stages: [st0, st0 + nst) of the K / kBK stages
+  const int st_all = p.K / kBK;
+  const int st0 = split * st_all / nsplit;
+  const int nst = (split + 1) * st_all / nsplit - st0;
+  const int last = st0 + nst - 1;
+
   // DMA addressing: lane l of instruction i of wave w supplies row (IPW w + i) * 8 + l / 8 at
-  // chunk position l % 8.
+  // chunk position l % 8. The weight rows need no gathered index, so the first two B stages are
+  // requested before the token rows of the A operand are looked up.
   Dma<IPW> d;
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
   d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K * 2u);
@@ -400,13 +412,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   for (int i = 0; i < IPW; ++i) {
     const int r = (wave * IPW + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int pos = tc.row0 + min(r, tc.rows - 1);
-    const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
-    d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
     const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
                                   : min(tc.ntile * kBN + r, p.N - 1);
     d.boff[i] = static_cast<uint32_t>(n) * p.K * 2u + c * 16;
   }
+  dma_b<DW>(b0, d, st0, last, wave);
+  dma_b<DW>(b1, d, st0 + 1, last, wave);
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = (wave * IPW + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int pos = tc.row0 + min(r, tc.rows - 1);
+    const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+    d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
+  }
+  dma_a<DW>(a0, d, st0, last, wave, tc.rows);
 
   acc_t<ME> acc[MI][NJ];
 #pragma unroll
@@ -416,15 +436,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
 #pragma unroll
       for (int e = 0; e < AccOf<ME>::n; ++e) acc[i][j][e] = 0.0f;
 
-  // this piece's stages: [st0, st0 + nst) of the K / kBK stages
-  const int st_all = p.K / kBK;
-  const int st0 = split * st_all / nsplit;
-  const int nst = (split + 1) * st_all / nsplit - st0;
-  const int last = st0 + nst - 1;
-  dma_a<DW>(a0, d, st0, last, wave, tc.rows);
-  dma_b<DW>(b0, d, st0, last, wave);
-  dma_b<DW>(b1, d, st0 + 1, last, wave);
-  wait_vmcnt<IPW>();  // all but this wave's B DMAs of stage 1
+  wait_vmcnt<0>();  // stage 0 (and B of stage 1, requested before it)
   __builtin_amdgcn_s_barrier();
   // Waves whose rows all lie past the tile's valid rows (the short last tile of an expert) skip
   // their fragment reads and MFMAs; the condition is wave-uniform.
@@ -475,7 +487,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
     if (s + 5 < nst) MOE_STAGE(a1, b2, a0, b0, b1, s + 5)
   }
 #undef MOE_STAGE
-  wait_vmcnt<0>();  // the clamped re-reads past the last stage
+  wait_vmcnt<0>();  // the past-the-end prefetches (no memory traffic)
   __syncthreads();
 
   if (nsplit > 1) {

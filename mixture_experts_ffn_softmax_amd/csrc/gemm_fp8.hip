@@ -80,7 +80,10 @@ struct DmaF {
   uint32_t bsoff;            // E2M1: this lane's weight row's MX scale offset
 };
 
-// Stage `st` (clamped to the last real stage so every access stays in bounds) into `buf`. Only
+// Stage `st` into `buf`. Stages past the last one (the prefetches the loop issues beyond the end)
+// get offsets past every buffer's range: the loads return zeros without touching memory, their
+// buffers are never read, and every stage issues the same instructions, so the loop's vmcnt waits
+// stay uniform (byte offsets stay below 2^31, so offset + 2^31 does not wrap). Only
 // waves 0..3, one per SIMD, issue it (the SIMD's other wave keeps its MFMA and promotion work
 // going while the DMA wave waits for the texture unit's queue; measured 5-6 % faster than all 8
 // waves sharing it): wave w fills A rows (4w + i) * 8 .. +7, B rows (8w + i) * 8 .. +7 (one KB
@@ -93,8 +96,10 @@ template <bool kW4>
 __device__ __forceinline__ void dmaf(const char* buf, const DmaF& d, int st, int nst, int wave,
                                      int lane) {
   if (wave >= 4) return;
-  const int sc = min(st, nst - 1);
-  const uint32_t kb = static_cast<uint32_t>(sc) * kBKf;
+  const bool in = st < nst;
+  const uint32_t sc = in ? static_cast<uint32_t>(st) : 0u;
+  const uint32_t past = in ? 0u : 0x80000000u;
+  const uint32_t kb = sc * kBKf + past;
   const uint32_t base = lds_offset(buf);
 #pragma unroll
   for (int i = 0; i < 4; ++i) dma16(base + (wave * 4 + i) * 1024, d.aoff[i], d.ra, kb);
@@ -102,15 +107,15 @@ __device__ __forceinline__ void dmaf(const char* buf, const DmaF& d, int st, int
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       dma16(base + kAf + (wave * 4 + i) * 1024, d.boff[i], wave < 2 ? d.rb0 : d.rb1,
-            static_cast<uint32_t>(sc) * 1024u);
+            sc * 1024u + past);
     dma4(base + kAf + kBf4 + kBMf * 4 + wave * 256, d.bsoff, wave < 2 ? d.rbs0 : d.rbs1,
-         static_cast<uint32_t>(sc) * 4u);
-    if (lane < 32) dma4(base + kAf + kBf4 + wave * 128, d.soff, d.rs, static_cast<uint32_t>(sc) * 4u);
+         sc * 4u + past);
+    if (lane < 32) dma4(base + kAf + kBf4 + wave * 128, d.soff, d.rs, sc * 4u + past);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       dma16(base + kAf + (wave * 8 + i) * 1024, d.boff[i], wave < 2 ? d.rb0 : d.rb1, kb);
-    if (lane < 32) dma4(base + kAf + kBf + wave * 128, d.soff, d.rs, static_cast<uint32_t>(sc) * 4u);
+    if (lane < 32) dma4(base + kAf + kBf + wave * 128, d.soff, d.rs, sc * 4u + past);
   }
 }
 

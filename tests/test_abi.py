@@ -270,3 +270,21 @@ def test_fused_noalloc_validation(lib):
     for wdt in (moe.MOE_BF16, moe.MOE_FP8_E4M3, moe.MOE_FP4_E2M1):
         n = lib.moe_fused_workspace_size(128, 4096, 14336, 8, 2, wdt, moe.MOE_BF16)
         assert 0 < n <= moe.NOALLOC_SCRATCH_BYTES, (wdt, n)
+
+
+def test_small_batch_switch(lib):
+    # the switch on mean rows per expert (host logic only)
+    sb = lib.moe_experts_small_batch
+    BF, F8, F4, F32 = moe.MOE_BF16, moe.MOE_FP8_E4M3, moe.MOE_FP4_E2M1, moe.MOE_F32
+    assert sb(32, 4096, 14336, 8, 2, BF, BF) == 1           # Mixtral decode: 8 rows per expert
+    assert sb(48, 4096, 14336, 8, 2, BF, BF) == 1           # 12 rows per expert
+    assert sb(49, 4096, 14336, 8, 2, BF, BF) == 0
+    assert sb(4096, 4096, 14336, 8, 2, BF, BF) == 0         # prefill
+    assert sb(40, 192, 320, 8, 2, BF, BF) == 0              # bf16 small-batch needs d, f % 128
+    assert sb(512, 7168, 2048, 256, 8, F8, F8) == 1         # 16 rows per expert
+    assert sb(513, 7168, 2048, 256, 8, F8, F4) == 0
+    assert sb(8192, 7168, 2048, 256, 8, F8, F8) == 0
+    assert sb(64, 4096, 14336, 8, 2, F8, F4) == 1
+    assert sb(64, 128, 256, 8, 2, F32, F32) == 0
+    assert sb(64, 128, 256, 8, 2, BF, F8) == -1
+    assert sb(0, 128, 256, 8, 2, BF, BF) == -1

@@ -110,9 +110,11 @@ def _quantised(spec):
 
 DECODE = [
     synth.DSV3_FP8.with_(name="fp4dec_T32_d512_f384_E8_k2", T=32, d=512, f=384, E=8, k=2),
-    # about 100 tokens per expert: several 64-token passes
-    synth.DSV3_FP8.with_(name="fp4dec_T200_d256_f256_E2_k1", T=200, d=256, f=256, E=2, k=1),
-    # P = 256, the largest batch the streaming kernels take; f not a multiple of 256
+    # 12.5 rows per expert on average, skewed: one expert holds 178 tokens (several 64-token
+    # passes), one 20, two 1, the others none
+    synth.DSV3_FP8.with_(name="fp4dec_T200_d256_f256_E16_k1_skew", T=200, d=256, f=256, E=16, k=1,
+                         skew=3.0),
+    # 16 rows per expert, the largest batch the streaming kernels take; f not a multiple of 256
     synth.DSV3_FP8.with_(name="fp4dec_T64_d384_f640_E16_k4", T=64, d=384, f=640, E=16, k=4),
     synth.DSV3_FP8.with_(name="fp4dec_T3_d128_f128_E4_k1", T=3, d=128, f=128, E=4, k=1),
     # every token on every expert
@@ -120,9 +122,10 @@ DECODE = [
 ]
 
 
-@pytest.mark.parametrize("spec", DECODE, ids=lambda s: s.name)
-def test_fp4_decode_layers(spec):
+def _fp4_layer(spec, small):
     log(spec.name)
+    assert moe.experts_small_batch(spec.T, spec.d, spec.f, spec.E, spec.k, moe.MOE_FP8_E4M3,
+                                   moe.MOE_FP4_E2M1) == small
     x = synth.gen_x(spec)
     logits = synth.gen_logits(spec)
     wq, wq_ref = _quantised(spec)
@@ -141,18 +144,24 @@ def test_fp4_decode_layers(spec):
         assert_close_rel_max(got, ref, 6e-2, "%s %s" % (spec.name, layout))
 
 
+@pytest.mark.parametrize("spec", DECODE, ids=lambda s: s.name)
+def test_fp4_decode_layers(spec):
+    _fp4_layer(spec, 1)
+
+
 # larger batches: the tiled fp8 GEMM with E2M1 weights (ragged row tiles, a partial down tile)
 PREFILL = [
     synth.DSV3_FP8.with_(name="fp4pf_T300_d512_f256_E16_k4", T=300, d=512, f=256, E=16, k=4),
     synth.DSV3_FP8.with_(name="fp4pf_T1000_d384_f640_E8_k2", T=1000, d=384, f=640, E=8, k=2),
     synth.DSV3_FP8.with_(name="fp4pf_T257_d256_f128_E4_k1", T=257, d=256, f=128, E=4, k=1),
+    # one pair past the small-batch limit (16 rows per expert)
+    synth.DSV3_FP8.with_(name="fp4pf_T65_d256_f256_E8_k2_switch", T=65, d=256, f=256, E=8, k=2),
 ]
 
 
 @pytest.mark.parametrize("spec", PREFILL, ids=lambda s: s.name)
 def test_fp4_prefill_layers(spec):
-    assert spec.P > 256
-    test_fp4_decode_layers(spec)
+    _fp4_layer(spec, 0)
 
 
 def test_fp4_rejects_unsupported():

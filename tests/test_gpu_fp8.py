@@ -43,7 +43,7 @@ SMALL = [
     synth.DSV3_FP8.with_(name="fp8_T1000_d384_f640_E8_k2", T=1000, d=384, f=640, E=8, k=2),
     synth.DSV3_FP8.with_(name="fp8_T7_d256_f128_E4_k1", T=7, d=256, f=128, E=4, k=1),
     # one expert (small-batch kernels) and k = E (tiled GEMMs)
-    synth.DSV3_FP8.with_(name="fp8_dense_T40_d256_f128_E1_k1", T=40, d=256, f=128, E=1, k=1),
+    synth.DSV3_FP8.with_(name="fp8_dense_T16_d256_f128_E1_k1", T=16, d=256, f=128, E=1, k=1),
     synth.DSV3_FP8.with_(name="fp8_all_T100_d256_f128_E4_k4", T=100, d=256, f=128, E=4, k=4),
     synth.DSV3_FP8.with_(name="fp8_one_T1_d256_f128_E8_k2", T=1, d=256, f=128, E=8, k=2),
 ]
@@ -192,12 +192,16 @@ def test_dsv3_fp8_full_sampled(fmt):
     assert n >= 4 * len(need)
 
 
-# ---- small batches: the weight-streaming fp8 kernels (P <= 256 pairs) ------------------------
+# ---- small batches: the weight-streaming fp8 kernels (at most 16 rows per expert) -----------
 
 DECODE = [
     synth.DSV3_FP8.with_(name="fp8dec_T32_d512_f384_E8_k2", T=32, d=512, f=384, E=8, k=2),
-    # about 100 tokens per expert: several 64-token passes
-    synth.DSV3_FP8.with_(name="fp8dec_T200_d256_f256_E2_k1", T=200, d=256, f=256, E=2, k=1),
+    # 12.5 rows per expert on average, skewed: one expert holds 178 tokens (several 64-token
+    # passes), one 20, two 1, the others none
+    synth.DSV3_FP8.with_(name="fp8dec_T200_d256_f256_E16_k1_skew", T=200, d=256, f=256, E=16, k=1,
+                         skew=3.0),
+    # the last batch of the small-batch kernels: 16 rows per expert
+    synth.DSV3_FP8.with_(name="fp8dec_T64_d256_f256_E8_k2_switch", T=64, d=256, f=256, E=8, k=2),
     # P = 256, the largest batch the streaming kernels take
     synth.DSV3_FP8.with_(name="fp8dec_T64_d384_f640_E16_k4", T=64, d=384, f=640, E=16, k=4),
 ]
@@ -206,7 +210,18 @@ DECODE = [
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("spec", DECODE, ids=lambda s: s.name)
 def test_fp8_decode_layers(spec, fmt):
-    assert spec.P <= 256
+    assert moe.experts_small_batch(spec.T, spec.d, spec.f, spec.E, spec.k, moe.MOE_FP8_E4M3,
+                                   moe.MOE_FP8_E4M3) == 1
+    test_small_fp8_layers(spec, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_first_tiled_batch(fmt):
+    # one pair past the small-batch limit (16 rows per expert): the tiled GEMMs
+    spec = synth.DSV3_FP8.with_(name="fp8_T65_d256_f256_E8_k2_switch", T=65, d=256, f=256, E=8,
+                                k=2)
+    assert moe.experts_small_batch(spec.T, spec.d, spec.f, spec.E, spec.k, moe.MOE_FP8_E4M3,
+                                   moe.MOE_FP8_E4M3) == 0
     test_small_fp8_layers(spec, fmt)
 
 

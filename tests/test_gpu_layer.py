@@ -84,14 +84,15 @@ SMALL_BF16 = [
     synth.TINY_F32.with_(name="bf16_T5_d128_f128_E8_k2", dtype="bf16", T=5, d=128, f=128),
     synth.MIXTRAL_PREFILL.with_(name="bf16_router_T600_d512_f1024_E8_k2", T=600, d=512, f=1024),
     # degenerate topologies: one expert (a dense gated MLP, routing weight 1) and every token on
-    # every expert (k = E), each on the tiled GEMMs (P > 256) and the small-batch kernels
+    # every expert (k = E), each on the tiled GEMMs and on the small-batch kernels (at most 12
+    # rows per expert)
     synth.TINY_F32.with_(name="bf16_dense_T300_d256_f384_E1_k1", dtype="bf16", T=300, d=256,
                          f=384, E=1, k=1),
-    synth.TINY_F32.with_(name="bf16_dense_T20_d256_f256_E1_k1", dtype="bf16", T=20, d=256, f=256,
+    synth.TINY_F32.with_(name="bf16_dense_T12_d256_f256_E1_k1", dtype="bf16", T=12, d=256, f=256,
                          E=1, k=1),
     synth.TINY_F32.with_(name="bf16_all_T100_d256_f256_E4_k4", dtype="bf16", T=100, d=256, f=256,
                          E=4, k=4),
-    synth.TINY_F32.with_(name="bf16_all_T16_d256_f256_E4_k4", dtype="bf16", T=16, d=256, f=256,
+    synth.TINY_F32.with_(name="bf16_all_T12_d256_f256_E4_k4", dtype="bf16", T=12, d=256, f=256,
                          E=4, k=4),
     # a single token: one row per selected expert, every other expert empty
     synth.TINY_F32.with_(name="bf16_one_T1_d256_f256_E8_k2", dtype="bf16", T=1, d=256, f=256,
@@ -138,7 +139,8 @@ def test_cut_tail_tiles(spec):
 
 
 def test_bf16_prefill_kernel_on_small_batch_shapes():
-    # P <= 256 goes to the decode kernels; d not a multiple of 128 forces the tiled kernels.
+    # 10 rows per expert would take the small-batch kernels; d not a multiple of 128 forces the
+    # tiled kernels.
     spec = synth.TINY_F32.with_(name="bf16_T40_d192_f320_E8_k2", dtype="bf16", T=40, d=192,
                                 f=320)
     inp = layer_inputs(spec)
@@ -146,22 +148,31 @@ def test_bf16_prefill_kernel_on_small_batch_shapes():
     _check_layer(spec, inp, res, 2e-2)
 
 
+def _assert_small_batch(spec, want=1):
+    act = moe.MOE_F32 if spec.dtype == "f32" else moe.MOE_BF16
+    assert moe.experts_small_batch(spec.T, spec.d, spec.f, spec.E, spec.k, act, act) == want, \
+        spec.name
+
+
 def test_decode_kernel_many_tokens_per_expert():
-    # all 128 tokens on 2 experts -> token passes of 64 in the decode kernels
-    spec = synth.TINY_F32.with_(name="bf16_decode_T128_d256_f512_E4_k2", dtype="bf16", T=128,
-                                d=256, f=512, E=4, k=2, skew=6.0)
+    # 8 rows per expert on average (small-batch kernels), skewed so that all 128 tokens sit on
+    # two experts -> token passes of 64 in the decode kernels
+    spec = synth.TINY_F32.with_(name="bf16_decode_T128_d256_f512_E32_k2", dtype="bf16", T=128,
+                                d=256, f=512, E=32, k=2, skew=6.0)
+    _assert_small_batch(spec)
     inp = layer_inputs(spec)
     res = _run_gpu(spec, inp)
     counts = _check_layer(spec, inp, res, 2e-2)
     assert counts.max() > 64
 
 
-@pytest.mark.parametrize("E", [16, 8])
+@pytest.mark.parametrize("E", [16, 12])
 def test_decode_skewed_partial_token_groups(E):
     # 128 pairs, skewed: two experts hold 50-64 tokens (a pass of 64 with its last group of 16
     # partly filled), the rest a few each (streaming gate/up kernel), the others none.
     spec = synth.TINY_F32.with_(name="bf16_decode_skew_T64_d256_f512_E%d_k2" % E, dtype="bf16",
                                 T=64, d=256, f=512, E=E, k=2, skew=3.0)
+    _assert_small_batch(spec)
     inp = layer_inputs(spec)
     ids, _ = oracle.route(inp["logits"], spec.k)
     counts = np.bincount(ids.reshape(-1), minlength=spec.E)
@@ -176,14 +187,28 @@ def test_decode_skewed_partial_token_groups(E):
 def test_decode_mixed_small_and_large_experts():
     # Skewed routing at a decode-sized batch: some experts get at most 16 tokens (streaming
     # kernel), others more (the multi-pass kernel); both run in one call, K a multiple of 256.
-    spec = synth.SKEWED_128E.with_(name="bf16_decode_mixed_T100_d512_f1024_E8_k2", T=100, d=512,
-                                   f=1024, E=8, k=2)
+    spec = synth.SKEWED_128E.with_(name="bf16_decode_mixed_T100_d512_f1024_E24_k2", T=100, d=512,
+                                   f=1024, E=24, k=2)
+    _assert_small_batch(spec)
     inp = layer_inputs(spec)
     ids, _ = oracle.route(inp["logits"], spec.k)
     counts = np.bincount(ids.reshape(-1), minlength=spec.E)
     assert counts.max() > 16 and ((counts > 0) & (counts <= 16)).any(), counts
     for layout in ("slots", "permuted", "acc_f32"):
         log(spec.name, layout, counts.tolist())
+        res = _run_gpu(spec, inp, layout)
+        _check_layer(spec, inp, res, 2e-2)
+
+
+@pytest.mark.parametrize("T,want", [(48, 1), (49, 0)])
+def test_small_batch_switch_boundary(T, want):
+    # the last batch of the small-batch kernels (12 rows per expert) and the first of the tiled
+    # GEMMs, same layer otherwise
+    spec = synth.MIXTRAL_DECODE.with_(name="bf16_switch_T%d_d512_f1024_E8_k2" % T, T=T, d=512,
+                                      f=1024)
+    _assert_small_batch(spec, want)
+    inp = layer_inputs(spec)
+    for layout in ("slots", "acc_f32"):
         res = _run_gpu(spec, inp, layout)
         _check_layer(spec, inp, res, 2e-2)
 
