@@ -47,22 +47,28 @@ typedef enum {
   MOE_ERR_INVALID_ARGUMENT = 1,   /* bad sizes, k > E, null required pointer, unknown enum */
   MOE_ERR_UNSUPPORTED = 2,        /* valid request without a kernel (e.g. fp8 dims not /128) */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,
-  MOE_ERR_DEVICE = 4              /* a HIP launch or API call failed */
+  MOE_ERR_DEVICE = 4,             /* a HIP launch or API call failed */
+  MOE_STATUS_RANGE_MIN_ = -0x7FFFFFFF - 1, /* range markers, not values: see below */
+  MOE_STATUS_RANGE_MAX_ = 0x7FFFFFFF
 } moe_status;
 
 typedef enum {
   MOE_F32 = 0,       /* IEEE binary32 */
   MOE_BF16 = 1,      /* bfloat16 */
   MOE_FP8_E4M3 = 2,  /* OCP E4M3FN: bias 7, max 448, no infinities */
-  MOE_FP4_E2M1 = 3   /* OCP E2M1 (0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte: element 2j in the
+  MOE_FP4_E2M1 = 3,  /* OCP E2M1 (0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte: element 2j in the
                         low nibble of byte j; expert weights only, with MX scales (below) */
+  MOE_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  MOE_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } moe_dtype;
 
 /* Format of fp8 block scales (Transformers "Fine-grained FP8" page, section "UE8M0 scale
  * format": checkpoints that store weight scales as packed float8_e8m0fnu instead of float32). */
 typedef enum {
   MOE_SCALE_F32 = 0,   /* one fp32 value per block */
-  MOE_SCALE_UE8M0 = 1  /* one byte b per block, value 2^(b - 127) (255 = NaN, never produced) */
+  MOE_SCALE_UE8M0 = 1, /* one byte b per block, value 2^(b - 127) (255 = NaN, never produced) */
+  MOE_SCALE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  MOE_SCALE_RANGE_MAX_ = 0x7FFFFFFF
 } moe_scale_fmt;
 
 /* Layout of the expert outputs that moe_experts_forward writes and moe_combine reads. */
@@ -70,10 +76,17 @@ typedef enum {
   MOE_Y_PERMUTED = 0, /* y [P, d]: unweighted expert outputs, rows in sorted-pair order */
   MOE_Y_SLOTS = 1,    /* y [T, k, d]: y[t][j] = w[t][j] * expert_{ids[t][j]}(x[t]) (fused
                          unpermute + weighting in the down-projection epilogue) */
-  MOE_Y_ACC_F32 = 2   /* y [T, d] fp32: the weighted sum accumulated with atomic adds (zeroed by
+  MOE_Y_ACC_F32 = 2,  /* y [T, d] fp32: the weighted sum accumulated with atomic adds (zeroed by
                          moe_experts_forward); summation order, and so rounding, is not fixed
                          when k > 2 */
+  MOE_Y_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  MOE_Y_RANGE_MAX_ = 0x7FFFFFFF
 } moe_y_layout;
+
+/* Every enum above and below carries a *_RANGE_MIN_ / *_RANGE_MAX_ pair that is not a value:
+ * it makes every int32 a representable value of the enum type (and keeps the type 4 bytes), so an
+ * out-of-range value from a C caller or a foreign-function binding is read without undefined
+ * behaviour and rejected with MOE_ERR_INVALID_ARGUMENT (moe_status_string: "MOE_ERR_UNKNOWN"). */
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
@@ -103,14 +116,22 @@ moe_status moe_route(const float* logits, const void* x, moe_dtype x_dtype,
  * (Transformers "Experts backends" page, backends table row grouped_mm: tokens are sorted by
  * their selected expert so one grouped GEMM projects them all.)
  *
- *  topk_ids     [T, k] int32 in [0, E).
+ *  topk_ids     [T, k] int32 in [0, E). The ids live on the device and are not read by the
+ *               host: an id outside [0, E) is a caller error that the kernels contain rather
+ *               than report. Such a pair is left out of counts and sorted_pair, its pair_pos
+ *               entry is -1, offsets[E] becomes the number of in-range pairs (so offsets[E] < P
+ *               flags the error), rows [offsets[E], P) of sorted_pair and x_perm are left
+ *               unwritten, and no memory outside the buffers named here is touched. moe_combine
+ *               (MOE_Y_PERMUTED) skips pairs whose pair_pos lies outside [0, P); moe_experts
+ *               must not be given such a permutation.
  *  counts       [E] int32 out: pairs per expert.
  *  offsets      [E+1] int32 out: exclusive prefix sum of counts; offsets[E] = P.
  *  sorted_pair  [P] int32 out: pair indices p = t*k + j, expert by expert, ascending p within an
  *               expert (a stable sort, so the result is deterministic).
  *  pair_pos     [P] int32 out: inverse of sorted_pair (pair p sits at row pair_pos[p]).
  *  x, x_perm    optional gather (both NULL to skip): x_perm[r] = x[sorted_pair[r] / k], rows of d
- *               elements of x_dtype (MOE_F32, MOE_BF16 or MOE_FP8_E4M3).
+ *               elements of x_dtype (MOE_F32, MOE_BF16 or MOE_FP8_E4M3); a row whose
+ *               sorted_pair entry lies outside [0, P) is skipped.
  *  x_scales     FP8 only, [T, d/128] fp32; x_perm_scales [P, d/128] receives the gathered rows.
  *  workspace    device scratch of at least moe_permute_workspace_size(T, k, E) bytes.
  * ------------------------------------------------------------------------------------------ */
@@ -249,7 +270,9 @@ moe_status fp4_tile_weight(const uint8_t* q, int batch, int N, int K, uint8_t* q
 typedef enum {
   MOE_PHASE_ALL = 0,      /* gate/up + SwiGLU, then down */
   MOE_PHASE_GATE_UP = 1,  /* gate/up + SwiGLU only: h in the workspace */
-  MOE_PHASE_DOWN = 2      /* down only, from the h of a previous MOE_PHASE_GATE_UP call */
+  MOE_PHASE_DOWN = 2,     /* down only, from the h of a previous MOE_PHASE_GATE_UP call */
+  MOE_PHASE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  MOE_PHASE_RANGE_MAX_ = 0x7FFFFFFF
 } moe_experts_phase;
 
 typedef struct {
@@ -300,7 +323,8 @@ int moe_experts_small_batch(int T, int d, int f, int E, int k, moe_dtype act_dty
  *  MOE_Y_SLOTS:    out[t] = sum_{j<k} y[t][j]                             (y [T, k, d])
  *  MOE_Y_ACC_F32:  out[t] = y[t]                                          (y [T, d] fp32)
  *  Sums run in fp32 in the order j = 0..k-1; one rounding to out_dtype (MOE_F32 or MOE_BF16).
- *  pair_pos and topk_w are read only for MOE_Y_PERMUTED.
+ *  pair_pos and topk_w are read only for MOE_Y_PERMUTED; a pair whose pair_pos lies outside
+ *  [0, T*k) (moe_permute's mark for an out-of-range expert id) adds nothing.
  * ------------------------------------------------------------------------------------------ */
 moe_status moe_combine(const void* y, moe_dtype y_dtype, moe_y_layout layout,
                        const int32_t* pair_pos, const float* topk_w, int T, int k, int d,

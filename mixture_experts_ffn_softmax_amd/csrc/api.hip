@@ -141,8 +141,8 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
     case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    default: return "MOE_ERR_UNKNOWN";
   }
-  return "MOE_ERR_UNKNOWN";
 }
 
 moe_status moe_route(const float* logits, const void* x, moe_dtype x_dtype,

@@ -48,8 +48,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y, 
   } else if (layout == MOE_Y_PERMUTED) {
     for (int j = 0; j < k; ++j) {
       const size_t p = static_cast<size_t>(t) * k + j;
+      const int pos = pair_pos[p];
+      if (pos < 0 || pos >= T * k) continue;  // a pair that moe_permute left out (bad expert id)
       const float wj = topk_w[p];
-      const size_t base = static_cast<size_t>(pair_pos[p]) * d + c0;
+      const size_t base = static_cast<size_t>(pos) * d + c0;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         if (c < n) acc[c] = fmaf(wj, ld(y, base + c), acc[c]);
@@ -127,8 +129,10 @@ __global__ __launch_bounds__(256) void combine_vec_kernel(const YT* __restrict__
   } else if (layout == MOE_Y_PERMUTED) {
     for (int j = 0; j < k; ++j) {
       const size_t p = static_cast<size_t>(t) * k + j;
+      const int pos = pair_pos[p];
+      if (pos < 0 || pos >= T * k) continue;
       const float wj = topk_w[p];
-      ld8(y + static_cast<size_t>(pair_pos[p]) * d + c0, v);
+      ld8(y + static_cast<size_t>(pos) * d + c0, v);
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] = fmaf(wj, v[c], acc[c]);
     }

@@ -13,6 +13,13 @@ namespace {
 constexpr int kChunk = 1024;       // pairs per block in the histogram and scatter kernels
 constexpr int kScatterThreads = 256;
 
+// An expert id outside [0, E) is a caller error. Such a pair is left out of every count, its
+// pair_pos entry is set to -1 and offsets[E] becomes the number of in-range pairs, so the error
+// shows as offsets[E] < P and no LDS or global address is formed from the bad id.
+__device__ __forceinline__ bool in_range(int e, int E) {
+  return static_cast<unsigned>(e) < static_cast<unsigned>(E);
+}
+
 __global__ __launch_bounds__(256) void chunk_histogram_kernel(const int32_t* __restrict__ ids,
                                                               int P, int E,
                                                               int32_t* __restrict__ chunk_hist) {
@@ -21,7 +28,10 @@ __global__ __launch_bounds__(256) void chunk_histogram_kernel(const int32_t* __r
   __syncthreads();
   const int p0 = blockIdx.x * kChunk;
   const int p1 = min(P, p0 + kChunk);
-  for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) atomicAdd(&hist[ids[p]], 1);
+  for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+    const int e = ids[p];
+    if (in_range(e, E)) atomicAdd(&hist[e], 1);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     chunk_hist[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
@@ -76,7 +86,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
       run += chunk_hist[static_cast<size_t>(c) * E + e];
     }
   }
-  if (tid == 0) offsets[E] = P;
+  if (tid == 0) offsets[E] = s[kMaxExperts - 1];
 }
 
 // Stable scatter of pairs [p0, p1) given each expert's next position in `cursor` (LDS). Pairs
@@ -85,7 +95,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // four waves then claim their positions one after another from the running per-expert cursor, so
 // positions follow the flat pair order exactly. Called by all 256 threads of the block.
 __device__ __forceinline__ void scatter_range(const int32_t* __restrict__ ids, int p0, int p1,
-                                              int id_bits, int* cursor,
+                                              int E, int id_bits, int* cursor,
                                               int32_t* __restrict__ sorted_pair,
                                               int32_t* __restrict__ pair_pos) {
   const int lane = lane_id();
@@ -93,8 +103,10 @@ __device__ __forceinline__ void scatter_range(const int32_t* __restrict__ ids, i
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = p0; base < p1; base += kScatterThreads) {
     const int p = base + threadIdx.x;
-    const bool valid = p < p1;
-    const int e = valid ? ids[p] : 0;
+    const int raw = p < p1 ? ids[p] : 0;
+    const bool valid = p < p1 && in_range(raw, E);
+    const int e = valid ? raw : 0;
+    if (p < p1 && !valid) pair_pos[p] = -1;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < id_bits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -123,7 +135,7 @@ __global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     cursor[e] = chunk_base[static_cast<size_t>(blockIdx.x) * E + e];
   __syncthreads();
-  scatter_range(ids, blockIdx.x * kChunk, min(P, (blockIdx.x + 1) * kChunk), id_bits, cursor,
+  scatter_range(ids, blockIdx.x * kChunk, min(P, (blockIdx.x + 1) * kChunk), E, id_bits, cursor,
                 sorted_pair, pair_pos);
 }
 
@@ -138,7 +150,10 @@ __global__ __launch_bounds__(kScatterThreads) void permute_small_kernel(
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kScatterThreads) cursor[e] = 0;
   __syncthreads();
-  for (int p = tid; p < P; p += kScatterThreads) atomicAdd(&cursor[ids[p]], 1);
+  for (int p = tid; p < P; p += kScatterThreads) {
+    const int e = ids[p];
+    if (in_range(e, E)) atomicAdd(&cursor[e], 1);
+  }
   __syncthreads();
   // thread t scans experts [t per, (t + 1) per); a block scan of the 256 partial sums gives each
   // run's start
@@ -162,9 +177,9 @@ __global__ __launch_bounds__(kScatterThreads) void permute_small_kernel(
     cursor[e] = run;
     run += c;
   }
-  if (tid == 0) offsets[E] = P;
+  if (tid == 0) offsets[E] = part[kScatterThreads - 1];
   __syncthreads();
-  scatter_range(ids, 0, P, id_bits, cursor, sorted_pair, pair_pos);
+  scatter_range(ids, 0, P, E, id_bits, cursor, sorted_pair, pair_pos);
 }
 
 // x_perm[r] = x[sorted_pair[r] / k]; one wave per row, 16-byte vectors when the row allows it.
@@ -175,7 +190,9 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
                                                           uint8_t* __restrict__ x_perm) {
   const int r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (r >= P) return;
-  const int t = sorted_pair[r] / k;
+  const int pair = sorted_pair[r];
+  if (static_cast<unsigned>(pair) >= static_cast<unsigned>(P)) return;  // a row left unwritten
+  const int t = pair / k;
   const uint8_t* src = x + static_cast<size_t>(t) * row_bytes;
   uint8_t* dst = x_perm + static_cast<size_t>(r) * row_bytes;
   const int lane = lane_id();

@@ -17,6 +17,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
 _lib = None
 
 F32, BF16, E4M3, E2M1 = 0, 1, 2, 3
@@ -34,12 +35,27 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(clang: str = "/opt/rocm/llvm/bin/clang") -> str:
+    """Compile ``liboracle_san.so``: the same source under AddressSanitizer and
+    UndefinedBehaviorSanitizer (clang, serial: the OpenMP pragmas are ignored). Loaded instead of
+    ``liboracle.so`` when MOE_ORACLE_LIBRARY names it, with clang's ASan runtime preloaded."""
+    tmp = _LIB_SAN + ".tmp%d" % os.getpid()
+    subprocess.check_call(
+        [clang, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+         "-fno-sanitize-recover=undefined", "-Wno-unknown-pragmas", "-shared-libsan", "-shared",
+         "-fPIC", "-o", tmp, _SRC, "-lm"]
+    )
+    os.replace(tmp, _LIB_SAN)
+    return _LIB_SAN
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get("MOE_ORACLE_LIBRARY") or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(path)
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_value.restype = ctypes.c_double

@@ -246,6 +246,27 @@ def test_experts_phase_validation(lib):
     assert _fwd(lib, phase=-1) == moe.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_enum_values_outside_the_declared_ones(lib):
+    # any int32 is a value of each enum type (range markers in the header): rejected, never UB
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    lo, hi = -2 ** 31, 2 ** 31 - 1
+    for v in (lo, -1, 4, hi):
+        assert _fwd(lib, act_dtype=v) in (INV, moe.MOE_ERR_UNSUPPORTED), v
+        assert _fwd(lib, w_dtype=v) in (INV, moe.MOE_ERR_UNSUPPORTED), v
+        assert _fwd(lib, y_dtype=v) in (INV, moe.MOE_ERR_UNSUPPORTED), v
+        assert _fwd(lib, y_layout=v) == INV, v
+        assert _fwd(lib, scale_fmt=v) == INV, v
+        assert _fwd(lib, phase=v) == INV, v
+        assert _fz(lib, out_dtype=v) == INV, v
+        assert _fz(lib, scale_fmt=v) == INV, v
+        assert lib.moe_combine(FAKE, moe.MOE_BF16, v, None, None, 4, 2, 64, FAKE, moe.MOE_BF16,
+                               None) == INV, v
+        assert lib.moe_combine(FAKE, v, moe.MOE_Y_SLOTS, None, None, 4, 2, 64, FAKE,
+                               moe.MOE_BF16, None) == INV, v
+    for v in (lo, -1, 5, hi):
+        assert lib.moe_status_string(v) == b"MOE_ERR_UNKNOWN"
+
+
 def test_fused_noalloc_validation(lib):
     # host-side checks before anything touches a device: the same argument checks as
     # moe_fused_forward, and requests whose workspace exceeds the fixed scratch array

@@ -149,6 +149,47 @@ def test_permute_gather_rows(dtype):
         np.testing.assert_array_equal(to_host(perm.x_perm_scales), xs[sp // k])
 
 
+@pytest.mark.parametrize("T,k,E", [(100, 2, 8), (1500, 3, 16)], ids=["one_workgroup", "chunked"])
+def test_permute_out_of_range_ids(T, k, E):
+    """Ids outside [0, E) are contained: left out of the counts and the scatter, pair_pos -1,
+    offsets[E] = number of in-range pairs, and the combine skips them."""
+    log("permute_bad_ids", T, k, E)
+    ids, w = oracle.route(synth.normal_f32(77, (T, E)), k)
+    rng = np.random.default_rng(78)
+    bad = rng.random(ids.shape) < 0.1
+    ids[bad] = rng.choice(np.array([-1, E, E + 5, -(2 ** 31), 2 ** 31 - 1], np.int32), bad.sum())
+    flat = ids.reshape(-1)
+    ok = (flat >= 0) & (flat < E)
+    nv = int(ok.sum())
+    assert 0 < nv < flat.size
+    d = 64
+    x = synth.normal_bf16(79, (T, d))
+    perm = moe.moe_permute(to_dev(ids), E, x=to_dev(x))
+    torch.cuda.synchronize()
+    counts = np.bincount(flat[ok], minlength=E).astype(np.int32)
+    np.testing.assert_array_equal(to_host(perm.counts), counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    np.testing.assert_array_equal(to_host(perm.offsets), offsets)
+    valid_pairs = np.nonzero(ok)[0]
+    sp = valid_pairs[np.argsort(flat[valid_pairs], kind="stable")].astype(np.int32)
+    np.testing.assert_array_equal(to_host(perm.sorted_pair)[:nv], sp)
+    pp = np.full(flat.size, -1, np.int32)
+    pp[sp] = np.arange(nv, dtype=np.int32)
+    np.testing.assert_array_equal(to_host(perm.pair_pos), pp)
+    np.testing.assert_array_equal(to_host(perm.x_perm)[:nv], x[sp // k])
+    # combine over the permuted rows: the left-out pairs add nothing
+    y = torch.zeros((flat.size, d), dtype=torch.float32, device="cuda")
+    y[:nv] = torch.from_numpy(synth.bf16_bits_to_f32(x[sp // k])).cuda()
+    out = moe.moe_combine(y, "permuted", T, k, d, pair_pos=perm.pair_pos, topk_w=to_dev(w),
+                          out_dtype=torch.float32)
+    wv = np.where(ok.reshape(T, k), w, 0.0).astype(np.float32)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float32)
+    expect = np.zeros((T, d), np.float32)
+    for j in range(k):
+        expect = (wv[:, j:j + 1] * xf + expect).astype(np.float32)
+    np.testing.assert_allclose(to_host(out), expect, rtol=1e-6, atol=1e-6)
+
+
 def _edge_values():
     vals = [0.0, -0.0, 448.0, -448.0, 1e-30, -1e-30, 2.0 ** -6, 2.0 ** -9, 2.0 ** -10,
             3 * 2.0 ** -10, 1.0625, 1.1875, 17.0, 18.0, 19.0, 240.0, 232.0, 0.015625]
