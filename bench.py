@@ -33,6 +33,16 @@ METRIC = "MoE layer active TFLOP/s (prefill) + tokens/s (decode), % MFMA/HBM pea
 CSRC = os.path.join(ROOT, "mixture_experts_ffn_softmax_amd", "csrc")
 GEMM_SOURCES = ("common.h", "gemm_bf16.hip")
 DECODE_SOURCES = ("common.h", "decode_bf16.hip")
+FP8_SOURCES = ("common.h", "gemm_fp8.hip")
+# counter summaries (profiles/) of the gate/up GEMM of the other workloads, by workload name
+OTHER_TRAFFIC = {
+    "skewed_bf16_T16384_d2048_f768_E128_k8": ("gemm_bf16_gate_up_skewed_128e_hbm_bytes.txt",
+                                              GEMM_SOURCES),
+    "dsv3_fp8_T8192_d7168_f2048_E256_k8": ("gemm_fp8_gate_up_dsv3_f32_scales_hbm_bytes.txt",
+                                           FP8_SOURCES),
+    "dsv3_fp8_T8192_d7168_f2048_E256_k8_ue8m0": ("gemm_fp8_gate_up_dsv3_ue8m0_hbm_bytes.txt",
+                                                 FP8_SOURCES),
+}
 
 
 def source_digest(files):
@@ -373,7 +383,7 @@ def measure_other(moe, synth, spec, steps, warmup, weights=None, scale_fmt="f32"
         roof = dict(hbm if t_hbm >= t_mfma else mfma)
         roof["kernel"] = "gemm_fp8_kernel<gate_up> (gate/up grouped GEMM + SwiGLU + h quantisation)"
         roof["other_roof_frac"] = (mfma if t_hbm >= t_mfma else hbm)["frac"]
-        roof["traffic"] = None
+        roof["traffic"] = measured_traffic(*OTHER_TRAFFIC[name]) if name in OTHER_TRAFFIC else None
         r["roofline"] = roof
         r["pct_fp8_peak"] = round(100 * tflops / FP8_PEAK_TFLOPS, 2)
         ideal = max(w_bytes / (HBM_PEAK_GBS * 1e9), spec.active_flops() / (FP8_PEAK_TFLOPS * 1e12))
@@ -384,7 +394,8 @@ def measure_other(moe, synth, spec, steps, warmup, weights=None, scale_fmt="f32"
                          "bound": "mfma", "achieved": r["gate_up_tflops"],
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(r["gate_up_tflops"] / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None}
+                         "traffic": (measured_traffic(*OTHER_TRAFFIC[name])
+                                     if name in OTHER_TRAFFIC else None)}
         r["pct_bf16_peak"] = round(100 * tflops / BF16_PEAK_TFLOPS, 2)
         r["layer_roofline_frac"] = round(
             spec.active_flops() / (BF16_PEAK_TFLOPS * 1e12) / (ms * 1e-3), 4)
