@@ -79,6 +79,10 @@ __device__ __forceinline__ i32x8_t ld16g(const uint8_t* p) {
   return r;
 }
 
+// 2^(b - 127) as fp32 bits (b = 0 is the subnormal 2^-127): an e8m0 byte turned into the fp32 scale
+// it stands for, exactly.
+__device__ __forceinline__ uint32_t e8m0_f32_bits(uint32_t b) { return b ? b << 23 : 0x00400000u; }
+
 // kW4: E2M1 weights with per-32 MX scales (implies kUE). kTG: groups of 16 tokens per pass over
 // the weights (fewer groups hold fewer registers and less LDS, so more waves stream at once).
 // kFused: the fused small-batch path (pairs from the routing ids; h and slots indexed by pair).
@@ -109,6 +113,11 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   // or the e8m0 byte), or for E2M1 the MX bytes of all 64 rows (dynamic, below). Loads of them
   // in the K loop would cost the texture-address unit about as much as the weight stream.
   __shared__ uint32_t wss[4][256];
+  // Where UE8M0 scales are applied: E2M1 weights always pass them to the instruction (the
+  // per-32 weight scales cannot be taken out of a 128-wide block's sum); e4m3 weights with one
+  // token group scale each block's product afterwards, which saves the scale-operand load ahead
+  // of every scaled MFMA and was measured faster with one group, slower with two or four.
+  constexpr bool kScaleInMfma = kW4 || (kUE && kTG > 1);
   extern __shared__ uint32_t wsx[];   // E2M1: [64 rows][KB | 1 dwords]: byte 4c+g = block (c, g)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -161,8 +170,10 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
   } else {
     for (int i = tid; i < 4 * KB; i += 256) {
       const int rg = i / KB, c = i - rg * KB;
-      wss[rg][c] = kUE ? static_cast<uint32_t>(static_cast<const uint8_t*>(ascale[rg])[c])
-                       : __float_as_uint(static_cast<const float*>(ascale[rg])[c]);
+      const uint32_t b = kUE ? static_cast<const uint8_t*>(ascale[rg])[c] : 0u;
+      wss[rg][c] = kScaleInMfma ? b
+                   : kUE ? e8m0_f32_bits(b)
+                   : __float_as_uint(static_cast<const float*>(ascale[rg])[c]);
     }
   }
   __syncthreads();
@@ -206,16 +217,21 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
       for (int tg = 0; tg < kTG; ++tg)
         if (tg < ntg) {
           bv[tg] = ld16x2g(brow[tg] + kb, brow[tg] + kb + 64);
-          if constexpr (kUE) bx[tg] = static_cast<const uint8_t*>(p.a_s)[bscale[tg] + c];
-          else bs[tg] = static_cast<const float*>(p.a_s)[bscale[tg] + c];
+          if constexpr (kScaleInMfma)
+            bx[tg] = static_cast<const uint8_t*>(p.a_s)[bscale[tg] + c];
+          else if constexpr (kUE)
+            bs[tg] = __uint_as_float(e8m0_f32_bits(static_cast<const uint8_t*>(p.a_s)[bscale[tg] + c]));
+          else
+            bs[tg] = static_cast<const float*>(p.a_s)[bscale[tg] + c];
         }
 #pragma unroll
       for (int tg = 0; tg < kTG; ++tg) {
         if (tg >= ntg) continue;
-        if constexpr (kUE) {
-          // the token's e8m0 byte goes to the instruction. Each block's product starts from
-          // zero and is added afterwards: with a token group or two the few accumulators would
-          // otherwise chain every MFMA to the previous K block's.
+        if constexpr (kScaleInMfma) {
+          // the weight byte (each lane's MX byte for E2M1) and the token's e8m0 byte go to the
+          // instruction. Each block's product starts from zero and is added afterwards: with a
+          // token group or two the few accumulators would otherwise chain every MFMA to the
+          // previous K block's.
           const int ex = bx[tg];
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
@@ -224,6 +240,10 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(Fp8DecodeArgs p) {
                 av[rg], bv[tg], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, kW4 ? 4 : 0, 0, 0, ew, 0, ex);
           }
         } else {
+          // one weight scale per 128x128 block and one activation scale per token and block:
+          // the block's product is scaled after the instruction. UE8M0 scales are powers of
+          // two, so while their product stays above 2^-149 this rounds exactly as the
+          // instruction's own scaling would.
 #pragma unroll
           for (int rg = 0; rg < 4; ++rg) {
             const float sc = __uint_as_float(wss[rg][c]) * bs[tg];
