@@ -207,6 +207,34 @@ def kernel_pass(layer, steps):
     return layer.kernel_ms(steps)
 
 
+def vendor_gemm(spec, iters=20):
+    """The vendor library on dense bf16 products with the FLOPs of the layer's two grouped GEMMs
+    (P = T*k rows, gate and up as one 2f-wide weight): context for the grouped kernels, not part
+    of the path."""
+    import torch
+    P, d, f = spec.P, spec.d, spec.f
+    out = {}
+    for name, (M, N, K) in (("gate_up", (P, 2 * f, d)), ("down", (P, d, f))):
+        a = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        w = (torch.randn((N, K), device="cuda") * 0.02).to(torch.bfloat16)
+        for _ in range(3):
+            y = torch.nn.functional.linear(a, w)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            y = torch.nn.functional.linear(a, w)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tf, 1),
+                     "pct_bf16_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2)}
+        log("vendor dense %s %dx%dx%d: %.3f ms, %.1f TFLOP/s" % (name, M, N, K, ms, tf))
+        del a, w, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def host_cpu():
     """Model name, logical CPUs available to this process, and the OpenMP thread setting."""
     model = "unknown"
@@ -510,6 +538,9 @@ def main():
                     help="also time the fp8 / FP4 and fused decode variants, the DeepSeek-V3-shaped "
                          "layer with FP4 experts and the tiny fp32 layer; write every workload's "
                          "figures to this JSON file")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="first time the vendor library (torch.nn.functional.linear, hipBLASLt) on "
+                         "dense bf16 products of the Mixtral-shaped GEMMs' sizes, for context")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain fp32 copy kernel (out = in * 1) over this many MiB, "
                          "3 times, to calibrate HBM byte counters")
@@ -536,6 +567,7 @@ def main():
         log("copy probe: %d MiB read + %d MiB written per launch" % (args.copy_probe_mib,
                                                                     args.copy_probe_mib))
         del src, dst
+    vendor = vendor_gemm(synth.MIXTRAL_PREFILL) if args.vendor_gemm else None
     spec = synth.MIXTRAL_PREFILL
     T, d, f, E, k = spec.T, spec.d, spec.f, spec.E, spec.k
     log("generating %s inputs" % spec.name)
@@ -597,6 +629,8 @@ def main():
                                         GEMM_SOURCES),
         },
     }
+    if vendor is not None:
+        result["vendor_dense_gemm"] = vendor
     del layer
     torch.cuda.empty_cache()
 
