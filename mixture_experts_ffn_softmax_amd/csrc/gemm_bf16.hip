@@ -400,8 +400,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   const int last = st0 + nst - 1;
 
   // DMA addressing: lane l of instruction i of wave w supplies row (IPW w + i) * 8 + l / 8 at
-  // chunk position l % 8. The weight rows need no gathered index, so the first two B stages are
-  // requested before the token rows of the A operand are looked up.
+  // chunk position l % 8.
   Dma<IPW> d;
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
   d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * p.K * 2u);
@@ -412,21 +411,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   for (int i = 0; i < IPW; ++i) {
     const int r = (wave * IPW + i) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int pos = tc.row0 + min(r, tc.rows - 1);
+    const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+    d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
     const int n = MODE == kGateUp ? min(tc.ntile * 128 + (r & 127), p.N - 1)
                                   : min(tc.ntile * kBN + r, p.N - 1);
     d.boff[i] = static_cast<uint32_t>(n) * p.K * 2u + c * 16;
   }
-  dma_b<DW>(b0, d, st0, last, wave);
-  dma_b<DW>(b1, d, st0 + 1, last, wave);
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int r = (wave * IPW + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int pos = tc.row0 + min(r, tc.rows - 1);
-    const int arow = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
-    d.aoff[i] = static_cast<uint32_t>(arow) * p.K * 2u + c * 16;
-  }
-  dma_a<DW>(a0, d, st0, last, wave, tc.rows);
 
   acc_t<ME> acc[MI][NJ];
 #pragma unroll
@@ -436,7 +427,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
 #pragma unroll
       for (int e = 0; e < AccOf<ME>::n; ++e) acc[i][j][e] = 0.0f;
 
-  wait_vmcnt<0>();  // stage 0 (and B of stage 1, requested before it)
+  dma_a<DW>(a0, d, st0, last, wave, tc.rows);
+  dma_b<DW>(b0, d, st0, last, wave);
+  dma_b<DW>(b1, d, st0 + 1, last, wave);
+  wait_vmcnt<IPW>();  // all but this wave's B DMAs of stage 1
   __builtin_amdgcn_s_barrier();
   // Waves whose rows all lie past the tile's valid rows (the short last tile of an expert) skip
   // their fragment reads and MFMAs; the condition is wave-uniform.
