@@ -149,6 +149,62 @@ __device__ __forceinline__ void spread_frag_reads() {
   __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - kPer * (MI + NJ), 0);
 }
 
+// ---- four waves of 128x128 (one wave per SIMD) ------------------------------------------------
+// With one wave per SIMD nothing else feeds the matrix pipe while a wave issues DMA or reads
+// fragments, so one k-step's work is issued as groups: a few MFMAs, one fragment read of the next
+// k-step, and the group's share of the stage's 16 DMA instructions (8 of A, then 8 of B), each
+// group fenced so the compiler keeps the order.
+template <int ME, int MI, int NJ>
+struct Sched4 {
+  static constexpr int kNM = MI * NJ;                 // MFMAs per k-step
+  static constexpr int kNR = MI + NJ;                 // fragment reads per k-step
+  static constexpr int kPer = kNM / kNR;              // MFMAs per group
+  static constexpr int kKS = (kBK / 8) / (ME == 32 ? 2 : 4);   // k-steps per stage
+  static constexpr int kPre = (kKS - 1) * kNR;        // groups before the stage's barrier
+  static_assert(kNM % kNR == 0, "whole groups");
+};
+
+// One k-step: the MFMAs of `cur`, the reads of `nxt` (k-step ks_next of As / Bs), and, with
+// kDma, DMA instructions m whose group (m * kPre / 16) falls in [g0, g0 + kNR).
+template <int MODE, int ME, int MI, int NJ, bool kDma>
+__device__ __forceinline__ void kstep4(acc_t<ME> (&acc)[MI][NJ], const Frag<MI, NJ>& cur,
+                                       Frag<MI, NJ>& nxt, const char* As, const char* Bs,
+                                       int arow0, int bcol0, int ks_next, int lane, int g0,
+                                       const Dma<8>& d, uint32_t abase, uint32_t kba,
+                                       uint32_t bbase, uint32_t kbb, int wave, int rows) {
+  using S4 = Sched4<ME, MI, NJ>;
+  const int ch = (ME == 32 ? 2 : 4) * ks_next + lane / ME;
+#pragma unroll
+  for (int g = 0; g < S4::kNR; ++g) {
+#pragma unroll
+    for (int q = 0; q < S4::kPer; ++q) {
+      const int idx = g * S4::kPer + q;
+      const int i = idx / NJ, j = idx % NJ;
+      if constexpr (ME == 32)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+    }
+    if (g < MI)
+      nxt.a[g] = *reinterpret_cast<const bf16x8_t*>(As + swz(arow0 + g * ME + (lane & (ME - 1)), ch));
+    else
+      nxt.b[g - MI] = *reinterpret_cast<const bf16x8_t*>(
+          Bs + swz(col_base<MODE, ME, NJ>(bcol0, g - MI) + (lane & (ME - 1)), ch));
+    if constexpr (kDma) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        if ((m * S4::kPre) / 16 != g0 + g) continue;
+        if (m < 8) {
+          if ((wave * 8 + m) * 8 < rows) dma16(abase + (wave * 8 + m) * 1024, d.aoff[m], d.ra, kba);
+        } else {
+          dma16(bbase + (wave * 8 + m - 8) * 1024, d.boff[m - 8], wave < 2 ? d.rb0 : d.rb1, kbb);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // DMA of stage `st` of one operand into one buffer. The first DW waves issue all of it: wave
 // w < DW fills rows (IPW w + i) * 8 .. +7 (i < IPW = 32 / DW); waves w >= DW issue none. A rows
 // at or past the tile's valid rows are skipped (their waves skip the MFMAs); B rows 0..127 come
@@ -355,7 +411,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
   // Waves issuing the stage DMA. In the gate/up GEMM only one wave per SIMD does (measured 3 %
   // faster there: the SIMD's other wave keeps the MFMA pipe fed while the DMA wave waits for the
   // texture unit's queue); in the down GEMM all waves share it.
-  constexpr int DW = MODE == kGateUp ? NW / 2 : NW;
+  constexpr int DW = NW == 4 ? NW : (MODE == kGateUp ? NW / 2 : NW);
   constexpr int IPW = 32 / DW;     // DMA instructions per DMA wave per operand per stage
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   // MFMA shape: 16x16x32 for gate/up, 32x32x16 for down (each measured the faster there)
@@ -471,6 +527,48 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
       spread_frag_reads<ME, MI, NJ>();                                               \
     }                                                                                \
   }
+  if constexpr (NW == 4) {
+    // Stage S: k-steps but the last with the DMA of A (S+1) -> AN and B (S+2) -> BN2 spread
+    // through them, then the wait for stage S+1 and the barrier, then the last k-step with the
+    // reads of stage S+1's first k-step. A wave whose rows lie past the tile issues its DMA only.
+    using S4 = Sched4<ME, MI, NJ>;
+#define MOE_STAGE4(AC, BC, AN, BN1, BN2, S)                                                     \
+    {                                                                                          \
+      const int sa = st0 + (S) + 1, sb = st0 + (S) + 2;                                        \
+      const uint32_t kba = sa <= last ? static_cast<uint32_t>(sa) * kBK * 2u : kPastEnd;       \
+      const uint32_t kbb = sb <= last ? static_cast<uint32_t>(sb) * kBK * 2u : kPastEnd;       \
+      const uint32_t abase = lds_offset(AN), bbase = lds_offset(BN2);                          \
+      if (active) {                                                                            \
+        _Pragma("unroll") for (int ks = 0; ks < S4::kKS - 1; ++ks) {                           \
+          if (ks % 2 == 0)                                                                     \
+            kstep4<MODE, ME, MI, NJ, true>(acc, fa, fb, AC, BC, arow0, bcol0, ks + 1, lane,    \
+                                           ks * S4::kNR, d, abase, kba, bbase, kbb, wave,      \
+                                           tc.rows);                                           \
+          else                                                                                 \
+            kstep4<MODE, ME, MI, NJ, true>(acc, fb, fa, AC, BC, arow0, bcol0, ks + 1, lane,    \
+                                           ks * S4::kNR, d, abase, kba, bbase, kbb, wave,      \
+                                           tc.rows);                                           \
+        }                                                                                      \
+      } else {                                                                                 \
+        dma_a<DW>(AN, d, sa, last, wave, tc.rows);                                             \
+        dma_b<DW>(BN2, d, sb, last, wave);                                                     \
+      }                                                                                        \
+      wait_vmcnt_lgkm0<IPW>();                                                                 \
+      __builtin_amdgcn_s_barrier();                                                            \
+      if (active)                                                                              \
+        kstep4<MODE, ME, MI, NJ, false>(acc, fb, fa, AN, BN1, arow0, bcol0, 0, lane, 0, d,     \
+                                        0u, 0u, 0u, 0u, wave, tc.rows);                        \
+    }
+    for (int s = 0; s < nst; s += 6) {
+      MOE_STAGE4(a0, b0, a1, b1, b2, s)
+      if (s + 1 < nst) MOE_STAGE4(a1, b1, a0, b2, b0, s + 1)
+      if (s + 2 < nst) MOE_STAGE4(a0, b2, a1, b0, b1, s + 2)
+      if (s + 3 < nst) MOE_STAGE4(a1, b0, a0, b1, b2, s + 3)
+      if (s + 4 < nst) MOE_STAGE4(a0, b1, a1, b2, b0, s + 4)
+      if (s + 5 < nst) MOE_STAGE4(a1, b2, a0, b0, b1, s + 5)
+    }
+#undef MOE_STAGE4
+  } else {
   // buffers of stage s: A a[s % 2], B b[s % 3]; the pattern repeats every 6 stages
   for (int s = 0; s < nst; s += 6) {
     MOE_STAGE(a0, b0, a1, b1, b2, s)
@@ -479,6 +577,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(Bf16GemmArgs p)
     if (s + 3 < nst) MOE_STAGE(a1, b0, a0, b1, b2, s + 3)
     if (s + 4 < nst) MOE_STAGE(a0, b1, a1, b2, b0, s + 4)
     if (s + 5 < nst) MOE_STAGE(a1, b2, a0, b0, b1, s + 5)
+  }
   }
 #undef MOE_STAGE
   wait_vmcnt<0>();  // the past-the-end prefetches (no memory traffic)
@@ -594,6 +693,9 @@ int bf16_tile_rows_down() { return kBM; }
 #ifndef MOE_BF16_WAVES
 #define MOE_BF16_WAVES 4, 2
 #endif
+#ifndef MOE_BF16_DOWN4_MIN_K
+#define MOE_BF16_DOWN4_MIN_K 8192
+#endif
 
 // The GEMM, then (when tail tiles may be cut) the fix-up of the cut tiles.
 template <int MODE, int WM, int WN>
@@ -654,8 +756,9 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream) {
   dn.max_split =
       L.split_partial && may_cut(P, (L.d + kBN - 1) / kBN, L.cpx) ? max_split_for(L.f) : 1;
   dn.partial = L.split_partial;
-  return launch_gemm<kDown, MOE_BF16_WAVES>(
-      dn, work_grid(max_tiles(P, L.E, (L.d + kBN - 1) / kBN), L.cpx), stream);
+  const unsigned grid2 = work_grid(max_tiles(P, L.E, (L.d + kBN - 1) / kBN), L.cpx);
+  if (L.f >= MOE_BF16_DOWN4_MIN_K) return launch_gemm<kDown, 2, 2>(dn, grid2, stream);
+  return launch_gemm<kDown, MOE_BF16_WAVES>(dn, grid2, stream);
 }
 
 }  // namespace moe

@@ -97,6 +97,13 @@ SMALL_BF16 = [
     # a single token: one row per selected expert, every other expert empty
     synth.TINY_F32.with_(name="bf16_one_T1_d256_f256_E8_k2", dtype="bf16", T=1, d=256, f=256,
                          E=8, k=2),
+    # down projections with K = f >= 8192 run on four waves of 128x128: experts of ~120 rows
+    # (the waves of the tile's second half hold no rows) and of 350 rows (a full and a ragged
+    # row tile)
+    synth.TINY_F32.with_(name="bf16_down4w_T300_d256_f8192_E5_k2", dtype="bf16", T=300, d=256,
+                         f=8192, E=5, k=2),
+    synth.TINY_F32.with_(name="bf16_down4w_T700_d256_f8192_E2_k1", dtype="bf16", T=700, d=256,
+                         f=8192, E=2, k=1),
 ]
 
 
@@ -119,6 +126,8 @@ CUT_TAIL = [
                          f=4096, E=2, k=2),
     synth.TINY_F32.with_(name="bf16_cut_both_T700_d1024_f2048_E4_k2", dtype="bf16", T=700,
                          d=1024, f=2048, E=4, k=2),
+    synth.TINY_F32.with_(name="bf16_cut_down4w_T200_d512_f8192_E2_k2", dtype="bf16", T=200,
+                         d=512, f=8192, E=2, k=2),
 ]
 
 
