@@ -1,4 +1,4 @@
-// bf16 grouped GEMMs on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// bf16 grouped GEMMs on the gfx950 matrix cores (fp32 accumulation).
 //
 // Gate/up projection fused with SwiGLU, then the down projection with the unpermute / routing
 // weight epilogue (Transformers "Experts backends" page, backends table rows grouped_mm,
@@ -6,13 +6,15 @@
 // SwiGLU). The rows of both GEMMs are the expert-sorted pairs; the gate/up GEMM reads each pair's
 // token row straight from x (gather on load), so no permuted copy of x is needed.
 //
-// Tiling: 256 x 256 output tile per workgroup of 8 waves (2 per SIMD); WM x WN waves each own a
-// (256/WM) x (256/WN) block of 32x32 MFMA tiles. K is staged 64 at a time through two LDS
-// buffers that buffer_load ... lds (global -> LDS DMA, no staging registers) fills one stage
-// ahead; one vmcnt wait and one barrier per stage. For the gate/up GEMM the 256 B-rows of
-// a tile are 128 gate rows and the same 128 up rows; each wave holds matching gate and up
-// accumulators and applies SwiGLU in registers. Results leave through LDS as whole 16-byte row
-// segments.
+// Tiling: 256 x 256 output tile per workgroup. Eight waves (two per SIMD) each own a 64 x 128
+// block (gate/up: v_mfma_f32_16x16x32_bf16; down: v_mfma_f32_32x32x16_bf16); a down GEMM with a
+// long K instead runs four waves (one per SIMD) of 128 x 128 whose k-steps interleave MFMAs,
+// fragment reads and DMA in fenced groups. K is staged 64 at a time through 160 KB of LDS (two A
+// and three B buffers) that buffer_load ... lds (global -> LDS DMA, no staging registers) fills,
+// A one stage and B two stages ahead; one vmcnt wait and one barrier per stage. For the gate/up
+// GEMM the 256 B-rows of a tile are 128 gate rows and the same 128 up rows; each wave holds
+// matching gate and up accumulators and applies SwiGLU in registers. Results leave through LDS
+// as whole 16-byte row segments.
 #include <algorithm>
 
 #include "common.h"
@@ -689,7 +691,8 @@ inline bool may_cut(int P, int NT, int cpx) {
 int bf16_tile_rows_gateup() { return kBM; }
 int bf16_tile_rows_down() { return kBM; }
 
-// Wave layout of both GEMMs: WM x WN waves (8 in total), each owning (256/WM) x (256/WN).
+// Wave layout: WM x WN waves, each owning (256/WM) x (256/WN); the gate/up GEMM and short-K down
+// GEMMs take 4 x 2, down GEMMs with K >= MOE_BF16_DOWN4_MIN_K take 2 x 2 (measured faster there).
 #ifndef MOE_BF16_WAVES
 #define MOE_BF16_WAVES 4, 2
 #endif
