@@ -116,6 +116,29 @@ def test_small_bf16_layers(spec):
         _check_layer(spec, inp, res, 2e-2)
 
 
+# bf16 layers with fp32 expert outputs (y_dtype f32): the down epilogue's fp32 passes, on the
+# eight-wave kernel and on the four-wave one (K = f >= 8192)
+FP32_OUT = [
+    synth.TINY_F32.with_(name="bf16_f32out_T300_d256_f1024_E5_k2", dtype="bf16", T=300, d=256,
+                         f=1024, E=5, k=2),
+    synth.TINY_F32.with_(name="bf16_f32out_T300_d256_f8192_E5_k2", dtype="bf16", T=300, d=256,
+                         f=8192, E=5, k=2),
+]
+
+
+@pytest.mark.parametrize("spec", FP32_OUT, ids=lambda s: s.name)
+def test_bf16_layers_fp32_outputs(spec):
+    inp = layer_inputs(spec)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    for layout in ("slots", "permuted"):
+        log(spec.name, layout, "fp32 y")
+        res = moe.moe_layer(dev["x"], dev["Wgate"], dev["Wup"], dev["Wdown"], spec.k,
+                            logits=dev.get("logits"), y_layout=layout, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert res.out.dtype == torch.float32
+        _check_layer(spec, inp, res, 2e-2)
+
+
 # Shapes whose last round of tiles is cut along K (few tiles per XCD, long K): gate/up cut 8 ways,
 # down cut 8 ways, and both GEMMs cut (2 and 4 ways). A fix-up kernel sums each cut tile's pieces
 # in piece order, so repeated runs must agree bit for bit.
