@@ -692,12 +692,12 @@ int bf16_tile_rows_gateup() { return kBM; }
 int bf16_tile_rows_down() { return kBM; }
 
 // Wave layout: WM x WN waves, each owning (256/WM) x (256/WN); the gate/up GEMM and short-K down
-// GEMMs take 4 x 2, down GEMMs with K >= MOE_BF16_DOWN4_MIN_K take 2 x 2 (measured faster there).
+// GEMMs take 4 x 2, down GEMMs with K >= MOE_BF16_DOWN4_MIN_K (4096) take 2 x 2 (measured faster there).
 #ifndef MOE_BF16_WAVES
 #define MOE_BF16_WAVES 4, 2
 #endif
 #ifndef MOE_BF16_DOWN4_MIN_K
-#define MOE_BF16_DOWN4_MIN_K 8192
+#define MOE_BF16_DOWN4_MIN_K 4096
 #endif
 
 // The GEMM, then (when tail tiles may be cut) the fix-up of the cut tiles.

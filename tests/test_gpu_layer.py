@@ -97,7 +97,7 @@ SMALL_BF16 = [
     # a single token: one row per selected expert, every other expert empty
     synth.TINY_F32.with_(name="bf16_one_T1_d256_f256_E8_k2", dtype="bf16", T=1, d=256, f=256,
                          E=8, k=2),
-    # down projections with K = f >= 8192 run on four waves of 128x128: experts of ~120 rows
+    # down projections with K = f >= 4096 run on four waves of 128x128: experts of ~120 rows
     # (the waves of the tile's second half hold no rows) and of 350 rows (a full and a ragged
     # row tile)
     synth.TINY_F32.with_(name="bf16_down4w_T300_d256_f8192_E5_k2", dtype="bf16", T=300, d=256,
