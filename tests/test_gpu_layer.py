@@ -117,7 +117,7 @@ def test_small_bf16_layers(spec):
 
 
 # bf16 layers with fp32 expert outputs (y_dtype f32): the down epilogue's fp32 passes, on the
-# eight-wave kernel and on the four-wave one (K = f >= 8192)
+# eight-wave kernel and on the four-wave one (K = f >= 4096)
 FP32_OUT = [
     synth.TINY_F32.with_(name="bf16_f32out_T300_d256_f1024_E5_k2", dtype="bf16", T=300, d=256,
                          f=1024, E=5, k=2),
