@@ -232,6 +232,35 @@ def test_decode_mixed_small_and_large_experts():
         _check_layer(spec, inp, res, 2e-2)
 
 
+def test_decode_streaming_limit_and_fp32_outputs():
+    # Routing built so that expert 0 gets exactly 16 tokens (the most the streaming kernels take)
+    # and expert 1 gets 17 (the K-split kernels), the others 5-6 each; bf16 and fp32 expert
+    # outputs in every layout the down kernels store.
+    spec = synth.TINY_F32.with_(name="bf16_decode_limit_T33_d256_f512_E8_k2", dtype="bf16", T=33,
+                                d=256, f=512, E=8, k=2)
+    _assert_small_batch(spec)
+    inp = layer_inputs(spec)
+    lg = np.random.default_rng(7).normal(0.0, 0.1, (spec.T, spec.E)).astype(np.float32)
+    for t in range(spec.T):
+        lg[t, 0 if t < 16 else 1] += 10.0
+        lg[t, 2 + t % 6] += 9.0
+    inp["logits"] = lg
+    ids, _ = oracle.route(lg, spec.k)
+    counts = np.bincount(ids.reshape(-1), minlength=spec.E)
+    assert counts[0] == 16 and counts[1] == 17, counts
+    for layout in ("slots", "permuted", "acc_f32"):
+        log(spec.name, layout, counts.tolist())
+        _check_layer(spec, inp, _run_gpu(spec, inp, layout), 2e-2)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    for layout in ("slots", "permuted"):
+        log(spec.name, layout, "fp32 y")
+        res = moe.moe_layer(dev["x"], dev["Wgate"], dev["Wup"], dev["Wdown"], spec.k,
+                            logits=dev["logits"], y_layout=layout, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert res.out.dtype == torch.float32
+        _check_layer(spec, inp, res, 2e-2)
+
+
 @pytest.mark.parametrize("T,want", [(48, 1), (49, 0)])
 def test_small_batch_switch_boundary(T, want):
     # the last batch of the small-batch kernels (12 rows per expert) and the first of the tiled
