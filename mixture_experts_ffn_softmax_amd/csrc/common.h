@@ -292,12 +292,12 @@ __device__ __forceinline__ bool map_cut_tile(const int32_t* __restrict__ tile_cu
 // ---- helpers of the fused small-batch path ----------------------------------------------------
 
 // The pairs (flat index t * k + j) routed to expert e, in ascending order, found by one workgroup
-// of NT threads in ids[0 .. P): the first CAP of them written to list (LDS), their number M
-// returned to every thread. wsum: LDS scratch of NT / 64 ints. Ends with a barrier, so list is
-// ready for the whole group.
+// of NT threads in ids[0 .. P): those of rank skip .. skip + CAP - 1 written to list (LDS), their
+// total number M returned to every thread. wsum: LDS scratch of NT / 64 ints. Ends with a
+// barrier, so list is ready for the whole group.
 template <int NT, int CAP>
 __device__ int expert_pair_list(const int32_t* __restrict__ ids, int P, int e, int32_t* list,
-                                int* wsum) {
+                                int* wsum, int skip = 0) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
   int total = 0;
   for (int base = 0; base < P; base += NT) {
@@ -313,7 +313,7 @@ __device__ int expert_pair_list(const int32_t* __restrict__ ids, int P, int e, i
       tot += wsum[v];
     }
     const int at = off + __popcll(m & ((1ull << lane) - 1ull));
-    if (hit && at < CAP) list[at] = i;
+    if (hit && at >= skip && at < skip + CAP) list[at - skip] = i;
     total += tot;
     __syncthreads();
   }

@@ -49,6 +49,7 @@ struct DecodeArgs {
   const float* topk_w;
   int small_max;              // experts with at most this many tokens belong to the streaming
                               // kernel (0: this kernel takes every expert)
+  int stream_max;             // the streaming kernels take experts with 1 .. stream_max tokens
   // fused small-batch path (see ExpertsLaunch): routing ids [P]
   const int32_t* ids;
   int P;
@@ -245,33 +246,21 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   const int nrb = (p.N + kOut - 1) / kOut;
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
-  // Exactly 32 KB, so that five workgroups fit a CU. On the fused path the expert's first 16
-  // pairs (experts with more belong to the K-split kernel) are gathered in the first slot before
-  // any DMA lands there.
+  // Exactly 32 KB, so that five workgroups fit a CU. On the fused path the pass's 16 pairs are
+  // gathered in the first slot before any DMA lands there.
   __shared__ __attribute__((aligned(1024))) char ring[kStrRing * kStage];
+  int32_t* plist = reinterpret_cast<int32_t*>(ring);
   const int lane = threadIdx.x;
   const int r16 = lane & 15, g = lane >> 4;
   int row0, M;
   if constexpr (kFused) {
-    int32_t* plist = reinterpret_cast<int32_t*>(ring);
     row0 = 0;
     M = expert_pair_list<64, 16>(p.ids, p.P, e, plist, plist + 16);
   } else {
     row0 = p.offsets[e];
     M = p.offsets[e + 1] - row0;
   }
-  if (M == 0 || M > 16) return;
-  // token r16's pair (its h row on the fused path) and the row of x it reads
-  const int t = min(r16, M - 1);
-  int pos, src;
-  if constexpr (kFused) {
-    pos = reinterpret_cast<const int32_t*>(ring)[t];
-    src = p.a_gather ? pos / p.k : pos;
-    __syncthreads();   // the list is read before the ring is refilled
-  } else {
-    pos = row0 + t;
-    src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
-  }
+  if (M == 0 || M > p.stream_max) return;
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
   const uint32_t wbytes = static_cast<uint32_t>(p.N) * p.K * 2u;
   const i32x4_t rs0 = make_rsrc(p.w0 + e * wstride, wbytes);
@@ -286,10 +275,24 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
     const int c = (lane % kCpr) ^ (r % kCpr);
     voff[i] = static_cast<uint32_t>(min(n, p.N - 1)) * p.K * 2u + c * 16;
   }
+  const int nst = p.K / KS;
+  // passes of 16 tokens (one unless the expert has more)
+  for (int tc0 = 0; tc0 < M; tc0 += 16) {
+  const int mp = min(16, M - tc0);
+  // token r16's pair (its h row on the fused path) and the row of x it reads
+  const int t = min(r16, mp - 1);
+  int pos, src;
+  if constexpr (kFused) {
+    if (tc0 > 0) expert_pair_list<64, 16>(p.ids, p.P, e, plist, plist + 16, tc0);
+    pos = plist[t];
+    src = p.a_gather ? pos / p.k : pos;
+    __syncthreads();   // the list is read before the ring is refilled
+  } else {
+    pos = row0 + tc0 + t;
+    src = p.a_gather ? p.sorted_pair[pos] / p.k : pos;
+  }
   // token operand: lane (t = l % 16, g = l / 16) holds k = 32 u + 8 g .. +7 of token t
   const uint16_t* trow = p.a + static_cast<size_t>(src) * p.K + g * 8;
-
-  const int nst = p.K / KS;
   u32x4_t tok[kStrRing][kNi];
   auto load_tok = [&](u32x4_t (&tv)[kNi], int st) {
     const int kb = min(st, nst - 1) * KS;
@@ -334,15 +337,16 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   f32x4_t up;
 #pragma unroll
   for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32, 64);
-  if (r16 >= M || g >= 2) return;
   const int n = rb * 8 + 4 * g;
-  if (n >= p.N) return;
-  u32x2_t o;
-  o[0] = f32_to_bf16_bits(silu_mul(acc[0], up[0])) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[1], up[1]))) << 16);
-  o[1] = f32_to_bf16_bits(silu_mul(acc[2], up[2])) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[3], up[3]))) << 16);
-  *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(pos) * p.N + n) = o;   // r16 < M: t == r16
+  if (r16 < mp && g < 2 && n < p.N) {   // r16 < mp: t == r16
+    u32x2_t o;
+    o[0] = f32_to_bf16_bits(silu_mul(acc[0], up[0])) |
+           (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[1], up[1]))) << 16);
+    o[1] = f32_to_bf16_bits(silu_mul(acc[2], up[2])) |
+           (static_cast<uint32_t>(f32_to_bf16_bits(silu_mul(acc[3], up[3]))) << 16);
+    *reinterpret_cast<u32x2_t*>(p.h + static_cast<size_t>(pos) * p.N + n) = o;
+  }
+  }  // passes
 }
 
 
@@ -371,39 +375,22 @@ __global__ __launch_bounds__(64) void decode_stream_down_kernel(DecodeArgs p) {
   const int nrb = p.N / kSdRows;                 // N = d, a multiple of 128 on this path
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
-  // 36 KB, so that four workgroups fit a CU. On the fused path the expert's pairs are gathered
+  // 36 KB, so that four workgroups fit a CU. On the fused path the pass's 16 pairs are gathered
   // in the first slot before any DMA lands there.
   __shared__ __attribute__((aligned(1024))) char ring[kSdRing * kSdSlot];
+  int32_t* plist = reinterpret_cast<int32_t*>(ring);
   const int lane = threadIdx.x;
   const int r16 = lane & 15, g = lane >> 4;
   int row0, M;
   if constexpr (kFused) {
-    int32_t* plist = reinterpret_cast<int32_t*>(ring);
     row0 = 0;
     M = expert_pair_list<64, 16>(p.ids, p.P, e, plist, plist + 16);
   } else {
     row0 = p.offsets[e];
     M = p.offsets[e + 1] - row0;
   }
-  if (M == 0 || M > 16) return;
-  // h row of token t: its pair on the fused path, its sorted position otherwise
-  auto hrow_of = [&](int t) {
-    return kFused ? reinterpret_cast<const int32_t*>(ring)[t] : row0 + t;
-  };
-  // Token DMA: instruction j brings token rows 4 j .. 4 j + 3 of the slot (lane l: row
-  // tr = 4 j + l / 16, filled from token min(tr, M - 1)), logical chunk (l % 16) ^ tr.
+  if (M == 0 || M > p.stream_max) return;
   const uint32_t row_bytes = static_cast<uint32_t>(p.K) * 2u;
-  uint32_t toff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tr = 4 * j + lane / 16;
-    toff[j] = static_cast<uint32_t>(hrow_of(min(tr, M - 1))) * row_bytes +
-              static_cast<uint32_t>(((lane & 15) ^ tr) << 4);
-  }
-  const int my_row = hrow_of(min(r16, M - 1));
-  if constexpr (kFused) __syncthreads();   // the list is read before the ring is refilled
-  const int pair = kFused ? my_row : p.sorted_pair[my_row];
-
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
   const i32x4_t rw = make_rsrc(p.w0 + e * wstride, static_cast<uint32_t>(wstride * 2u));
   const i32x4_t rh = make_rsrc(p.a, static_cast<uint32_t>(p.P) * row_bytes);
@@ -417,6 +404,24 @@ __global__ __launch_bounds__(64) void decode_stream_down_kernel(DecodeArgs p) {
               static_cast<uint32_t>(((lane & 15) ^ (r & 15)) << 4);
   }
   const int nst = p.K / kSdKS;
+  // passes of 16 tokens (one unless the expert has more)
+  for (int tc0 = 0; tc0 < M; tc0 += 16) {
+  const int mp = min(16, M - tc0);
+  if (kFused && tc0 > 0) expert_pair_list<64, 16>(p.ids, p.P, e, plist, plist + 16, tc0);
+  // h row of the pass's token t: its pair on the fused path, its sorted position otherwise
+  auto hrow_of = [&](int t) { return kFused ? plist[t] : row0 + tc0 + t; };
+  // Token DMA: instruction j brings token rows 4 j .. 4 j + 3 of the slot (lane l: row
+  // tr = 4 j + l / 16, filled from token min(tr, mp - 1)), logical chunk (l % 16) ^ tr.
+  uint32_t toff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tr = 4 * j + lane / 16;
+    toff[j] = static_cast<uint32_t>(hrow_of(min(tr, mp - 1))) * row_bytes +
+              static_cast<uint32_t>(((lane & 15) ^ tr) << 4);
+  }
+  const int my_row = hrow_of(min(r16, mp - 1));
+  if constexpr (kFused) __syncthreads();   // the list is read before the ring is refilled
+  const int pair = kFused ? my_row : p.sorted_pair[my_row];
   auto issue = [&](int q, int st) {
     const uint32_t kb = static_cast<uint32_t>(min(st, nst - 1)) * kSdKS * 2u;
     const uint32_t base = lds_offset(ring + q * kSdSlot);
@@ -455,14 +460,22 @@ __global__ __launch_bounds__(64) void decode_stream_down_kernel(DecodeArgs p) {
   wait_vmcnt<0>();  // the clamped re-reads past the last stage
 
   // lane l holds token l % 16 and weight rows 4 (l / 16) + i of each 16-row group
-  if (r16 >= M) return;
-  store_down(p, my_row, pair, n0 + 4 * g, acc0);
-  store_down(p, my_row, pair, n0 + 16 + 4 * g, acc1);
+  if (r16 < mp) {
+    store_down(p, my_row, pair, n0 + 4 * g, acc0);
+    store_down(p, my_row, pair, n0 + 16 + 4 * g, acc1);
+  }
+  }  // passes
 }
 
 }  // namespace
 
 constexpr int kStrK = 256;  // K per stage of the streaming kernel
+// Batches of at most this many tokens give no expert more than this many pairs when each token's
+// k experts are distinct (the router's are): the streaming kernels then take every expert, in
+// one or two passes of 16 tokens, and the K-split kernels are not launched (each launch costs
+// ~4 us even when all its workgroups exit at once). Experts with more pairs stay correct, in more
+// passes.
+constexpr int kStreamAllTokens = 32;
 
 
 hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream) {
@@ -484,7 +497,9 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   const unsigned grid1 = static_cast<unsigned>(L.E) * ((L.f + kDecodeGateRows - 1) / kDecodeGateRows);
   // the streaming kernel needs whole K stages
   const bool stream_small = L.d % kStrK == 0;
+  const bool gu_all = stream_small && L.T <= kStreamAllTokens;
   g.small_max = stream_small ? 16 : 0;
+  g.stream_max = gu_all ? P : 16;
   const unsigned grid1s = static_cast<unsigned>(L.E) * ((L.f + 7) / 8);
   if (L.run_gate_up && stream_small) {
     if (fused)
@@ -493,7 +508,7 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
       hipLaunchKernelGGL((decode_stream_kernel<kStrK, false>), dim3(grid1s), dim3(64), 0, stream,
                          g);
   }
-  if (L.run_gate_up) {
+  if (L.run_gate_up && !gu_all) {
     if (fused)
       hipLaunchKernelGGL((decode_bf16_kernel<kGateUp, true>), dim3(grid1), dim3(256), 0, stream, g);
     else
@@ -518,7 +533,9 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
   const unsigned grid2 = static_cast<unsigned>(L.E) * ((L.d + kDecodeDownRows - 1) / kDecodeDownRows);
   // the streaming kernel needs whole K stages and whole 32-row panels
   const bool stream_down = L.f % kSdKS == 0 && L.d % kSdRows == 0;
+  const bool dn_all = stream_down && L.T <= kStreamAllTokens;
   dn.small_max = stream_down ? 16 : 0;
+  dn.stream_max = dn_all ? P : 16;
   dn.ids = L.pair_ids;
   dn.P = P;
   if (stream_down) {
@@ -529,6 +546,7 @@ hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream
       hipLaunchKernelGGL((decode_stream_down_kernel<false>), dim3(grid2s), dim3(64), 0, stream,
                          dn);
   }
+  if (dn_all) return hipGetLastError();
   if (fused)
     hipLaunchKernelGGL((decode_bf16_kernel<kDown, true>), dim3(grid2), dim3(256), 0, stream, dn);
   else

@@ -35,7 +35,11 @@ __device__ __forceinline__ void load_x8<uint16_t>(const uint16_t* p, float (&v)[
 
 // Router logits of one token with a block of 256 threads: thread j covers x[i .. i+8) for
 // i = 8 j + 2048 n against 8 experts at a time; the 8 sums are reduced over each wave and then over
-// the 4 waves in wave order, and logits[e] (global memory or LDS) gets expert e's sum.
+// the 4 waves in wave order, and logits[e] (global memory or LDS) gets expert e's sum. Two 2048-wide
+// chunks go per iteration with all their loads issued before the first product (rows past the
+// last expert read the last expert's row and are dropped), so a token waits on one memory round
+// trip per 4096 channels instead of one per expert and chunk; each sum still takes its products in
+// ascending i.
 template <typename XT>
 __device__ void token_logits(const XT* __restrict__ x, const float* __restrict__ wr, int d, int E,
                              float* logits, float (*red)[kVecExperts]) {
@@ -43,20 +47,40 @@ __device__ void token_logits(const XT* __restrict__ x, const float* __restrict__
   const int wave = threadIdx.x / kWave;
   for (int e0 = 0; e0 < E; e0 += kVecExperts) {
     float acc[kVecExperts];
+    const float* wrow[kVecExperts];
 #pragma unroll
-    for (int b = 0; b < kVecExperts; ++b) acc[b] = 0.0f;
-    for (int i = threadIdx.x * 8; i < d; i += 256 * 8) {
-      float xv[8];
-      load_x8<XT>(x + i, xv);
+    for (int b = 0; b < kVecExperts; ++b) {
+      acc[b] = 0.0f;
+      wrow[b] = wr + static_cast<size_t>(min(e0 + b, E - 1)) * d;
+    }
+    int i = threadIdx.x * 8;
+    for (; i + 256 * 8 < d; i += 2 * 256 * 8) {   // both chunks: loads, fence, products
+      float xv[2][8], wv[2][kVecExperts][8];
+      load_x8<XT>(x + i, xv[0]);
+      load_x8<XT>(x + i + 256 * 8, xv[1]);
 #pragma unroll
       for (int b = 0; b < kVecExperts; ++b) {
-        if (e0 + b < E) {
-          float wv[8];
-          load_x8<float>(wr + static_cast<size_t>(e0 + b) * d + i, wv);
-#pragma unroll
-          for (int c = 0; c < 8; ++c) acc[b] = fmaf(xv[c], wv[c], acc[b]);
-        }
+        load_x8<float>(wrow[b] + i, wv[0][b]);
+        load_x8<float>(wrow[b] + i + 256 * 8, wv[1][b]);
       }
+      __builtin_amdgcn_sched_barrier(0);   // every load issued before the first product
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < kVecExperts; ++b)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) acc[b] = fmaf(xv[h][c], wv[h][b][c], acc[b]);
+    }
+    if (i < d) {   // a last single chunk
+      float xv[8], wv[kVecExperts][8];
+      load_x8<XT>(x + i, xv);
+#pragma unroll
+      for (int b = 0; b < kVecExperts; ++b) load_x8<float>(wrow[b] + i, wv[b]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < kVecExperts; ++b)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[b] = fmaf(xv[c], wv[b][c], acc[b]);
     }
 #pragma unroll
     for (int b = 0; b < kVecExperts; ++b) {

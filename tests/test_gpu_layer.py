@@ -261,6 +261,52 @@ def test_decode_streaming_limit_and_fp32_outputs():
         _check_layer(spec, inp, res, 2e-2)
 
 
+def test_decode_two_token_passes():
+    # At most 32 tokens: the streaming kernels take every expert (the K-split kernels are not
+    # launched), expert 0 with 20 pairs in two passes (16 + 4), expert 1 with 12 in one.
+    spec = synth.TINY_F32.with_(name="bf16_decode_passes_T32_d256_f512_E8_k2", dtype="bf16",
+                                T=32, d=256, f=512, E=8, k=2)
+    _assert_small_batch(spec)
+    inp = layer_inputs(spec)
+    lg = np.random.default_rng(11).normal(0.0, 0.1, (spec.T, spec.E)).astype(np.float32)
+    for t in range(spec.T):
+        lg[t, 0 if t < 20 else 1] += 10.0
+        lg[t, 2 + t % 6] += 9.0
+    inp["logits"] = lg
+    ids, _ = oracle.route(lg, spec.k)
+    counts = np.bincount(ids.reshape(-1), minlength=spec.E)
+    assert counts[0] == 20 and counts[1] == 12, counts
+    for layout in ("slots", "permuted", "acc_f32"):
+        log(spec.name, layout, counts.tolist())
+        _check_layer(spec, inp, _run_gpu(spec, inp, layout), 2e-2)
+
+
+def test_decode_repeated_expert_ids():
+    # Routing ids that name one expert twice for a token (not what the router makes, but what the
+    # permutation accepts): with 24 tokens expert 0 gets 44 pairs, three passes of the streaming
+    # kernels; checked against the oracle's per-token sum over the given ids and weights.
+    spec = synth.TINY_F32.with_(name="bf16_decode_repeat_T24_d256_f512_E4_k2", dtype="bf16",
+                                T=24, d=256, f=512, E=4, k=2)
+    _assert_small_batch(spec)
+    inp = layer_inputs(spec)
+    ids = np.zeros((spec.T, spec.k), dtype=np.int32)
+    ids[20:, 1] = 1
+    w = np.random.default_rng(5).uniform(0.2, 0.8, (spec.T, spec.k)).astype(np.float32)
+    assert np.bincount(ids.reshape(-1), minlength=spec.E).tolist() == [44, 4, 0, 0]
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    ids_d, w_d = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    perm = moe.moe_permute(ids_d, spec.E)
+    ex = oracle.Experts(inp["Wgate"], inp["Wup"], inp["Wdown"])
+    ref = oracle.moe_forward(inp["x"], ex, ids, w)
+    for layout in ("slots", "permuted"):
+        y = moe.moe_experts_forward(dev["x"], dev["Wgate"], dev["Wup"], dev["Wdown"], perm.offsets,
+                                    perm.sorted_pair, w_d, spec.k, y_layout=layout)
+        out = moe.moe_combine(y, layout, spec.T, spec.k, spec.d, pair_pos=perm.pair_pos,
+                              topk_w=w_d, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert_close_rel_max(out_to_f64(out), ref, 2e-2, "%s %s" % (spec.name, layout))
+
+
 @pytest.mark.parametrize("T,want", [(48, 1), (49, 0)])
 def test_small_batch_switch_boundary(T, want):
     # the last batch of the small-batch kernels (12 rows per expert) and the first of the tiled
