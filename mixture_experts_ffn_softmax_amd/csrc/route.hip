@@ -115,32 +115,32 @@ __global__ __launch_bounds__(256) void router_logits_vec_kernel(const XT* __rest
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int t0 = blockIdx.x * kVecTokens;
+  // Tokens past T and experts past E read the last token's or expert's row; their sums are
+  // dropped. All of a chunk's loads are issued before its first product (one memory round trip
+  // per 2048 channels); each sum takes its products in ascending channel order.
+  const XT* xrow[kVecTokens];
+#pragma unroll
+  for (int a = 0; a < kVecTokens; ++a) xrow[a] = x + static_cast<size_t>(min(t0 + a, T - 1)) * d;
   for (int e0 = 0; e0 < E; e0 += kVecExperts) {
     float acc[64];
 #pragma unroll
     for (int q = 0; q < 64; ++q) acc[q] = 0.0f;
+    const float* wrow[kVecExperts];
+#pragma unroll
+    for (int b = 0; b < kVecExperts; ++b) wrow[b] = wr + static_cast<size_t>(min(e0 + b, E - 1)) * d;
     for (int i = (wave * kWave + lane) * 8; i < d; i += 4 * kWave * 8) {
-      float xv[kVecTokens][8];
+      float xv[kVecTokens][8], wv[kVecExperts][8];
 #pragma unroll
-      for (int a = 0; a < kVecTokens; ++a) {
-        if (t0 + a < T) {
-          load_x8<XT>(x + static_cast<size_t>(t0 + a) * d + i, xv[a]);
-        } else {
+      for (int a = 0; a < kVecTokens; ++a) load_x8<XT>(xrow[a] + i, xv[a]);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) xv[a][c] = 0.0f;
-        }
-      }
+      for (int b = 0; b < kVecExperts; ++b) load_x8<float>(wrow[b] + i, wv[b]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < kVecExperts; ++b) {
-        if (e0 + b < E) {
-          float wv[8];
-          load_x8<float>(wr + static_cast<size_t>(e0 + b) * d + i, wv);
+      for (int b = 0; b < kVecExperts; ++b)
 #pragma unroll
-          for (int a = 0; a < kVecTokens; ++a)
+        for (int a = 0; a < kVecTokens; ++a)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[a * 8 + b] = fmaf(xv[a][c], wv[c], acc[a * 8 + b]);
-        }
-      }
+          for (int c = 0; c < 8; ++c) acc[a * 8 + b] = fmaf(xv[a][c], wv[b][c], acc[a * 8 + b]);
     }
     red[wave][lane] = wave_reduce_scatter64(acc, lane);
     __syncthreads();
