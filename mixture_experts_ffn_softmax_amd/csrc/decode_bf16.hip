@@ -294,10 +294,16 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   // token operand: lane (t = l % 16, g = l / 16) holds k = 32 u + 8 g .. +7 of token t
   const uint16_t* trow = p.a + static_cast<size_t>(src) * p.K + g * 8;
   u32x4_t tok[kStrRing][kNi];
+  // Lanes of tokens past the pass's last load nothing (their output columns are not stored): the
+  // token operand's bytes through the texture path shrink with the pass's token count. Lanes of
+  // token 0 are always live, so every load instruction issues and the per-stage count holds.
+  const bool tok_live = r16 < mp;
   auto load_tok = [&](u32x4_t (&tv)[kNi], int st) {
     const int kb = min(st, nst - 1) * KS;
 #pragma unroll
-    for (int u = 0; u < kNi; ++u) tv[u] = *reinterpret_cast<const u32x4_t*>(trow + kb + u * 32);
+    for (int u = 0; u < kNi; ++u)
+      tv[u] = tok_live ? *reinterpret_cast<const u32x4_t*>(trow + kb + u * 32)
+                       : u32x4_t{0u, 0u, 0u, 0u};
   };
   // prologue: stages 0 .. kStrAhead - 1
 #pragma unroll
@@ -421,14 +427,14 @@ __global__ __launch_bounds__(64) void decode_stream_down_kernel(DecodeArgs p) {
   }
   const int my_row = hrow_of(min(r16, mp - 1));
   if constexpr (kFused) __syncthreads();   // the list is read before the ring is refilled
-  const int pair = kFused ? my_row : p.sorted_pair[my_row];
   auto issue = [&](int q, int st) {
     const uint32_t kb = static_cast<uint32_t>(min(st, nst - 1)) * kSdKS * 2u;
     const uint32_t base = lds_offset(ring + q * kSdSlot);
 #pragma unroll
     for (int i = 0; i < kSdW / 1024; ++i) dma16(base + i * 1024, voff[i], rw, kb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(base + kSdW + j * 1024, toff[j], rh, kb);
+    for (int j = 0; j < 4; ++j)   // token rows past the pass's last: only lane 0 moves (a duplicate)
+      if (4 * j + lane / 16 < mp || lane == 0) dma16(base + kSdW + j * 1024, toff[j], rh, kb);
   };
 #pragma unroll
   for (int q = 0; q < kSdAhead; ++q) issue(q, q);
@@ -459,8 +465,10 @@ __global__ __launch_bounds__(64) void decode_stream_down_kernel(DecodeArgs p) {
 #undef MOE_SD_STAGE
   wait_vmcnt<0>();  // the clamped re-reads past the last stage
 
-  // lane l holds token l % 16 and weight rows 4 (l / 16) + i of each 16-row group
+  // lane l holds token l % 16 and weight rows 4 (l / 16) + i of each 16-row group (the pair is
+  // read only now: a load in flight beside the DMA would make the compiler wait on the ring)
   if (r16 < mp) {
+    const int pair = kFused ? my_row : p.sorted_pair[my_row];
     store_down(p, my_row, pair, n0 + 4 * g, acc0);
     store_down(p, my_row, pair, n0 + 16 + 4 * g, acc1);
   }
