@@ -18,9 +18,9 @@
 // Experts with at most 16 tokens (the usual decode case) take streaming kernels instead, one wave
 // per workgroup owning its weight rows for all of K, so no cross-wave reduction and no barrier is
 // needed. Gate/up: a wave owns 8 gate rows and the matching 8 up rows; each stage moves 256
-// K-elements of the 16 rows (512 contiguous bytes per row) into a four-slot LDS ring by DMA,
-// three stages ahead, and the 16 tokens' slices of the same stages are loaded into registers at
-// the same depth. Down: a wave owns 32 W_down rows; each 128-wide stage brings the rows and the
+// K-elements of the 16 rows (512 contiguous bytes per row) into a two-slot LDS ring by DMA, one
+// stage ahead, and the 16 tokens' slices of the same stages are loaded into registers at the same
+// depth. Down: a wave owns 32 W_down rows; each 128-wide stage brings the rows and the
 // 16 token rows of h into a three-slot ring by DMA.
 #include "common.h"
 #include "launch.h"
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
 
 // ---- streaming kernel for experts with 1..16 tokens ------------------------------------------
 constexpr int kStrRows = 16;                       // weight rows per wave
-constexpr int kStrRing = 4;                        // LDS slots
+constexpr int kStrRing = 2;                        // LDS slots
 constexpr int kStrAhead = kStrRing - 1;            // stages in flight
 
 // Stage `st` (clamped to the last stage) of the wave's 16 rows into `slot` (KS K-elements per
@@ -246,8 +246,10 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   const int nrb = (p.N + kOut - 1) / kOut;
   const int e = blockIdx.x / nrb;
   const int rb = blockIdx.x - e * nrb;
-  // Exactly 32 KB, so that five workgroups fit a CU. On the fused path the pass's 16 pairs are
-  // gathered in the first slot before any DMA lands there.
+  // 16 KB, so that ten workgroups fit a CU (measured on Mixtral-shaped decode: two slots with ten
+  // workgroups per CU 0.322 ms, three with six 0.326, four with five 0.329; 128- or 512-wide
+  // stages in two slots 0.326). On the fused path the pass's 16 pairs are gathered in the first
+  // slot before any DMA lands there.
   __shared__ __attribute__((aligned(1024))) char ring[kStrRing * kStage];
   int32_t* plist = reinterpret_cast<int32_t*>(ring);
   const int lane = threadIdx.x;
@@ -312,9 +314,10 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
     load_tok(tok[q], q);
   }
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  // Stage S in slot S % 4: wait until stage S has landed (the two newer stages may still be in
-  // flight), issue stage S + 3 into the slot stage S - 1 used (its LDS reads were consumed by that
-  // stage's MFMAs), then KS / 32 MFMAs of 16 weight rows x 16 tokens x 32 K.
+  // Stage S in slot S % kStrRing: wait until stage S has landed (the kStrAhead - 1 newer stages
+  // may still be in flight), issue stage S + kStrAhead into the slot stage S - 1 used (its LDS
+  // reads were consumed by that stage's MFMAs), then KS / 32 MFMAs of 16 weight rows x 16 tokens
+  // x 32 K.
 #define MOE_STR_STAGE(Q, S)                                                                   \
   {                                                                                           \
     constexpr int QN = (Q + kStrAhead) % kStrRing;                                            \
@@ -332,8 +335,12 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
   for (int s = 0; s < nst; s += kStrRing) {
     MOE_STR_STAGE(0, s)
     if (s + 1 < nst) MOE_STR_STAGE(1, s + 1)
-    if (s + 2 < nst) MOE_STR_STAGE(2, s + 2)
-    if (s + 3 < nst) MOE_STR_STAGE(3, s + 3)
+    if constexpr (kStrRing >= 3) {
+      if (s + 2 < nst) MOE_STR_STAGE(2, s + 2)
+    }
+    if constexpr (kStrRing >= 4) {
+      if (s + 3 < nst) MOE_STR_STAGE(3, s + 3)
+    }
   }
 #undef MOE_STR_STAGE
   wait_vmcnt<0>();  // the clamped re-reads past the last stage
