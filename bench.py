@@ -45,13 +45,23 @@ OTHER_TRAFFIC = {
 }
 
 
+def source_code_text(text):
+    """C++ source text with // and /* */ comments removed and whitespace runs collapsed, so that
+    editing a comment does not change what identifies a kernel build."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(files):
-    """sha256 over the named kernel sources (identifies the kernel build a counter run measured)."""
+    """sha256 over the code of the named kernel sources, comments and layout left out (identifies
+    the kernel build a counter run measured)."""
     import hashlib
     h = hashlib.sha256()
     for name in files:
-        with open(os.path.join(CSRC, name), "rb") as fh:
-            h.update(name.encode() + b"\0" + fh.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as fh:
+            h.update(name.encode() + b"\0" + source_code_text(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -15,9 +15,9 @@
 // four MFMAs of the chunk take 8 of those elements each; the token operand uses the same k
 // assignment, so every product pairs matching k.
 //
-// Experts with at most 16 tokens (the usual decode case) take streaming kernels instead, one wave
-// per workgroup owning its weight rows for all of K, so no cross-wave reduction and no barrier is
-// needed. Gate/up: a wave owns 8 gate rows and the matching 8 up rows; each stage moves 256
+// Experts with at most 16 tokens (the usual decode case), or every expert when the batch has at
+// most 32 tokens (in passes of 16), take streaming kernels instead, one wave per workgroup owning
+// its weight rows for all of K, so no cross-wave reduction and no barrier is needed. Gate/up: a wave owns 8 gate rows and the matching 8 up rows; each stage moves 256
 // K-elements of the 16 rows (512 contiguous bytes per row) into a two-slot LDS ring by DMA, one
 // stage ahead, and the 16 tokens' slices of the same stages are loaded into registers at the same
 // depth. Down: a wave owns 32 W_down rows; each 128-wide stage brings the rows and the

@@ -43,3 +43,11 @@ def test_measured_traffic_follows_the_source_hash(tmp_path, monkeypatch):
     write("0" * 64)
     assert bench.measured_traffic("x.txt", files) is None
     assert bench.measured_traffic("missing.txt", files) is None
+
+
+def test_source_digest_ignores_comments_and_layout_only():
+    a = "int f(int x) {  // add one\n  return x + 1; /* a block\n   comment */ }\n"
+    b = "int f(int x) {\n\n  return x + 1;   }  // another note\n"
+    c = "int f(int x) { return x + 2; }"
+    assert bench.source_code_text(a) == bench.source_code_text(b)
+    assert bench.source_code_text(a) != bench.source_code_text(c)
