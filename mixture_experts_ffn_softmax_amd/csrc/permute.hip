@@ -70,8 +70,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
   s[tid] = total;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the experts' totals.
-  for (int o = 1; o < kMaxExperts; o <<= 1) {
+  // Hillis-Steele inclusive scan over the experts' totals (the first EP entries; the rest are 0).
+  for (int o = 1; o < EP; o <<= 1) {
     int v = (tid >= o) ? s[tid - o] : 0;
     __syncthreads();
     s[tid] += v;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
       run += chunk_hist[static_cast<size_t>(c) * E + e];
     }
   }
-  if (tid == 0) offsets[E] = s[kMaxExperts - 1];
+  if (tid == 0) offsets[E] = s[EP - 1];
 }
 
 // Stable scatter of pairs [p0, p1) given each expert's next position in `cursor` (LDS). Pairs
@@ -163,7 +163,12 @@ __global__ __launch_bounds__(kScatterThreads) void permute_small_kernel(
   for (int e = e0; e < e1; ++e) sum += cursor[e];
   part[tid] = sum;
   __syncthreads();
-  for (int o = 1; o < kScatterThreads; o <<= 1) {
+  // scan the first NP partial sums (NP: a power of two covering the threads that hold experts;
+  // the others hold 0)
+  const int nparts = (E + per - 1) / per;
+  int NP = 1;
+  while (NP < nparts) NP <<= 1;
+  for (int o = 1; o < NP; o <<= 1) {
     const int v = tid >= o ? part[tid - o] : 0;
     __syncthreads();
     part[tid] += v;
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(kScatterThreads) void permute_small_kernel(
     cursor[e] = run;
     run += c;
   }
-  if (tid == 0) offsets[E] = part[kScatterThreads - 1];
+  if (tid == 0) offsets[E] = part[NP - 1];
   __syncthreads();
   scatter_range(ids, 0, P, E, id_bits, cursor, sorted_pair, pair_pos);
 }
