@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs p) {
   }
 }
 
-// ---- streaming kernel for experts with 1..16 tokens ------------------------------------------
+// ---- streaming gate/up kernel (experts of 1..16 tokens; every expert, in passes, at T <= 32) 
 constexpr int kStrRows = 16;                       // weight rows per wave
 constexpr int kStrRing = 2;                        // LDS slots
 constexpr int kStrAhead = kStrRing - 1;            // stages in flight
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
 }
 
 
-// ---- streaming down kernel for experts with 1..16 tokens -------------------------------------
+// ---- streaming down kernel (experts of 1..16 tokens; every expert, in passes, at T <= 32) ----
 // One wave owns 32 consecutive W_down rows (two 16-row A operands that share each token operand,
 // so a token byte read serves two weight bytes) for all of K = f. Each 128-wide K stage moves the
 // 32 weight rows (256 contiguous bytes each) and the expert's 16 token rows of h into one slot of
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(DecodeArgs p) {
 // against 0.182 ms for the K-split kernel; workgroups of two or four such waves sharing one
 // token slot per stage (a four-slot ring, a barrier per stage) took 0.161 and 0.166 ms. The same
 // form for the gate/up GEMM (16 gate + 16 up rows per wave, x rows gathered by DMA) took 0.353
-// against 0.344 ms for the streaming gate/up kernel above.
+// against 0.344 ms for the streaming gate/up kernel above (then with its four-slot ring).
 constexpr int kSdRows = 32;                      // W_down rows per wave
 constexpr int kSdKS = 128;                       // K per stage
 constexpr int kSdW = kSdRows * kSdKS * 2;        // weight bytes per stage (8 KB)
