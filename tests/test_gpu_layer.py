@@ -281,6 +281,19 @@ def test_decode_two_token_passes():
         _check_layer(spec, inp, _run_gpu(spec, inp, layout), 2e-2)
 
 
+def test_decode_kernel_mix_when_d_is_not_a_stage_multiple():
+    # d = 384 is a multiple of 128 but not of the gate/up streaming kernel's 256-wide stage: with
+    # T <= 32 the gate/up projection runs on the K-split kernel for every expert while the down
+    # projection streams every expert.
+    spec = synth.TINY_F32.with_(name="bf16_decode_mix_T24_d384_f256_E4_k2", dtype="bf16", T=24,
+                                d=384, f=256, E=4, k=2)
+    _assert_small_batch(spec)
+    inp = layer_inputs(spec)
+    for layout in ("slots", "permuted", "acc_f32"):
+        log(spec.name, layout)
+        _check_layer(spec, inp, _run_gpu(spec, inp, layout), 2e-2)
+
+
 def test_decode_repeated_expert_ids():
     # Routing ids that name one expert twice for a token (not what the router makes, but what the
     # permutation accepts): with 24 tokens expert 0 gets 44 pairs, three passes of the streaming
