@@ -96,59 +96,107 @@ __device__ void token_logits(const XT* __restrict__ x, const float* __restrict__
   }
 }
 
-// "a is a better candidate than b": larger logit, equal logits -> lower expert index;
-// index < 0 means "no candidate".
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-  if (ib < 0) return ia >= 0;
-  if (ia < 0) return false;
-  return va > vb || (va == vb && ia < ib);
+// Selection key of expert e with logit x: unsigned 64-bit keys compare as "larger logit, equal
+// logits -> lower expert index". High word: the logit's bits mapped to an unsigned order (-0
+// taken as +0, so the two zeros tie like equal floats; NaNs order by their bits, above +inf when
+// positive and below -inf when negative); low word: ~e. Key 0 stands for "no candidate": every
+// real key is larger, since its low word ~e is not zero.
+__device__ __forceinline__ uint64_t topk_key(float x, int e) {
+  uint32_t b = __float_as_uint(x);
+  if (b == 0x80000000u) b = 0u;
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~e);
+}
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+  const uint32_t ord = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ __forceinline__ int topk_key_index(uint64_t key) {
+  return static_cast<int>(~static_cast<uint32_t>(key));
+}
+
+// A 32-bit value from another lane of the same 16-lane row through a DPP move (no LDS round trip).
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return (static_cast<uint64_t>(dpp_u32<kCtrl>(static_cast<uint32_t>(v >> 32))) << 32) |
+         dpp_u32<kCtrl>(static_cast<uint32_t>(v));
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  return __longlong_as_double(static_cast<long long>(dpp_u64<kCtrl>(u)));
+}
+
+// Reductions over the G lanes of a group (a power of two, groups aligned to G). Up to 16 lanes
+// the partner of each step is reached by DPP: after steps that leave every lane of a 2^s-lane
+// block holding that block's result, pairing lane i with lane 7 - i (or 15 - i) pairs it with a
+// lane of the other block of the next size, so every lane ends with the group's result, formed
+// by the same association in every lane. Wider groups continue with cross-row shuffles.
+__device__ __forceinline__ uint64_t group_max_key(uint64_t v, int G) {
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  if (G > 1) v = mx(v, dpp_u64<0xB1>(v));    // quad_perm [1,0,3,2]: lane ^ 1
+  if (G > 2) v = mx(v, dpp_u64<0x4E>(v));    // quad_perm [2,3,0,1]: lane ^ 2
+  if (G > 4) v = mx(v, dpp_u64<0x141>(v));   // row_half_mirror: lane i <-> 7 - i within eight
+  if (G > 8) v = mx(v, dpp_u64<0x140>(v));   // row_mirror: lane i <-> 15 - i within sixteen
+  for (int o = 16; o < G; o <<= 1) {
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, 64);
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, 64);
+    v = mx(v, (static_cast<uint64_t>(hi) << 32) | lo);
+  }
+  return v;
+}
+__device__ __forceinline__ double group_sum_f64(double s, int G) {
+  if (G > 1) s += dpp_f64<0xB1>(s);
+  if (G > 2) s += dpp_f64<0x4E>(s);
+  if (G > 4) s += dpp_f64<0x141>(s);
+  if (G > 8) s += dpp_f64<0x140>(s);
+  for (int o = 16; o < G; o <<= 1) s += __shfl_xor(s, o, 64);
+  return s;
 }
 
 // Top-k + renormalised softmax weights. A group of G lanes (a power of two: pow2(E) up to 16 lanes,
-// more only when k > 16 so that every pick has its own lane) handles one token (row: its E logits, in global memory or LDS); each lane holds
-// VPL logits (expert e = lane_in_group + G * v). k rounds of a lane-local scan plus a butterfly
-// argmax inside the group pick the experts in descending order; the lane whose slot index equals
-// the round keeps the winner, so lane j of the group ends with the j-th selection.
+// more only when k > 16 so that every pick has its own lane) handles one token (row: its E logits,
+// in global memory or LDS; every lane of the group active); each lane holds VPL selection keys
+// (expert e = lane_in_group + G * v). Each of the k rounds takes the largest key of every lane,
+// then of the group, and clears the winner's key where it sits; lane j of the group keeps the
+// j-th selection, so the experts come out in descending order with the lower-index tie rule.
 template <int VPL>
 __device__ __forceinline__ void topk_select(const float* row, bool tok_ok, int E, int k, int G,
                                             int gl, int32_t* ids, float* w) {
-  float v[VPL];
-  uint64_t taken = 0;
+  uint64_t key[VPL];
 #pragma unroll
   for (int q = 0; q < VPL; ++q) {
-    int e = gl + G * q;
-    v[q] = (tok_ok && e < E) ? row[e] : 0.0f;
+    const int e = gl + G * q;
+    const float x = row[min(e, E - 1)];   // in bounds for every lane; the key drops e >= E
+    key[q] = (tok_ok && e < E) ? topk_key(x, e) : 0ull;
   }
-  float my_v = 0.0f, vmax = 0.0f;
-  int my_i = -1;
+  uint64_t first = 0, mine = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = 0.0f;
-    int bi = -1;
+    uint64_t best = 0;
 #pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-      int e = gl + G * q;
-      bool cand = e < E && !((taken >> q) & 1ull);
-      if (cand && better(v[q], e, bv, bi)) { bv = v[q]; bi = e; }
-    }
-    for (int o = G >> 1; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (j == 0) vmax = bv;
+    for (int q = 0; q < VPL; ++q) best = key[q] > best ? key[q] : best;
+    best = group_max_key(best, G);
+    // keys are unique (the expert index is in the low word), so one slot of one lane matches
+    const uint32_t won = static_cast<uint32_t>(best);
 #pragma unroll
-    for (int q = 0; q < VPL; ++q)
-      if (gl + G * q == bi) taken |= 1ull << q;
-    if (gl == j) { my_v = bv; my_i = bi; }
+    for (int q = 0; q < VPL; ++q) key[q] = static_cast<uint32_t>(key[q]) == won ? 0ull : key[q];
+    if (j == 0) first = best;
+    if (gl == j) mine = best;
   }
   // The k weights in double, rounded once to fp32: the result is the correctly rounded value of
   // exp(l_j - l_max) / sum exp(l - l_max) except within ~1e-16 of a rounding boundary, so it does
   // not depend on the order of the sum (k exponentials per token: negligible work).
-  const double a = (gl < k) ? exp(static_cast<double>(my_v) - static_cast<double>(vmax)) : 0.0;
-  double s = a;
-  for (int o = G >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  const double a = (gl < k) ? exp(static_cast<double>(topk_key_value(mine)) -
+                                  static_cast<double>(topk_key_value(first)))
+                            : 0.0;
+  const double s = group_sum_f64(a, G);
   if (tok_ok && gl < k) {
-    ids[gl] = my_i;
+    ids[gl] = topk_key_index(mine);
     w[gl] = static_cast<float>(a / s);
   }
 }

@@ -48,6 +48,13 @@ def test_route_ties_and_equal_logits():
     lg[2] = np.float32(1.0)
     lg[2, 7] = np.nextafter(np.float32(1.0), np.float32(2.0))
     lg[3:] = np.round(synth.normal_f32(77, (T - 3, E)) * 2) / 2
+    # signed zeros tie like equal values; negative values, subnormals of both signs
+    lg[4] = np.where(np.arange(E) % 3 == 0, np.float32(-0.0), np.float32(0.0))
+    lg[4, 9] = np.float32(-1e-30)
+    lg[5] = -np.abs(synth.normal_f32(78, (E,)))
+    lg[6] = np.float32(1e-45) * (np.arange(E) % 5 - 2)
+    lg[7] = np.float32(-3.0)
+    lg[7, 2] = lg[7, 11] = np.float32(-0.0)
     for k in (1, 2, 5, 16):
         ids_ref, w_ref = oracle.route(lg, k)
         ids, w, _ = moe.moe_route(k, logits=to_dev(lg))
