@@ -95,6 +95,22 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// A 32-bit value from another lane of the same 16-lane row by a DPP move (no LDS round trip).
+// Controls used here: lane ^ 1 and lane ^ 2 (quad permutes [1,0,3,2] and [2,3,0,1]), lane i <->
+// 7 - i within eight (row half mirror) and lane i <-> 15 - i within sixteen (row mirror). Applied
+// in that order to a commutative reduction they leave every lane of a 2, 4, 8 or 16-lane group
+// with the group's result: each step pairs a lane with one of the other block of the next size.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -331,8 +347,10 @@ __device__ __forceinline__ float quant_group16(const float (&v)[8], uint32_t& lo
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));
+  amax = fmaxf(amax, dpp_f32<kDppXor2>(amax));
+  amax = fmaxf(amax, dpp_f32<kDppHalfMirror>(amax));
+  amax = fmaxf(amax, dpp_f32<kDppMirror>(amax));
   lo = hi = 0;
   if constexpr (kUE) {
     const int b = ue8m0_byte(amax);

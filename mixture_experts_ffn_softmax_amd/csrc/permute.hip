@@ -37,6 +37,36 @@ __global__ __launch_bounds__(256) void chunk_histogram_kernel(const int32_t* __r
     chunk_hist[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
 }
 
+// Walks expert e's chunk counts over chunks [c0, c1), adding them to run (and, with kBase, writing
+// each chunk's starting position first). Counts are loaded in batches whose loads all issue before
+// any is used (a loop adding each count as it arrives waits a full memory round trip per chunk):
+// 16 at a time while more than 8 remain, then 4, then one, so short ranges load little extra.
+// Batch slots past c1 reread chunk c1 - 1 and are not used.
+template <int B, bool kBase>
+__device__ __forceinline__ void chunk_batch(const int32_t* __restrict__ chunk_hist, int cb, int c1,
+                                            int E, int e, int& run,
+                                            int32_t* __restrict__ chunk_base) {
+  int v[B];
+#pragma unroll
+  for (int u = 0; u < B; ++u) v[u] = chunk_hist[static_cast<size_t>(min(cb + u, c1 - 1)) * E + e];
+#pragma unroll
+  for (int u = 0; u < B; ++u) {
+    if (cb + u < c1) {
+      if constexpr (kBase) chunk_base[static_cast<size_t>(cb + u) * E + e] = run;
+      run += v[u];
+    }
+  }
+}
+template <bool kBase>
+__device__ __forceinline__ void chunk_walk(const int32_t* __restrict__ chunk_hist, int c0, int c1,
+                                           int E, int e, int& run,
+                                           int32_t* __restrict__ chunk_base) {
+  int cb = c0;
+  for (; c1 - cb > 8; cb += 16) chunk_batch<16, kBase>(chunk_hist, cb, c1, E, e, run, chunk_base);
+  for (; c1 - cb > 1; cb += 4) chunk_batch<4, kBase>(chunk_hist, cb, c1, E, e, run, chunk_base);
+  if (cb < c1) chunk_batch<1, kBase>(chunk_hist, cb, c1, E, e, run, chunk_base);
+}
+
 // One block of 1024 threads. counts[e] = sum over chunks; offsets = exclusive scan over experts;
 // chunk_base[c][e] = offsets[e] + pairs of expert e in chunks before c. Thread (part, e) with
 // tid = part * EP + e (EP = E rounded up to a power of two) owns a contiguous range of the chunks
@@ -54,8 +84,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   const int c0 = static_cast<int>(static_cast<long>(part) * nchunks / G);
   const int c1 = static_cast<int>(static_cast<long>(part + 1) * nchunks / G);
   int sum = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) sum += chunk_hist[static_cast<size_t>(c) * E + e];
+  if (e < E) chunk_walk<false>(chunk_hist, c0, c1, E, e, sum, nullptr);
   part_sum[tid] = sum;
   __syncthreads();
   // per expert: total over parts, and each part's exclusive prefix (kept in part_sum)
@@ -81,10 +110,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     // start of expert e (inclusive scan of the experts before it) + this part's prefix
     int run = (e > 0 ? s[e - 1] : 0) + part_sum[tid];
     if (part == 0) offsets[e] = run;
-    for (int c = c0; c < c1; ++c) {
-      chunk_base[static_cast<size_t>(c) * E + e] = run;
-      run += chunk_hist[static_cast<size_t>(c) * E + e];
-    }
+    chunk_walk<true>(chunk_hist, c0, c1, E, e, run, chunk_base);
   }
   if (tid == 0) offsets[E] = s[EP - 1];
 }

@@ -115,12 +115,6 @@ __device__ __forceinline__ int topk_key_index(uint64_t key) {
   return static_cast<int>(~static_cast<uint32_t>(key));
 }
 
-// A 32-bit value from another lane of the same 16-lane row through a DPP move (no LDS round trip).
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, 0xF, 0xF, false));
-}
 template <int kCtrl>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
   return (static_cast<uint64_t>(dpp_u32<kCtrl>(static_cast<uint32_t>(v >> 32))) << 32) |
@@ -132,17 +126,15 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __longlong_as_double(static_cast<long long>(dpp_u64<kCtrl>(u)));
 }
 
-// Reductions over the G lanes of a group (a power of two, groups aligned to G). Up to 16 lanes
-// the partner of each step is reached by DPP: after steps that leave every lane of a 2^s-lane
-// block holding that block's result, pairing lane i with lane 7 - i (or 15 - i) pairs it with a
-// lane of the other block of the next size, so every lane ends with the group's result, formed
-// by the same association in every lane. Wider groups continue with cross-row shuffles.
+// Reductions over the G lanes of a group (a power of two, groups aligned to G): DPP steps up to
+// 16 lanes (every lane ends with the group's result, formed by the same association in every
+// lane), cross-row shuffles beyond.
 __device__ __forceinline__ uint64_t group_max_key(uint64_t v, int G) {
   auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
-  if (G > 1) v = mx(v, dpp_u64<0xB1>(v));    // quad_perm [1,0,3,2]: lane ^ 1
-  if (G > 2) v = mx(v, dpp_u64<0x4E>(v));    // quad_perm [2,3,0,1]: lane ^ 2
-  if (G > 4) v = mx(v, dpp_u64<0x141>(v));   // row_half_mirror: lane i <-> 7 - i within eight
-  if (G > 8) v = mx(v, dpp_u64<0x140>(v));   // row_mirror: lane i <-> 15 - i within sixteen
+  if (G > 1) v = mx(v, dpp_u64<kDppXor1>(v));
+  if (G > 2) v = mx(v, dpp_u64<kDppXor2>(v));
+  if (G > 4) v = mx(v, dpp_u64<kDppHalfMirror>(v));
+  if (G > 8) v = mx(v, dpp_u64<kDppMirror>(v));
   for (int o = 16; o < G; o <<= 1) {
     const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, 64);
     const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, 64);
@@ -151,10 +143,10 @@ __device__ __forceinline__ uint64_t group_max_key(uint64_t v, int G) {
   return v;
 }
 __device__ __forceinline__ double group_sum_f64(double s, int G) {
-  if (G > 1) s += dpp_f64<0xB1>(s);
-  if (G > 2) s += dpp_f64<0x4E>(s);
-  if (G > 4) s += dpp_f64<0x141>(s);
-  if (G > 8) s += dpp_f64<0x140>(s);
+  if (G > 1) s += dpp_f64<kDppXor1>(s);
+  if (G > 2) s += dpp_f64<kDppXor2>(s);
+  if (G > 4) s += dpp_f64<kDppHalfMirror>(s);
+  if (G > 8) s += dpp_f64<kDppMirror>(s);
   for (int o = 16; o < G; o <<= 1) s += __shfl_xor(s, o, 64);
   return s;
 }
