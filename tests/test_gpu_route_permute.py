@@ -109,6 +109,9 @@ PERMUTE_CASES = [
     ("all_one_expert", 3000, 1, 64, "one"),
     ("max_E_k", 700, 32, 1024, None),
     ("ragged_chunk", 1025, 3, 7, None),
+    # scan threads walking 11-12 and 29-30 chunks each (batched loads with partial batches)
+    ("chunk_runs_11_12", 6000, 8, 256, None),
+    ("chunk_runs_29_30", 7500, 8, 512, None),
     # one-workgroup path (P <= 1024): many experts per thread in its scan, and its exact limit
     ("small_many_experts", 30, 32, 1024, None),
     ("small_limit", 512, 2, 8, None),
