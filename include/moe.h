@@ -102,8 +102,10 @@ const char* moe_status_string(moe_status s);
  *  logits_out  [T, E] fp32: receives the logits that the selection used. Required when
  *              logits == NULL (the computed logits live there); nullable otherwise.
  *  topk_ids    [T, k] int32 out: expert ids by descending logit; equal logits go to the lower
- *              expert index. (Selecting on logits picks the same set as selecting on softmax
- *              probabilities, since softmax is strictly increasing.)
+ *              expert index (+0 and -0 are equal). (Selecting on logits picks the same set as
+ *              selecting on softmax probabilities, since softmax is strictly increasing.) NaN
+ *              logits are outside the contract: they are ordered by their bits (above +inf
+ *              with the sign bit clear, below -inf with it set) and make weights NaN.
  *  topk_w      [T, k] fp32 out: w[t][j] = exp(l_j - l_max) / sum_{j'<k} exp(l_j' - l_max), the
  *              selected softmax probabilities renormalised to sum to 1.
  * ------------------------------------------------------------------------------------------ */
