@@ -392,7 +392,7 @@ moe_status moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
   int bm_a, bm_b;
   if (f32) { bm_a = bm_b = f32_tile_rows(); }
   else if (fp8_decode) { bm_a = bm_b = 0; }  // no tile table
-  else if (fp8) { bm_a = fp8_tile_rows_gateup(); bm_b = fp8_tile_rows_down(); }
+  else if (fp8) { bm_a = bm_b = fp8_tile_rows(w4, ue8m0); }
   else if (decode) { bm_a = bm_b = 0; }  // no tile table
   else { bm_a = bf16_tile_rows_gateup(); bm_b = bf16_tile_rows_down(); }
 

@@ -108,8 +108,7 @@ hipError_t launch_experts_bf16(const ExpertsLaunch& L, hipStream_t stream);
 
 hipError_t launch_experts_bf16_decode(const ExpertsLaunch& L, hipStream_t stream);
 
-int fp8_tile_rows_gateup();
-int fp8_tile_rows_down();
+int fp8_tile_rows(bool w4, bool ue8m0);   // rows of the fp8 GEMMs' tile tables
 hipError_t launch_experts_fp8(const ExpertsLaunch& L, hipStream_t stream);
 hipError_t launch_experts_fp8_decode(const ExpertsLaunch& L, hipStream_t stream);
 
