@@ -46,10 +46,11 @@ SMALL = [
     synth.DSV3_FP8.with_(name="fp8_dense_T16_d256_f128_E1_k1", T=16, d=256, f=128, E=1, k=1),
     synth.DSV3_FP8.with_(name="fp8_all_T100_d256_f128_E4_k4", T=100, d=256, f=128, E=4, k=4),
     synth.DSV3_FP8.with_(name="fp8_one_T1_d256_f128_E8_k2", T=1, d=256, f=128, E=8, k=2),
-    # skewed loads on the 256-row tiles: experts of 531, 403, 289, 206, 168, 158, 134, 111 rows
-    # (two pair tiles and a 19-row remainder tile, a pair tile of 147 rows, a pair tile plus a
-    # 33-row remainder, pair tiles whose last wave rows hold no rows, one 128-row tile); K = 384
-    # and 640 take an odd number of stages, N = 384 a down tile half past the weights
+    # skewed loads: experts of 531, 403, 289, 206, 168, 158, 134, 111 rows. With UE8M0 scales
+    # (256-row tiles) two 256-row tiles and a 19-row remainder tile, a 256-row tile of 147 rows, a
+    # 256-row tile plus a 33-row remainder, 256-row tiles whose last wave rows hold no rows, one
+    # 128-row tile; with fp32 scales 128-row tiles with ragged tails. K = 384 and 640 take an odd
+    # number of stages, N = 384 a down tile half past the weights
     synth.DSV3_FP8.with_(name="fp8_skew_T1000_d384_f640_E8_k2", T=1000, d=384, f=640, E=8, k=2,
                          skew=0.6),
     # experts of 569, 465, 353, 254, 223, 213, 170, 153 rows; even stage counts
