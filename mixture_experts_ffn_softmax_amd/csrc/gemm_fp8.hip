@@ -327,11 +327,10 @@ __device__ __forceinline__ void fp8_tile(const Fp8GemmArgs p, const TileCoord tc
     // half of stage s's MFMAs runs. Stage s: MFMAs of row blocks 0..1 from registers; wait for this wave's DMA of
     // stage s + 1 and its own LDS reads, barrier (stage s + 1 in LDS, every wave done reading
     // stage s); DMA of stage s + 3 into stage s's buffer; reads of stage s + 1; MFMAs of row
-    // blocks 2..3 of stage s. (Without the overlap every wave read its fragments right after the
-    // barrier, all at once, while the matrix pipe waited on them: measured 2 % faster on the
-    // DeepSeek-V3-shaped gate/up. With fp32 scales the second set of fragments and scales takes
-    // the promotion's registers (255 VGPRs) and the same schedule ran 1.9x slower, so those
-    // tiles, and E2M1 weights, keep the schedule below.)
+    // blocks 2..3 of stage s. With e4m3 weights and UE8M0 scales these 128-row tiles are the
+    // remainders past an expert's 256-row tiles, mostly one active wave row; there the overlap
+    // measured 2 % faster on the DeepSeek-V3-shaped gate/up. On full 128-row tiles (fp32 scales,
+    // E2M1 weights) the same schedule ran 1.85-1.9x slower, so those keep the schedule below.)
     struct Fr {
       i32x8_t fa[MI], fb[4];
       f32x4_t sa[MI];
