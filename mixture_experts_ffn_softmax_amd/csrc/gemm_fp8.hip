@@ -328,9 +328,13 @@ __device__ __forceinline__ void fp8_tile(const Fp8GemmArgs p, const TileCoord tc
     // stage s + 1 and its own LDS reads, barrier (stage s + 1 in LDS, every wave done reading
     // stage s); DMA of stage s + 3 into stage s's buffer; reads of stage s + 1; MFMAs of row
     // blocks 2..3 of stage s. With e4m3 weights and UE8M0 scales these 128-row tiles are the
-    // remainders past an expert's 256-row tiles, mostly one active wave row; there the overlap
-    // measured 2 % faster on the DeepSeek-V3-shaped gate/up. On full 128-row tiles (fp32 scales,
-    // E2M1 weights) the same schedule ran 1.85-1.9x slower, so those keep the schedule below.)
+    // remainders past an expert's 256-row tiles, mostly one active wave row. The slot pointer is
+    // picked from an array at run time, so the compiler emits these reads as flat loads, which
+    // also wait for the wave's outstanding DMA; as built, this measured 2 % faster on the
+    // DeepSeek-V3-shaped gate/up than the read-after-barrier order below, and 3 % faster than the
+    // same overlap with the slots addressed as ring + slot * size (LDS reads). On full 128-row
+    // tiles (fp32 scales, E2M1 weights) the overlap was slower in both builds (LDS reads: 11 % and
+    // 5 %), so those keep the schedule below.)
     struct Fr {
       i32x8_t fa[MI], fb[4];
       f32x4_t sa[MI];
